@@ -1,0 +1,230 @@
+"""Decode benchmark: indexer + sparse attention over an NVFP4 paged KV cache.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+
+One step = one decode step of one layer: msa_indexer_decode (scan the whole
+NVFP4 index cache of every sequence, score blocks, select top-16 + recent)
+then msa_sparse_attn_decode (exact attention over the selected blocks).
+Inputs are synthetic and already resident in HBM (seeded generator, cache
+written by msa_nvfp4_quantize) before the timed region starts.
+
+Prints one JSON line: query tokens/s (value), achieved HBM GB/s of the step,
+the indexer kernel against the HBM roofline (HIP events on the launch
+stream), and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
+IDX_BYTES_PER_TOKEN_HEAD = 72   # 64 code bytes + 8 scale bytes
+KV_BYTES_PER_BLOCK_HEAD = 128 * 72
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", type=int, default=2,
+                   help="workload index (0..4); 2 = 8 x 262,144 tokens")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-blocks", type=int, default=256,
+                   help="index blocks of one sequence the CPU oracle scans")
+    return p.parse_args()
+
+
+def algorithmic_bytes(wl, ids):
+    """Bytes the method must move per step (never the dense K/V it skips)."""
+    import numpy as np
+    tq, hq = wl.num_q_tokens, wl.num_q_heads
+    nblocks = sum(wl.blocks_of(b) for b in range(wl.num_seqs))
+    idx = (sum(int(L) for L in wl.seq_lens) * wl.num_idx_heads * IDX_BYTES_PER_TOKEN_HEAD
+           + tq * hq * 128          # FP8 index queries
+           + tq * hq * 4            # head weights
+           + nblocks * 4            # block-table entries
+           + tq * (wl.topk + 1) * 4)  # ids written
+    union = 0
+    for b in range(wl.num_seqs):
+        rows = ids[b * wl.q_per_seq:(b + 1) * wl.q_per_seq]
+        union += len(set(int(x) for x in rows.reshape(-1) if x >= 0))
+    attn = (union * 2 * wl.num_kv_heads * KV_BYTES_PER_BLOCK_HEAD
+            + tq * hq * 128             # FP8 attention queries
+            + tq * (wl.topk + 1) * 4    # ids read
+            + tq * hq * 128 * 4)        # fp32 output
+    return idx, attn, union
+
+
+def cpu_baseline(wl, nblk):
+    """The oracle (as is) timed on one query token: its index scan over the
+    first `nblk` blocks of sequence 0 (scaled to the full context) plus exact
+    attention over 17 blocks. Quantising the sources is setup (untimed)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import _support as S
+    from msa_workloads import synth
+    from oracle import msa, nvfp4
+
+    S.tune_host_malloc()
+    cores = len(os.sched_getaffinity(0))
+    b, nb_full = 0, wl.blocks_of(0)
+    nblk = min(nblk, nb_full)
+    pages = wl.block_table[b, :nblk].astype(np.int64)
+    q = S.fp8_values(wl.q_idx())[0]
+    qa = S.fp8_values(wl.q_attn())[0]
+    w = wl.weights().numpy().astype(np.float64)[0]
+    enc = {}
+    for st in (synth.STREAM_IDX, synth.STREAM_K, synth.STREAM_V):
+        pg = pages if st == synth.STREAM_IDX else pages[:17]
+        chunks = []
+        for c0 in range(0, len(pg), 16):
+            src = wl.sources(st, pg[c0:c0 + 16]).numpy()
+            chunks.append(nvfp4.quantize(src))
+        enc[st] = chunks
+    with threadpool_limits(limits=cores):
+        t0 = time.perf_counter()
+        bs = []
+        for c, s in enc[synth.STREAM_IDX]:
+            kh = nvfp4.dequant_fp8(c, s)[1]
+            local = kh.shape[0] - 1
+            bs.append(msa.block_scores(msa.token_scores(q, w, kh, local), local))
+        ids = msa.select_blocks(np.concatenate(bs), wl.topk)
+        t_idx = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        kh = np.concatenate([nvfp4.dequant_fp8(c, s)[1] for c, s in enc[synth.STREAM_K]])
+        vh = np.concatenate([nvfp4.dequant_fp8(c, s)[1] for c, s in enc[synth.STREAM_V]])
+        sel = np.arange(min(17, nblk))
+        msa.sparse_attention(qa, kh, vh, sel, kh.shape[0] - 1, 1 / math.sqrt(128))
+        t_attn = time.perf_counter() - t0
+    per_token = t_idx * (nb_full / nblk) + t_attn
+    return {
+        "value": round(1.0 / per_token, 4),
+        "unit": "query-tokens/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"1 query token of sequence 0: NumPy fp64 oracle index scan (NVFP4->FP8 "
+                   f"dequant, token scores, block max) over the first {nblk} of {nb_full} "
+                   f"blocks, time scaled x{nb_full / nblk:g}, then top-16 selection and exact "
+                   f"attention over 17 blocks; BLAS threads={cores}, elementwise NumPy "
+                   f"single-threaded; measured {t_idx + t_attn:.1f} s"),
+        "selected_in_sample": int(len(ids)),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the path has no multi-GPU mode)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import nvfp4_kv_cache_amd as nb
+    from msa_workloads import get_config, synth
+    from msa_workloads.device import device_inputs, fill_pools
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    nb.lib()
+    wl = get_config(args.workload)
+    print(f"[bench] workload {wl.name}: filling pools", file=sys.stderr, flush=True)
+    pools = fill_pools(wl, nb, garbage=False)
+    inp = device_inputs(wl)
+    tq = wl.num_q_tokens
+    dev = "cuda"
+    ws_i = nb.indexer_workspace(wl.num_seqs, wl.q_per_seq, wl.max_blocks)
+    ws_a = nb.attn_workspace(wl.num_seqs, wl.q_per_seq, wl.num_q_heads, wl.topk + 1)
+    ids = torch.empty((tq, wl.topk + 1), dtype=torch.int32, device=dev)
+    out = torch.empty((tq, wl.num_q_heads, 128), dtype=torch.float32, device=dev)
+    ic, isc = pools[synth.STREAM_IDX]
+    kc, ks = pools[synth.STREAM_K]
+    vc, vs = pools[synth.STREAM_V]
+    scale = 1.0 / math.sqrt(128)
+
+    def step():
+        nb.msa_indexer_decode(ic, isc, inp["q_idx"], inp["w"], inp["block_table"],
+                              inp["seq_lens"], wl.q_per_seq, ids, ws_i)
+        nb.msa_sparse_attn_decode(kc, ks, vc, vs, inp["q_attn"], inp["block_table"],
+                                  inp["seq_lens"], wl.q_per_seq, ids, scale, out, ws_a)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K back-to-back steps, synchronised on both sides
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # per-kernel durations with HIP events on the launch stream
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for e in ev:
+        e[0].record(stream)
+        nb.msa_indexer_decode(ic, isc, inp["q_idx"], inp["w"], inp["block_table"],
+                              inp["seq_lens"], wl.q_per_seq, ids, ws_i)
+        e[1].record(stream)
+        nb.msa_sparse_attn_decode(kc, ks, vc, vs, inp["q_attn"], inp["block_table"],
+                                  inp["seq_lens"], wl.q_per_seq, ids, scale, out, ws_a)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    t_idx = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
+    t_attn = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
+
+    ids_np = ids.cpu().numpy()
+    idx_bytes, attn_bytes, union = algorithmic_bytes(wl, ids_np)
+    ms = wall / args.steps * 1e3
+    step_bytes = idx_bytes + attn_bytes
+    idx_gbs = idx_bytes / t_idx / 1e9
+    res = {
+        "metric": "decode query-tokens/s + achieved HBM GB/s (indexer+sparse-attn, 1 layer)",
+        "value": round(tq * args.steps / wall, 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic (seeded N(0,1) fp32 sources quantised to NVFP4 on the GPU; "
+                "FP8 queries; U(0,1) head weights)",
+        "config": {"workload": wl.name, "num_seqs": wl.num_seqs,
+                   "context_tokens": int(max(wl.seq_lens)), "q_per_seq": wl.q_per_seq,
+                   "kv_heads": wl.num_kv_heads, "index_heads": wl.num_idx_heads,
+                   "q_heads": wl.num_q_heads, "head_dim": 128, "block_tokens": 128,
+                   "topk": wl.topk},
+        "achieved_hbm_gbs": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+        "hbm_frac_of_peak": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes_per_step": int(step_bytes),
+        "kernels_us": {"msa_indexer_decode": round(t_idx * 1e6, 2),
+                       "msa_sparse_attn_decode": round(t_attn * 1e6, 2)},
+        "selected_blocks_union": int(union),
+        "roofline": {"bound": "hbm", "kernel": "indexer_kernel (msa_indexer_decode)",
+                     "achieved": round(idx_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(idx_gbs / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes": int(idx_bytes), "traffic": None},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_blocks)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,181 @@
+/*
+ * msa_nvfp4.h -- C ABI of libmsa_nvfp4.so: MiniMax-style sparse-attention
+ * decode over an NVFP4 paged KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (the pages this follows):
+ *  - The KV cache and the indexer's key cache are stored as NVFP4: every 16
+ *    consecutive channels of one token and one head share one E4M3 scale and
+ *    hold 4-bit E2M1 codes (vLLM Delivers Day-0 Support for MiniMax M3.1
+ *    Flash, section "NVFP4 KV Cache and MoE Weights"; MiniMax-M3.1-Flash lands
+ *    in vLLM on day one, first paragraph: 34,560 instead of 61,440 bytes per
+ *    token).
+ *  - Queries stay FP8 (E4M3), so the cache is converted to FP8 before every
+ *    product (same page, third paragraph). On CDNA4 the conversion is a small
+ *    lookup table of scaled values plus sign handling (MiniMax-M3.1-Flash
+ *    serving summary, yuxiaoba.github.io, section "AMD uses different
+ *    conversion and communication mechanisms").
+ *  - KV is organised in 128-token blocks; a lightweight indexer scores the
+ *    context, keeps the 16 best blocks and the most recent one, and exact
+ *    attention runs over those roughly 2,048 keys (same summary, section
+ *    "Sparse attention still scans an index").
+ *
+ * Conventions shared by every entry point:
+ *  - Every pointer argument is DEVICE memory owned by the caller, except the
+ *    msa_pool_desc pointers, which are host memory read during the call.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream). The library allocates nothing and keeps no state between calls;
+ *    two calls may run concurrently only if they use different workspaces.
+ *  - Arguments are checked on the host before anything is launched; a failed
+ *    check returns a status and launches nothing. MSA_ERR_HIP reports a failed
+ *    kernel launch. Device data (block tables, sequence lengths, selected ids,
+ *    slots) is checked on the device: out-of-range values are never
+ *    dereferenced (see each entry point for what they produce instead).
+ *  - Device buffers read or written in 16-byte units must be 16-byte aligned:
+ *    codes, scales, queries, workspaces, outputs.
+ *  - Supported shapes: head_dim 128, block_tokens 128, topk 16, and 8 query
+ *    heads per KV / index-key head (num_q_heads == 8 * num_heads); other
+ *    values return MSA_ERR_UNSUPPORTED.
+ *
+ * Paged pool layout (one pool per cache: K, V and index keys), per page of
+ * 128 token slots; a token in slot s lives in page s / 128, row s % 128:
+ *   codes  uint8 [num_pages][num_heads][128 rows][64]  two E2M1 codes per byte,
+ *          channel 2j in the low nibble of byte j, 2j+1 in the high nibble;
+ *          code = sign << 3 | magnitude index (0, .5, 1, 1.5, 2, 3, 4, 6)
+ *   scales uint8 [num_pages][num_heads][128 rows][8]   E4M3 scale of channels
+ *          16g .. 16g+15 in byte g
+ *
+ * Sequences: sequence b has seq_lens[b] tokens in its pages, including its
+ * q_per_seq query tokens (their keys are already written). Query token i of
+ * sequence b (row b * q_per_seq + i of every per-query array) sits at
+ * position pos = seq_lens[b] - q_per_seq + i and sees tokens 0..pos.
+ * block_table[b * max_blocks + j] is the physical page of its logical block j.
+ */
+#ifndef MSA_NVFP4_H
+#define MSA_NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSA_HEAD_DIM 128
+#define MSA_BLOCK_TOKENS 128
+#define MSA_GROUP 16
+#define MSA_TOPK 16
+#define MSA_HEADS_PER_KV 8
+#define MSA_MAX_Q_PER_SEQ 8
+#define MSA_MAX_HEADS 8
+
+typedef enum msa_status {
+  MSA_OK = 0,
+  MSA_ERR_INVALID_ARG = 1, /* null pointer, negative size, misalignment */
+  MSA_ERR_UNSUPPORTED = 2, /* a shape this build does not implement */
+  MSA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+  MSA_ERR_HIP = 4          /* the HIP runtime refused a launch */
+} msa_status;
+
+/* Shape of one paged pool. */
+typedef struct msa_pool_desc {
+  int32_t num_heads;    /* heads per token: KV heads, or index-key heads; 1..8 */
+  int32_t head_dim;     /* channels per head; must be 128 */
+  int32_t block_tokens; /* token slots per page; must be 128 */
+  int32_t reserved;     /* set to 0 */
+  int64_t num_pages;    /* pages in the pool; > 0 */
+} msa_pool_desc;
+
+/* Human-readable name of a status code (static storage). */
+const char* msa_status_string(msa_status s);
+
+/*
+ * Cache writer: quantise fp32 rows to NVFP4 and store them into a pool.
+ * Defines: the NVFP4 encoding above. For each (token, head, group of 16):
+ *   amax = max |x|; s = E4M3 value nearest to amax/6 (ties to even,
+ *   saturating at 448); each element's magnitude is the E2M1 value nearest to
+ *   |x|/s (ties to even, saturating at 6; 0 when s == 0); the sign bit is
+ *   kept, also for elements that round to 0.
+ *   src          float [num_tokens][pool->num_heads][128]
+ *   slot_mapping int64 [num_tokens]; token t goes to slot slot_mapping[t];
+ *                slots < 0 or >= num_pages * 128 are skipped (not written)
+ *   codes/scales the pool (layout above)
+ * num_tokens == 0 is a no-op. Inputs must be finite.
+ */
+msa_status msa_nvfp4_quantize(const msa_pool_desc* pool, const float* src,
+                              const int64_t* slot_mapping, int64_t num_tokens,
+                              uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
+ * Workspace bytes msa_indexer_decode needs (block scores and per-sequence
+ * completion counters). The workspace must be zero-filled before its first
+ * use; every call leaves its counters at zero again, so one zero-fill at
+ * allocation is enough.
+ */
+size_t msa_indexer_workspace_bytes(int32_t num_seqs, int32_t q_per_seq, int32_t max_blocks);
+
+/*
+ * Indexer: scan the whole NVFP4 index-key cache of every sequence, score its
+ * 128-token blocks against FP8 index queries and select, per query token,
+ * the 16 best blocks plus the most recent one.
+ * Defines (the build's reading of "a lightweight indexer scores context"):
+ *   S(t)  = sum_h w_h * max(0, q_h . K(t, h / 8)), K = the FP8 dequantised key
+ *   B(j)  = max of S(t) over the visible tokens of block j
+ *   ids   = top-16 of blocks 0..nb-2 by (B descending, j ascending), plus block
+ *           nb-1, in ascending order; all blocks when nb <= 17; -1 padding.
+ *           nb = pos / 128 + 1.
+ *   idx          pool of index keys (num_heads = index-key heads)
+ *   q_fp8        uint8 E4M3 [num_seqs * q_per_seq][num_q_heads][128]
+ *   head_w       float [num_seqs * q_per_seq][num_q_heads]; must be >= 0
+ *   block_table  int32 [num_seqs][max_blocks]
+ *   seq_lens     int32 [num_seqs]
+ *   out_ids      int32 [num_seqs * q_per_seq][topk + 1]
+ *   out_scores   float [num_seqs * q_per_seq][topk + 1] or NULL: B(j) of each
+ *                selected block (0 for padding)
+ * Device-side checks: a sequence with seq_lens < q_per_seq or
+ * seq_lens > max_blocks * 128 gets all ids -1; a block whose page id is
+ * outside [0, num_pages) scores 0 and its page is not read.
+ * 1 <= q_per_seq <= 8; topk must be 16.
+ */
+msa_status msa_indexer_decode(const msa_pool_desc* idx, const uint8_t* idx_codes,
+                              const uint8_t* idx_scales, const uint8_t* q_fp8,
+                              const float* head_w, int32_t num_q_heads,
+                              const int32_t* block_table, int32_t max_blocks,
+                              const int32_t* seq_lens, int32_t num_seqs, int32_t q_per_seq,
+                              int32_t topk, int32_t* out_ids, float* out_scores,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes msa_sparse_attn_decode needs (split partial results and
+ * completion counters). Same zero-fill rule as the indexer's workspace.
+ */
+size_t msa_attn_workspace_bytes(int32_t num_seqs, int32_t q_per_seq, int32_t num_q_heads,
+                                int32_t num_sel);
+
+/*
+ * Sparse attention: for each query token and query head h, exact softmax
+ * attention over the visible tokens (t <= pos) of the selected blocks,
+ *   o = sum_t softmax_t(softmax_scale * q_h . K(t)) V(t),  KV head h / 8,
+ * with K and V dequantised to FP8 from their NVFP4 pools.
+ *   kv           shape of both pools (num_heads = KV heads)
+ *   q_fp8        uint8 E4M3 [num_seqs * q_per_seq][num_q_heads][128]
+ *   sel_ids      int32 [num_seqs * q_per_seq][num_sel] logical block ids,
+ *                distinct; entries < 0, >= max_blocks, past pos, or whose
+ *                page is outside [0, num_pages) are ignored
+ *   out          float [num_seqs * q_per_seq][num_q_heads][128]; a query
+ *                token with no usable block gets zeros
+ * 1 <= num_sel <= 64.
+ */
+msa_status msa_sparse_attn_decode(const msa_pool_desc* kv, const uint8_t* k_codes,
+                                  const uint8_t* k_scales, const uint8_t* v_codes,
+                                  const uint8_t* v_scales, const uint8_t* q_fp8,
+                                  int32_t num_q_heads, const int32_t* block_table,
+                                  int32_t max_blocks, const int32_t* seq_lens, int32_t num_seqs,
+                                  int32_t q_per_seq, const int32_t* sel_ids, int32_t num_sel,
+                                  float softmax_scale, float* out, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_NVFP4_H */

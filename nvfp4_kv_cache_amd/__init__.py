@@ -1,0 +1,11 @@
+"""MI355X-native MiniMax-style sparse-attention decode over an NVFP4 paged KV cache.
+
+The compute lives in libmsa_nvfp4.so (HIP, gfx950; C ABI in include/msa_nvfp4.h).
+This package is its thin ctypes binding; PyTorch supplies device memory and
+the current HIP stream only.
+"""
+from .binding import (  # noqa: F401
+    LIB_PATH, MsaError, PoolDesc, attn_workspace, empty_pool, indexer_workspace, lib,
+    msa_attn_workspace_bytes, msa_indexer_decode, msa_indexer_workspace_bytes,
+    msa_nvfp4_quantize, msa_sparse_attn_decode, msa_status_string, pool_desc,
+)

@@ -1,0 +1,211 @@
+"""ctypes binding of libmsa_nvfp4.so (include/msa_nvfp4.h).
+
+Argument marshalling only: shapes and dtypes are checked, device pointers and
+torch's current HIP stream are passed through, and a non-OK status raises
+MsaError. Every step of the computation runs in the library's HIP kernels;
+there is no fallback of any kind. If the library is not built, loading it
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmsa_nvfp4.so")
+
+MSA_OK = 0
+HEAD_DIM = 128
+BLOCK_TOKENS = 128
+TOPK = 16
+
+_lib = None
+
+
+class MsaError(RuntimeError):
+    pass
+
+
+class PoolDesc(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block_tokens", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("num_pages", ctypes.c_int64)]
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+_F32 = ctypes.c_float
+_DESC = ctypes.POINTER(PoolDesc)
+
+SIGNATURES = {
+    "msa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "msa_nvfp4_quantize": (ctypes.c_int, [_DESC, _P, _P, _I64, _P, _P, _P]),
+    "msa_indexer_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
+    "msa_indexer_decode": (ctypes.c_int, [_DESC, _P, _P, _P, _P, _I32, _P, _I32, _P, _I32, _I32,
+                                          _I32, _P, _P, _P, _SZ, _P]),
+    "msa_attn_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
+    "msa_sparse_attn_decode": (ctypes.c_int, [_DESC, _P, _P, _P, _P, _P, _I32, _P, _I32, _P,
+                                              _I32, _I32, _P, _I32, _F32, _P, _P, _SZ, _P]),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmsa_nvfp4.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise MsaError(f"{LIB_PATH} is not built: run `python -m nvfp4_kv_cache_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def msa_status_string(status: int) -> str:
+    return lib().msa_status_string(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != MSA_OK:
+        raise MsaError(f"{what}: {msa_status_string(status)}")
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtype, ndim=None, device=True):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if device and t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def pool_desc(codes: torch.Tensor) -> PoolDesc:
+    """Pool shape from a codes tensor uint8 [num_pages, num_heads, 128, 64]."""
+    if codes.dim() != 4 or codes.shape[2] != BLOCK_TOKENS or codes.shape[3] != HEAD_DIM // 2:
+        raise ValueError(f"codes must be [pages, heads, 128, 64], got {tuple(codes.shape)}")
+    return PoolDesc(codes.shape[1], HEAD_DIM, BLOCK_TOKENS, 0, codes.shape[0])
+
+
+def _check_pool(codes, scales, name):
+    _need(codes, f"{name}_codes", torch.uint8, 4)
+    _need(scales, f"{name}_scales", torch.uint8, 4)
+    if tuple(scales.shape) != tuple(codes.shape[:3]) + (HEAD_DIM // 16,):
+        raise ValueError(f"{name}_scales shape {tuple(scales.shape)} does not match codes")
+
+
+def empty_pool(num_pages: int, num_heads: int, device="cuda"):
+    """Uninitialised (codes, scales) pool tensors in the library's layout."""
+    codes = torch.empty((num_pages, num_heads, BLOCK_TOKENS, HEAD_DIM // 2), dtype=torch.uint8,
+                        device=device)
+    scales = torch.empty((num_pages, num_heads, BLOCK_TOKENS, HEAD_DIM // 16), dtype=torch.uint8,
+                         device=device)
+    return codes, scales
+
+
+def msa_nvfp4_quantize(src, slot_mapping, codes, scales):
+    """Quantise src float32 [T, H, 128] into the pool at slot_mapping int64 [T]."""
+    _check_pool(codes, scales, "pool")
+    _need(src, "src", torch.float32, 3)
+    _need(slot_mapping, "slot_mapping", torch.int64, 1)
+    desc = pool_desc(codes)
+    if src.shape[1] != desc.num_heads or src.shape[2] != HEAD_DIM:
+        raise ValueError(f"src must be [T, {desc.num_heads}, 128], got {tuple(src.shape)}")
+    if slot_mapping.shape[0] != src.shape[0]:
+        raise ValueError("slot_mapping length must equal the number of tokens")
+    _check(lib().msa_nvfp4_quantize(ctypes.byref(desc), _ptr(src), _ptr(slot_mapping),
+                                    src.shape[0], _ptr(codes), _ptr(scales), _stream()),
+           "msa_nvfp4_quantize")
+
+
+def msa_indexer_workspace_bytes(num_seqs: int, q_per_seq: int, max_blocks: int) -> int:
+    return int(lib().msa_indexer_workspace_bytes(num_seqs, q_per_seq, max_blocks))
+
+
+def msa_attn_workspace_bytes(num_seqs: int, q_per_seq: int, num_q_heads: int, num_sel: int) -> int:
+    return int(lib().msa_attn_workspace_bytes(num_seqs, q_per_seq, num_q_heads, num_sel))
+
+
+def indexer_workspace(num_seqs, q_per_seq, max_blocks, device="cuda"):
+    """Zero-filled workspace for msa_indexer_decode (zeroed once; calls keep it reusable)."""
+    n = msa_indexer_workspace_bytes(num_seqs, q_per_seq, max_blocks)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def attn_workspace(num_seqs, q_per_seq, num_q_heads, num_sel, device="cuda"):
+    """Zero-filled workspace for msa_sparse_attn_decode."""
+    n = msa_attn_workspace_bytes(num_seqs, q_per_seq, num_q_heads, num_sel)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def msa_indexer_decode(idx_codes, idx_scales, q_fp8, head_w, block_table, seq_lens, q_per_seq,
+                       out_ids, workspace, out_scores=None, topk=TOPK):
+    """Top-16 + recent block ids per query token into out_ids int32 [B*Q, 17]."""
+    _check_pool(idx_codes, idx_scales, "idx")
+    _need(q_fp8, "q_fp8", torch.uint8, 3)
+    _need(head_w, "head_w", torch.float32, 2)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    _need(out_ids, "out_ids", torch.int32, 2)
+    _need(workspace, "workspace", torch.uint8, 1)
+    if out_scores is not None:
+        _need(out_scores, "out_scores", torch.float32, 2)
+    num_seqs, max_blocks = block_table.shape
+    tq = num_seqs * q_per_seq
+    hq = q_fp8.shape[1]
+    if seq_lens.shape[0] != num_seqs or q_fp8.shape != (tq, hq, HEAD_DIM):
+        raise ValueError("q_fp8 must be [num_seqs*q_per_seq, Hq, 128] and seq_lens [num_seqs]")
+    if head_w.shape != (tq, hq) or out_ids.shape != (tq, topk + 1):
+        raise ValueError("head_w must be [T_q, Hq] and out_ids [T_q, topk+1]")
+    if out_scores is not None and out_scores.shape != out_ids.shape:
+        raise ValueError("out_scores must match out_ids")
+    desc = pool_desc(idx_codes)
+    _check(lib().msa_indexer_decode(
+        ctypes.byref(desc), _ptr(idx_codes), _ptr(idx_scales), _ptr(q_fp8), _ptr(head_w), hq,
+        _ptr(block_table), max_blocks, _ptr(seq_lens), num_seqs, q_per_seq, topk, _ptr(out_ids),
+        _ptr(out_scores), _ptr(workspace), workspace.numel(), _stream()), "msa_indexer_decode")
+
+
+def msa_sparse_attn_decode(k_codes, k_scales, v_codes, v_scales, q_fp8, block_table, seq_lens,
+                           q_per_seq, sel_ids, softmax_scale, out, workspace):
+    """Attention over the selected blocks into out float32 [B*Q, Hq, 128]."""
+    _check_pool(k_codes, k_scales, "k")
+    _check_pool(v_codes, v_scales, "v")
+    if k_codes.shape != v_codes.shape:
+        raise ValueError("K and V pools must have the same shape")
+    _need(q_fp8, "q_fp8", torch.uint8, 3)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    _need(sel_ids, "sel_ids", torch.int32, 2)
+    _need(out, "out", torch.float32, 3)
+    _need(workspace, "workspace", torch.uint8, 1)
+    num_seqs, max_blocks = block_table.shape
+    tq = num_seqs * q_per_seq
+    hq = q_fp8.shape[1]
+    if q_fp8.shape != (tq, hq, HEAD_DIM) or out.shape != (tq, hq, HEAD_DIM):
+        raise ValueError("q_fp8 and out must be [num_seqs*q_per_seq, Hq, 128]")
+    if sel_ids.shape[0] != tq or seq_lens.shape[0] != num_seqs:
+        raise ValueError("sel_ids must be [T_q, num_sel] and seq_lens [num_seqs]")
+    desc = pool_desc(k_codes)
+    _check(lib().msa_sparse_attn_decode(
+        ctypes.byref(desc), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales),
+        _ptr(q_fp8), hq, _ptr(block_table), max_blocks, _ptr(seq_lens), num_seqs, q_per_seq,
+        _ptr(sel_ids), sel_ids.shape[1], float(softmax_scale), _ptr(out), _ptr(workspace),
+        workspace.numel(), _stream()), "msa_sparse_attn_decode")

@@ -1,0 +1,339 @@
+// indexer.hip -- msa_indexer_decode: scan the NVFP4 index-key cache, score
+// 128-token blocks, and select the top-16 blocks plus the most recent one.
+//
+// The pages: the indexer still scans the whole history, only with smaller
+// reads than K/V (MiniMax-M3.1-Flash serving summary, section "Sparse
+// attention still scans an index"); the index cache is NVFP4 and the FP8
+// queries force a conversion to FP8 before the QK product (MiniMax-M3.1-Flash
+// lands in vLLM on day one, third paragraph); several heads and speculative
+// query tokens are batched to fill the matrix units (serving summary,
+// section "Parallelize index work across context").
+//
+// One kernel, grid (block chunks, sequences); one wavefront per index-key
+// head. Per 128-token block a wave streams its head's 8 KiB of codes and
+// 1 KiB of scales in coalesced 16-byte loads (lane l: token row 16j + l%16,
+// 32-channel slice l/16), turns them into FP8 MFMA operands through the LDS
+// lookup table, and multiplies them with the FP8 index queries held in
+// registers: A = queries (16 rows = 8 heads x up to 2 query tokens),
+// B = 16 tokens x 128 channels. The epilogue applies ReLU and the head
+// weights, sums the 8 heads of the group across the two 16-lane halves,
+// and leaves per-token partial scores in LDS; the waves' partials are summed
+// over heads and maximised over the block's visible tokens. When every
+// workgroup of a sequence has written its block scores, the last one selects
+// the blocks (wavefront ballots and lane reads, no sort).
+#include "msa_nvfp4.h"
+#include "nvfp4_tile.h"
+
+namespace msa {
+
+__constant__ Fp8Lut kIdxLut = make_fp8_lut();
+
+struct IndexerArgs {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  int64_t num_pages;
+  int num_heads;  // index-key heads = wavefronts per workgroup
+  const uint8_t* q;
+  const float* w;
+  int num_q_heads;
+  const int32_t* block_table;
+  int max_blocks;
+  const int32_t* seq_lens;
+  int q_per_seq;
+  int blocks_per_wg;
+  float* bscore;       // [num_seqs * q_per_seq][max_blocks]
+  uint32_t* counters;  // [num_seqs]
+  int32_t* out_ids;
+  float* out_scores;
+};
+
+__device__ __forceinline__ float canon_score(float s) { return s > 0.0f ? s : 0.0f; }
+
+// Unique ordering key: larger score first, then lower block index.
+__device__ __forceinline__ uint64_t score_key(float s, int j) {
+  return (uint64_t(__float_as_uint(canon_score(s))) << 32) | uint32_t(0xFFFFFFFFu - uint32_t(j));
+}
+__device__ __forceinline__ int key_block(uint64_t k) { return int(0xFFFFFFFFu - uint32_t(k)); }
+__device__ __forceinline__ float key_score(uint64_t k) { return __uint_as_float(uint32_t(k >> 32)); }
+
+// Top-16 of blocks 0..nb-2 plus block nb-1, ascending, for one query token;
+// executed by one whole wavefront. buf: 80 wave-private LDS slots.
+__device__ void select_blocks(const float* __restrict__ bs, int nb, int32_t* __restrict__ ids,
+                              float* __restrict__ scores, uint64_t* buf, int lane) {
+  constexpr int K = MSA_TOPK;
+  if (nb <= K + 1) {
+    if (lane < K + 1) {
+      ids[lane] = lane < nb ? lane : -1;
+      if (scores) scores[lane] = lane < nb ? canon_score(bs[lane]) : 0.0f;
+    }
+    return;
+  }
+  const int n = nb - 1;  // candidates; the recent block is always kept
+  // 1. each lane's best key; theta = the 16th best lane maximum. At least 16
+  //    keys are >= theta, so the top-16 are among the keys >= theta.
+  uint64_t best = 0;
+  for (int j = lane; j < n; j += 64) {
+    const uint64_t k = score_key(bs[j], j);
+    best = k > best ? k : best;
+  }
+  int rank = 0;
+  for (int src = 0; src < 64; ++src) rank += readlane_u64(best, src) > best ? 1 : 0;
+  const uint64_t m15 = __ballot(rank == K - 1);
+  const uint64_t theta = readlane_u64(best, __builtin_ctzll(m15));
+  int cnt = 0;
+  for (int j = lane; j < n; j += 64) cnt += score_key(bs[j], j) >= theta ? 1 : 0;
+  const int survivors = wave_sum_int(cnt);
+
+  uint64_t mine = 0;  // lanes 0..15 end with the selected keys (any order)
+  if (survivors <= 64) {
+    // 2a. gather the survivors, rank them exactly, keep ranks 0..15
+    int base = 0;
+    for (int j0 = 0; j0 < n; j0 += 64) {
+      const int j = j0 + lane;
+      const uint64_t k = j < n ? score_key(bs[j], j) : 0;
+      const bool p = j < n && k >= theta;
+      const uint64_t mask = __ballot(p);
+      if (p) buf[base + __popcll(mask & ((1ull << lane) - 1ull))] = k;
+      base += __popcll(mask);
+    }
+    wave_lds_sync();
+    const uint64_t cand = lane < survivors ? buf[lane] : 0;
+    int r = 0;
+    for (int i = 0; i < survivors; ++i) r += buf[i] > cand ? 1 : 0;
+    if (lane < survivors && r < K) buf[64 + r] = cand;
+    wave_lds_sync();
+    mine = lane < K ? buf[64 + lane] : 0;
+    wave_lds_sync();
+  } else {
+    // 2b. many near-equal candidates: 16 rounds of wavefront arg-max
+    uint64_t last = ~0ull;
+    for (int r = 0; r < K; ++r) {
+      uint64_t b = 0;
+      for (int j = lane; j < n; j += 64) {
+        const uint64_t k = score_key(bs[j], j);
+        if (k < last && k > b) b = k;
+      }
+      b = wave_max_u64(b);
+      if (lane == r) mine = b;
+      last = b;
+    }
+  }
+  // 3. ascending block order
+  const int myblk = key_block(mine);
+  int order = 0;
+  for (int i = 0; i < K; ++i) order += key_block(readlane_u64(mine, i)) < myblk ? 1 : 0;
+  if (lane < K) {
+    ids[order] = myblk;
+    if (scores) scores[order] = key_score(mine);
+  }
+  if (lane == 0) {
+    ids[K] = nb - 1;
+    if (scores) scores[K] = canon_score(bs[nb - 1]);
+  }
+}
+
+// QG: 16-row MFMA groups per index head = ceil(8 * q_per_seq / 16).
+template <int QG>
+__global__ __launch_bounds__(512) void indexer_kernel(const IndexerArgs a) {
+  extern __shared__ float part[];  // [2][H][Q][128] per-head partial token scores
+  __shared__ uint2 lut[128];
+  __shared__ uint64_t topk_buf[MSA_MAX_HEADS][80];
+  __shared__ int s_last;
+
+  const int H = a.num_heads;
+  const int Q = a.q_per_seq;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int slice = lane >> 4;  // 32-channel slice of the reduction dimension
+  const int b = blockIdx.y;
+
+  for (int i = threadIdx.x; i < 128; i += blockDim.x) lut[i] = make_uint2(kIdxLut.lo[i], kIdxLut.hi[i]);
+
+  const int L = a.seq_lens[b];
+  const bool seq_ok = L >= Q && L <= a.max_blocks * kBlockTokens;
+  const int nb_last = seq_ok ? (L - 1) / kBlockTokens + 1 : 0;
+  const int blk0 = blockIdx.x * a.blocks_per_wg;
+  const int blk1 = min(nb_last, blk0 + a.blocks_per_wg);
+  const int64_t qrow0 = int64_t(b) * Q;
+  const int Hq = a.num_q_heads;
+
+  // Query operands (rows: query token R/8, head wave*8 + R%8) and weights.
+  v8i qop[QG];
+  float wv[QG][4];
+#pragma unroll
+  for (int rg = 0; rg < QG; ++rg) {
+    const int R = 16 * rg + (lane & 15);
+    const int qi = R >> 3;
+    if (qi < Q) {
+      const uint4* qp = reinterpret_cast<const uint4*>(
+          a.q + ((qrow0 + qi) * Hq + wave * kHeadsPerKv + (R & 7)) * kHeadDim + slice * 32);
+      qop[rg] = q_operand(qp[0], qp[1]);
+    } else {
+      qop[rg] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int R2 = 16 * rg + 4 * slice + v;
+      const int qi2 = R2 >> 3;
+      wv[rg][v] = qi2 < Q ? a.w[(qrow0 + qi2) * Hq + wave * kHeadsPerKv + (R2 & 7)] : 0.0f;
+    }
+  }
+  __syncthreads();
+
+  const int64_t page_codes = int64_t(H) * kCodePage;
+  const int64_t page_scales = int64_t(H) * kScalePage;
+  const uint8_t* codes_h = a.codes + int64_t(wave) * kCodePage + (lane & 15) * kCodeRow + slice * 16;
+  const uint8_t* scales_h = a.scales + int64_t(wave) * kScalePage + (lane & 15) * kScaleRow + slice * 2;
+  const int part_stride = H * Q * kBlockTokens;
+
+  int buf = 0;
+  for (int blk = blk0; blk < blk1; ++blk) {
+    const int page = a.block_table[int64_t(b) * a.max_blocks + blk];
+    const bool page_ok = page >= 0 && page < a.num_pages;
+    uint4 cw[8];
+    uint32_t sw[8];
+    if (page_ok) {
+      const uint8_t* cp = codes_h + int64_t(page) * page_codes;
+      const uint8_t* sp = scales_h + int64_t(page) * page_scales;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        cw[j] = *reinterpret_cast<const uint4*>(cp + j * 16 * kCodeRow);
+        sw[j] = *reinterpret_cast<const uint16_t*>(sp + j * 16 * kScaleRow);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        cw[j] = make_uint4(0, 0, 0, 0);
+        sw[j] = 0;
+      }
+    }
+    float* pw = part + buf * part_stride + wave * Q * kBlockTokens;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const v8i kop = dequant32(cw[j], lut[sw[j] & 0x7F], lut[(sw[j] >> 8) & 0x7F]);
+#pragma unroll
+      for (int rg = 0; rg < QG; ++rg) {
+        const v4f acc = mfma_fp8_16x16x128(qop[rg], kop, v4f{0.0f, 0.0f, 0.0f, 0.0f});
+        float s = wv[rg][0] * fmaxf(acc[0], 0.0f);
+        s += wv[rg][1] * fmaxf(acc[1], 0.0f);
+        s += wv[rg][2] * fmaxf(acc[2], 0.0f);
+        s += wv[rg][3] * fmaxf(acc[3], 0.0f);
+        // lanes l and l^16 hold heads 0-3 and 4-7 of the same query token
+        s += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(s), 0x401F));
+        const int qi = 2 * rg + (lane >> 5);
+        if (!(lane & 16) && qi < Q) pw[qi * kBlockTokens + 16 * j + (lane & 15)] = s;
+      }
+    }
+    __syncthreads();
+    for (int qi = wave; qi < Q; qi += H) {
+      const int pos = L - Q + qi;
+      if (blk * kBlockTokens > pos) continue;  // block not visible to this query token
+      const float* pq = part + buf * part_stride + qi * kBlockTokens;
+      float m = 0.0f;
+      for (int t = lane; t < kBlockTokens; t += 64) {
+        float s = 0.0f;
+        for (int h = 0; h < H; ++h) s += pq[h * Q * kBlockTokens + t];
+        if (blk * kBlockTokens + t <= pos) m = fmaxf(m, s);
+      }
+      m = wave_max(m);
+      if (lane == 0) a.bscore[(qrow0 + qi) * a.max_blocks + blk] = page_ok ? m : 0.0f;
+    }
+    buf ^= 1;
+  }
+
+  // The last workgroup of this sequence to finish selects its blocks.
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = atomicAdd(&a.counters[b], 1u) == gridDim.x - 1 ? 1 : 0;
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  for (int qi = wave; qi < Q; qi += H) {
+    const int64_t row = qrow0 + qi;
+    int32_t* ids = a.out_ids + row * (MSA_TOPK + 1);
+    float* sc = a.out_scores ? a.out_scores + row * (MSA_TOPK + 1) : nullptr;
+    if (!seq_ok) {
+      if (lane < MSA_TOPK + 1) {
+        ids[lane] = -1;
+        if (sc) sc[lane] = 0.0f;
+      }
+      continue;
+    }
+    const int nb = (L - Q + qi) / kBlockTokens + 1;
+    select_blocks(a.bscore + row * a.max_blocks, nb, ids, sc, topk_buf[wave], lane);
+  }
+  if (threadIdx.x == 0) a.counters[b] = 0u;  // ready for the next call
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace msa
+
+extern "C" size_t msa_indexer_workspace_bytes(int32_t num_seqs, int32_t q_per_seq,
+                                              int32_t max_blocks) {
+  if (num_seqs <= 0 || q_per_seq <= 0 || max_blocks <= 0) return 0;
+  return msa::align256(size_t(num_seqs) * 4) +
+         msa::align256(size_t(num_seqs) * q_per_seq * max_blocks * 4);
+}
+
+extern "C" msa_status msa_indexer_decode(const msa_pool_desc* idx, const uint8_t* idx_codes,
+                                         const uint8_t* idx_scales, const uint8_t* q_fp8,
+                                         const float* head_w, int32_t num_q_heads,
+                                         const int32_t* block_table, int32_t max_blocks,
+                                         const int32_t* seq_lens, int32_t num_seqs,
+                                         int32_t q_per_seq, int32_t topk, int32_t* out_ids,
+                                         float* out_scores, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  using namespace msa;
+  if (!idx || num_seqs < 0 || max_blocks <= 0 || q_per_seq <= 0) return MSA_ERR_INVALID_ARG;
+  if (idx->head_dim != MSA_HEAD_DIM || idx->block_tokens != MSA_BLOCK_TOKENS)
+    return MSA_ERR_UNSUPPORTED;
+  if (idx->num_heads < 1 || idx->num_heads > MSA_MAX_HEADS) return MSA_ERR_UNSUPPORTED;
+  if (num_q_heads != MSA_HEADS_PER_KV * idx->num_heads) return MSA_ERR_UNSUPPORTED;
+  if (topk != MSA_TOPK || q_per_seq > MSA_MAX_Q_PER_SEQ) return MSA_ERR_UNSUPPORTED;
+  if (idx->num_pages <= 0 || idx->num_pages > 0x7FFFFFFF) return MSA_ERR_INVALID_ARG;
+  if (int64_t(max_blocks) * MSA_BLOCK_TOKENS > 0x7FFFFFFF) return MSA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return MSA_OK;
+  if (num_seqs > 65535) return MSA_ERR_UNSUPPORTED;
+  if (!idx_codes || !idx_scales || !q_fp8 || !head_w || !block_table || !seq_lens || !out_ids)
+    return MSA_ERR_INVALID_ARG;
+  auto mis = [](const void* p, uintptr_t m) { return (reinterpret_cast<uintptr_t>(p) & m) != 0; };
+  if (mis(idx_codes, 15) || mis(idx_scales, 15) || mis(q_fp8, 15) || mis(head_w, 3) ||
+      mis(block_table, 3) || mis(seq_lens, 3) || mis(out_ids, 3) || mis(out_scores, 3))
+    return MSA_ERR_INVALID_ARG;
+  const size_t need = msa_indexer_workspace_bytes(num_seqs, q_per_seq, max_blocks);
+  if (!workspace || workspace_bytes < need || mis(workspace, 255)) return MSA_ERR_WORKSPACE;
+
+  IndexerArgs a;
+  a.codes = idx_codes;
+  a.scales = idx_scales;
+  a.num_pages = idx->num_pages;
+  a.num_heads = idx->num_heads;
+  a.q = q_fp8;
+  a.w = head_w;
+  a.num_q_heads = num_q_heads;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks;
+  a.seq_lens = seq_lens;
+  a.q_per_seq = q_per_seq;
+  a.counters = static_cast<uint32_t*>(workspace);
+  a.bscore = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(size_t(num_seqs) * 4));
+  a.out_ids = out_ids;
+  a.out_scores = out_scores;
+  // enough workgroups to fill 256 CUs several times over
+  int bpw = 8;
+  while (bpw > 1 && int64_t(num_seqs) * ((max_blocks + bpw - 1) / bpw) < 2048) bpw >>= 1;
+  a.blocks_per_wg = bpw;
+  const dim3 grid((max_blocks + bpw - 1) / bpw, num_seqs);
+  const dim3 block(64 * idx->num_heads);
+  const size_t lds = size_t(2) * idx->num_heads * q_per_seq * MSA_BLOCK_TOKENS * sizeof(float);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int qg = (MSA_HEADS_PER_KV * q_per_seq + 15) / 16;
+  if (qg == 1)
+    hipLaunchKernelGGL(indexer_kernel<1>, grid, block, lds, s, a);
+  else if (qg == 2)
+    hipLaunchKernelGGL(indexer_kernel<2>, grid, block, lds, s, a);
+  else
+    hipLaunchKernelGGL(indexer_kernel<4>, grid, block, lds, s, a);
+  return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
+}

@@ -1,0 +1,102 @@
+// quantize.hip -- msa_nvfp4_quantize: the NVFP4 paged-cache writer.
+//
+// One thread per (token, head, 16-channel group): it reads the group's 64
+// source bytes, picks the E4M3 scale nearest to amax/6 and the E2M1 code of
+// every element, and writes 8 code bytes plus 1 scale byte into the token's
+// page row. Both roundings are decided by exact fp32 comparisons: amax
+// against 6 x (midpoint of two E4M3 values) and |x| against
+// s x (midpoint of two E2M1 values); every such threshold has at most 7
+// significant bits, so no division and no rounding of the thresholds occur.
+// Format: NVFP4 as reproduced by the pages' 34,560 bytes per token
+// (MiniMax-M3.1-Flash lands in vLLM on day one, first paragraph).
+#include "msa_nvfp4.h"
+#include "nvfp4_tile.h"
+
+namespace msa {
+
+__constant__ ScaleThresholds kScaleThr = make_scale_thresholds();
+
+__global__ __launch_bounds__(256) void nvfp4_quantize_kernel(
+    const float* __restrict__ src, const int64_t* __restrict__ slot_mapping, int64_t num_groups,
+    int num_heads, int64_t num_slots, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  __shared__ float thr[128];
+  if (threadIdx.x < 128) thr[threadIdx.x] = kScaleThr.t[threadIdx.x];
+  __syncthreads();
+
+  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= num_groups) return;
+  const int g = int(gid % kScaleRow);
+  const int64_t th = gid / kScaleRow;  // token * num_heads + head
+  const int h = int(th % num_heads);
+  const int64_t t = th / num_heads;
+  const int64_t slot = slot_mapping[t];
+  if (slot < 0 || slot >= num_slots) return;
+
+  const float4* p = reinterpret_cast<const float4*>(src + gid * kGroup);
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 v = p[i];
+    x[4 * i + 0] = v.x;
+    x[4 * i + 1] = v.y;
+    x[4 * i + 2] = v.z;
+    x[4 * i + 3] = v.w;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
+
+  // scale byte = number of thresholds strictly below amax, tie -> even
+  int sb = 0;
+#pragma unroll
+  for (int step = 64; step > 0; step >>= 1)
+    if (thr[sb + step - 1] < amax) sb += step;
+  if (sb < 126 && amax == thr[sb] && (sb & 1)) sb += 1;
+  const float s = e4m3_to_float(sb);
+
+  // E2M1 midpoints times s: exact
+  const float m0 = 0.25f * s, m1 = 0.75f * s, m2 = 1.25f * s, m3 = 1.75f * s;
+  const float m4 = 2.5f * s, m5 = 3.5f * s, m6 = 5.0f * s;
+  uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float a = fabsf(x[i]);
+    int below = (a > m0) + (a > m1) + (a > m2) + (a > m3) + (a > m4) + (a > m5) + (a > m6);
+    const bool tie = (a == m0) | (a == m1) | (a == m2) | (a == m3) | (a == m4) | (a == m5) |
+                     (a == m6);
+    below += (tie & (below & 1)) ? 1 : 0;
+    if (sb == 0) below = 0;
+    const uint32_t nib = (uint32_t(__float_as_uint(x[i]) >> 31) << 3) | uint32_t(below);
+    packed[i >> 3] |= nib << (4 * (i & 7));
+  }
+
+  const int64_t page = slot / kBlockTokens;
+  const int row = int(slot % kBlockTokens);
+  const int64_t head_row = (page * num_heads + h) * kBlockTokens + row;
+  *reinterpret_cast<uint2*>(codes + head_row * kCodeRow + g * 8) = make_uint2(packed[0], packed[1]);
+  scales[head_row * kScaleRow + g] = uint8_t(sb);
+}
+
+}  // namespace msa
+
+extern "C" msa_status msa_nvfp4_quantize(const msa_pool_desc* pool, const float* src,
+                                         const int64_t* slot_mapping, int64_t num_tokens,
+                                         uint8_t* codes, uint8_t* scales, void* stream) {
+  if (!pool || num_tokens < 0) return MSA_ERR_INVALID_ARG;
+  if (pool->head_dim != MSA_HEAD_DIM || pool->block_tokens != MSA_BLOCK_TOKENS)
+    return MSA_ERR_UNSUPPORTED;
+  if (pool->num_heads < 1 || pool->num_heads > MSA_MAX_HEADS) return MSA_ERR_UNSUPPORTED;
+  if (pool->num_pages <= 0) return MSA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return MSA_OK;
+  if (!src || !slot_mapping || !codes || !scales) return MSA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(src) & 15) || (reinterpret_cast<uintptr_t>(codes) & 15) ||
+      (reinterpret_cast<uintptr_t>(slot_mapping) & 7))
+    return MSA_ERR_INVALID_ARG;
+  const int64_t num_groups = num_tokens * pool->num_heads * msa::kScaleRow;
+  const int64_t blocks = (num_groups + 255) / 256;
+  if (blocks > 0x7FFFFFFF) return MSA_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(msa::nvfp4_quantize_kernel, dim3(unsigned(blocks)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), src, slot_mapping, num_groups,
+                     pool->num_heads, pool->num_pages * MSA_BLOCK_TOKENS, codes, scales);
+  return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
+}

@@ -1,0 +1,267 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bytes of the cache writer must match bit for bit; selected ids must pass the
+acceptance rule (exact unless the oracle's 16th/17th gap is below 1e-4
+relative); attention must be within max-abs 2e-2 / mean-abs 2e-3 of the
+oracle evaluated in fp64 on the GPU's ids with identical FP8 operands.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import _support as S
+from msa_workloads import get_config, synth, tiny_config
+from oracle import formats, nvfp4
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module")
+def nb():
+    import nvfp4_kv_cache_amd as m
+    m.lib()
+    return m
+
+
+def _to_np(out):
+    torch.cuda.synchronize()
+    return out["ids"].cpu().numpy(), out["scores"].cpu().numpy(), out["o"].cpu().numpy()
+
+
+def _structural(wl, ids):
+    """Properties of the ids that hold at any size, for every query token."""
+    for b in range(wl.num_seqs):
+        for i, pos in enumerate(wl.positions(b)):
+            r = ids[b * wl.q_per_seq + i]
+            nbk = pos // 128 + 1
+            if nbk <= wl.topk + 1:
+                assert r.tolist() == list(range(nbk)) + [-1] * (wl.topk + 1 - nbk), (b, i, r)
+            else:
+                assert np.all(np.diff(r) > 0) and r[-1] == nbk - 1 and r[0] >= 0, (b, i, r)
+
+
+# ------------------------------------------------------------------ cache writer
+def _special_groups():
+    """fp32 rows [T, 4, 128] with rounding ties, saturation, zeros and -0."""
+    rng = np.random.default_rng(77)
+    x = rng.standard_normal((96, 4, 128)).astype(np.float32)
+    g = x.reshape(-1, 16)
+    n = g.shape[0]
+    for i in range(0, min(n, 126 * 3), 3):              # scale ties and neighbours
+        k = (i // 3) % 125
+        t = np.float32(6.0 * formats.E4M3_MID[k])
+        g[i] = 0
+        g[i, i % 16] = t
+        g[i + 1] = 0
+        g[i + 1, 0] = np.nextafter(t, np.float32(np.inf))
+        g[i + 2] = 0
+        g[i + 2, 5] = -np.nextafter(t, np.float32(0))
+    s = np.float32(1.0)
+    g[400] = np.array([6, .25, .75, 1.25, 1.75, 2.5, 3.5, 5, -.25, -.75, -1.25, -1.75,
+                       -2.5, -3.5, -5, -0.0], dtype=np.float32) * s
+    g[401] = 0.0
+    g[402] = -0.0
+    g[403] = np.float32(3000.0)
+    g[403, 1::2] = -np.float32(2999.0)
+    g[404] = np.float32(-6.0 * 2.0 ** -10)
+    g[405, :] = np.float32(1e-30)
+    return g.reshape(x.shape)
+
+
+def test_quantize_bytes_bit_exact(nb):
+    say("quantize: special groups + skipped/out-of-range slots")
+    x = _special_groups()
+    T = x.shape[0]
+    pages = 3
+    rng = np.random.default_rng(1)
+    slots = rng.permutation(pages * 128)[:T].astype(np.int64)
+    slots[5] = -1
+    slots[6] = pages * 128 + 3          # out of range: skipped
+    codes, scales = nb.empty_pool(pages, 4)
+    codes.fill_(0xAB)
+    scales.fill_(0xCD)
+    nb.msa_nvfp4_quantize(torch.from_numpy(x).cuda(), torch.from_numpy(slots).cuda(), codes,
+                          scales)
+    rc, rs = nvfp4.empty_pool(pages, 4)
+    rc[:] = 0xAB
+    rs[:] = 0xCD
+    ok = (slots >= 0) & (slots < pages * 128)
+    nvfp4.write_cache(rc, rs, x[ok], slots[ok])
+    torch.cuda.synchronize()
+    assert np.array_equal(codes.cpu().numpy(), rc)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+
+
+def test_quantize_empty_is_noop(nb):
+    codes, scales = nb.empty_pool(1, 4)
+    codes.fill_(7)
+    nb.msa_nvfp4_quantize(torch.empty((0, 4, 128), device="cuda"),
+                          torch.empty(0, dtype=torch.int64, device="cuda"), codes, scales)
+    torch.cuda.synchronize()
+    assert int(codes.min()) == 7 == int(codes.max())
+
+
+# ------------------------------------------------------------------ small ragged cases
+TINY = [
+    ([1, 130, 2177, 4099], 1),
+    ([17 * 128, 18 * 128, 17 * 128 + 1, 16 * 128 + 5, 128, 129], 1),
+    ([2, 129, 2400, 3000], 2),
+    ([3, 300, 2200], 3),
+    ([4, 640, 2560 + 1], 4),
+    ([5, 700, 2304], 5),
+    ([8, 135, 2300, 5000], 8),
+    ([8 * 128 + 3, 19 * 128 + 7, 3001], 8),
+]
+
+
+@pytest.mark.parametrize("lens,q", TINY)
+def test_tiny_parity(nb, lens, q):
+    say(f"tiny parity lens={lens} q={q}")
+    wl = tiny_config(lens, q, seed=sum(lens) + q)
+    pools = S.fill_pools(wl, nb)
+    inp = S.device_inputs(wl)
+    ids, sc, o = _to_np(S.run_step(nb, wl, pools, inp))
+    _structural(wl, ids)
+    fails = S.check_page_bytes(wl, pools, np.unique(wl.block_table[wl.block_table >= 0]))
+    for b in range(wl.num_seqs):
+        fails += S.check_sequence(wl, b, ids, sc, o)
+    assert not fails, "\n".join(fails[:20])
+
+
+def test_outlier_channels_parity(nb):
+    say("tiny parity with 5% outlier channels")
+    wl = tiny_config([3000, 4100], 1, seed=5, outliers=True)
+    pools = S.fill_pools(wl, nb)
+    ids, sc, o = _to_np(S.run_step(nb, wl, pools, S.device_inputs(wl)))
+    fails = S.check_page_bytes(wl, pools, wl.pages_in_use())
+    for b in range(wl.num_seqs):
+        fails += S.check_sequence(wl, b, ids, sc, o)
+    assert not fails, "\n".join(fails[:20])
+
+
+# ------------------------------------------------------------------ planted / ties
+def _plant(wl, rows_by_page, coef_by_page):
+    """Override: token row r of page p's index key = coef * sum of the query
+    heads of each index head's group (strongly aligned with every head)."""
+    qv = S.fp8_values(wl.q_idx())[0]          # [32, 128]
+    keys = np.stack([qv[8 * g:8 * g + 8].sum(axis=0) for g in range(4)]).astype(np.float32)
+
+    def ov(stream, pages, src):
+        if stream != synth.STREAM_IDX:
+            return src
+        src = src.clone()
+        for k, p in enumerate(np.asarray(pages).tolist()):
+            if p in rows_by_page:
+                r = rows_by_page[p]
+                src[k * 128 + r] = torch.from_numpy(keys * coef_by_page[p]).to(src.device)
+        return src
+    return ov
+
+
+def test_planted_blocks_and_duplicate_page_tie(nb):
+    say("planted blocks + duplicated page tie")
+    wl = tiny_config([40 * 128], 1, seed=21, spare_pages=0, permute=False)
+    bt = wl.block_table
+    # logical blocks 10 and 25 share one physical page (a shared prefix-like alias)
+    bt[0, 25] = bt[0, 10]
+    planted = [2, 4, 5, 7, 9, 13, 15, 17, 19, 22, 27, 30, 33, 35, 38]   # 15 blocks
+    rows = {int(bt[0, j]): (7 * j) % 128 for j in planted + [10]}
+    coef = {int(bt[0, j]): 1.0 for j in planted}
+    coef[int(bt[0, 10])] = 0.5                      # 16th place, tied between 10 and 25
+    ov = _plant(wl, rows, coef)
+    pools = S.fill_pools(wl, nb, overrides=ov)
+    ids, sc, o = _to_np(S.run_step(nb, wl, pools, S.device_inputs(wl)))
+    assert ids[0].tolist() == sorted(planted + [10]) + [39]
+    fails = S.check_sequence(wl, 0, ids, sc, o, overrides=ov)
+    assert not fails, "\n".join(fails)
+
+
+# ------------------------------------------------------------------ device-side checks
+def test_invalid_lengths_and_pages_do_not_fault(nb):
+    say("invalid lengths / page ids")
+    wl = tiny_config([3000, 2500, 2600, 2700], 2, seed=8)
+    pools = S.fill_pools(wl, nb)
+    inp = S.device_inputs(wl)
+    lens = inp["seq_lens"].clone()
+    lens[1] = 1                                   # shorter than q_per_seq
+    lens[2] = wl.max_blocks * 128 + 1             # longer than the block table
+    inp["seq_lens"] = lens
+    bt = inp["block_table"].clone()
+    bt[3, 2] = wl.num_pages + 7                   # page ids out of range
+    bt[3, 5] = -3
+    inp["block_table"] = bt
+    ids, sc, o = _to_np(S.run_step(nb, wl, pools, inp))
+    for b in (1, 2):
+        assert np.all(ids[2 * b:2 * b + 2] == -1)
+        assert np.all(o[2 * b:2 * b + 2] == 0)
+    assert np.all(np.isfinite(o))
+    assert np.all(sc[6:8][ids[6:8] == 2] == 0) and np.all(sc[6:8][ids[6:8] == 5] == 0)
+    fails = S.check_sequence(wl, 0, ids, sc, o)
+    assert not fails, "\n".join(fails)
+
+
+def test_deterministic_and_reusable_workspace(nb):
+    say("determinism over repeated calls with one workspace")
+    wl = tiny_config([5000, 3001, 129], 8, seed=3)
+    pools = S.fill_pools(wl, nb)
+    inp = S.device_inputs(wl)
+    ws_i = nb.indexer_workspace(wl.num_seqs, wl.q_per_seq, wl.max_blocks)
+    ws_a = nb.attn_workspace(wl.num_seqs, wl.q_per_seq, wl.num_q_heads, wl.topk + 1)
+    first = _to_np(S.run_step(nb, wl, pools, inp, ws_i, ws_a))
+    for _ in range(3):
+        again = _to_np(S.run_step(nb, wl, pools, inp, ws_i, ws_a))
+        for x, y in zip(first, again):
+            assert np.array_equal(x, y)
+    assert int(ws_i[:256].abs().sum()) == 0       # counters back at zero
+
+
+def test_empty_batch_and_bad_shapes(nb):
+    wl = tiny_config([300], 1)
+    pools = S.fill_pools(wl, nb)
+    ic, isc = pools[synth.STREAM_IDX]
+    z = torch.empty((0, 32, 128), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    nb.msa_indexer_decode(ic, isc, z, torch.empty((0, 32), device="cuda"),
+                          torch.empty((0, 4), dtype=torch.int32, device="cuda"),
+                          torch.empty(0, dtype=torch.int32, device="cuda"), 1,
+                          torch.empty((0, 17), dtype=torch.int32, device="cuda"), ws)
+    inp = S.device_inputs(wl)
+    with pytest.raises(nb.MsaError):
+        nb.msa_indexer_decode(ic, isc, inp["q_idx"], inp["w"], inp["block_table"],
+                              inp["seq_lens"], 1,
+                              torch.empty((1, 17), dtype=torch.int32, device="cuda"),
+                              torch.zeros(16, dtype=torch.uint8, device="cuda"))
+
+
+# ------------------------------------------------------------------ the five workloads
+SAMPLES = {0: [0], 1: [0, 19], 2: [5], 3: [2, 11], 4: None}
+
+
+@pytest.mark.parametrize("ci", [0, 1, 2, 3, 4])
+def test_workload_parity(nb, ci):
+    wl = get_config(ci)
+    say(f"workload {ci} {wl.name}: filling pools")
+    pools = S.fill_pools(wl, nb)
+    inp = S.device_inputs(wl)
+    say(f"workload {ci}: decode step")
+    ids, sc, o = _to_np(S.run_step(nb, wl, pools, inp))
+    _structural(wl, ids)
+    assert np.all(np.isfinite(o))
+    seqs = SAMPLES[ci]
+    if seqs is None:                               # shortest and longest request
+        seqs = [int(np.argmin(wl.seq_lens)), int(np.argmax(wl.seq_lens))]
+    rng = np.random.default_rng(ci)
+    used = wl.pages_in_use()
+    pages = rng.choice(used, size=min(6, len(used)), replace=False)
+    say(f"workload {ci}: page bytes {pages.tolist()}")
+    fails = S.check_page_bytes(wl, pools, pages)
+    for b in seqs:
+        say(f"workload {ci}: oracle on sequence {b} (length {wl.seq_lens[b]})")
+        fails += S.check_sequence(wl, b, ids, sc, o)
+    assert not fails, "\n".join(fails[:20])

@@ -1,0 +1,101 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/msa_nvfp4.h declares, sizes workspaces, and rejects
+bad arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa_nvfp4.h")
+
+nb = pytest.importorskip("nvfp4_kv_cache_amd")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(nb.LIB_PATH):
+        pytest.skip("library not built")
+    return nb.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert {"msa_nvfp4_quantize", "msa_indexer_decode", "msa_sparse_attn_decode"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in nb.binding.SIGNATURES, f"binding lacks {n}"
+
+
+def test_status_strings(L):
+    for s in range(5):
+        assert nb.msa_status_string(s).startswith("MSA_")
+    assert "unknown" in nb.msa_status_string(99)
+
+
+def test_workspace_sizes(L):
+    assert nb.msa_indexer_workspace_bytes(8, 1, 2048) == 256 + 8 * 2048 * 4
+    assert nb.msa_indexer_workspace_bytes(0, 1, 10) == 0
+    rows = 16 * 8 * 32
+    want = rows * 4 + rows * 17 * 128 * 4 + rows * 17 * 2 * 4
+    got = nb.msa_attn_workspace_bytes(16, 8, 32, 17)
+    assert want <= got <= want + 3 * 255
+
+
+def _desc(heads=4, d=128, bt=128, pages=10):
+    return nb.PoolDesc(heads, d, bt, 0, pages)
+
+
+def test_quantize_rejects_before_launch(L):
+    f = L.msa_nvfp4_quantize
+    assert f(None, None, None, 1, None, None, None) == 1
+    assert f(ctypes.byref(_desc(d=64)), None, None, 1, None, None, None) == 2
+    assert f(ctypes.byref(_desc(heads=9)), None, None, 1, None, None, None) == 2
+    assert f(ctypes.byref(_desc()), None, None, -1, None, None, None) == 1
+    assert f(ctypes.byref(_desc()), None, None, 0, None, None, None) == 0      # no-op
+    assert f(ctypes.byref(_desc()), None, None, 5, None, None, None) == 1      # null buffers
+    assert f(ctypes.byref(_desc()), 16, 8, 5, 3, 16, None) == 1                # misaligned codes
+
+
+def test_indexer_rejects_before_launch(L):
+    f = L.msa_indexer_decode
+    d = ctypes.byref(_desc())
+    ok = dict(q=32, mb=4, ns=1, qps=1, topk=16)
+
+    def call(desc=d, q=32, mb=4, ns=1, qps=1, topk=16, ptr=256, ws=None, wsb=0):
+        return f(desc, ptr, ptr, ptr, ptr, q, ptr, mb, ptr, ns, qps, topk, ptr, None,
+                 ws, wsb, None)
+    assert call(desc=None) == 1
+    assert call(q=16) == 2                       # not 8 query heads per index head
+    assert call(topk=8) == 2
+    assert call(qps=9) == 2
+    assert call(qps=0) == 1
+    assert call(ns=0) == 0
+    assert call(ptr=None) == 1
+    assert call(ptr=4096 + 8) == 1               # misaligned
+    assert call(ws=None) == 3                    # workspace missing
+    assert call(ws=4096, wsb=16) == 3            # too small
+    assert call(desc=ctypes.byref(_desc(bt=64))) == 2
+
+
+def test_attention_rejects_before_launch(L):
+    f = L.msa_sparse_attn_decode
+    d = ctypes.byref(_desc())
+
+    def call(desc=d, q=32, mb=4, ns=1, qps=1, nsel=17, scale=0.088, ptr=256, ws=None, wsb=0):
+        return f(desc, ptr, ptr, ptr, ptr, ptr, q, ptr, mb, ptr, ns, qps, ptr, nsel, scale,
+                 ptr, ws, wsb, None)
+    assert call(desc=None) == 1
+    assert call(q=24) == 2
+    assert call(nsel=0) == 2 and call(nsel=65) == 2
+    assert call(scale=0.0) == 1 and call(scale=float("nan")) == 1
+    assert call(ns=0) == 0
+    assert call(ptr=None) == 1
+    assert call(ws=None) == 3
