@@ -23,8 +23,9 @@
  *  - Every pointer argument is DEVICE memory owned by the caller, except the
  *    msa_pool_desc pointers, which are host memory read during the call.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
- *    stream). The library allocates nothing and keeps no state between calls;
- *    two calls may run concurrently only if they use different workspaces.
+ *    stream); an entry point enqueues one or two kernels on it. The library
+ *    allocates nothing and keeps no state between calls; two calls may run
+ *    concurrently only if they use different workspaces.
  *  - Arguments are checked on the host before anything is launched; a failed
  *    check returns a status and launches nothing. MSA_ERR_HIP reports a failed
  *    kernel launch. Device data (block tables, sequence lengths, selected ids,
@@ -106,10 +107,8 @@ msa_status msa_nvfp4_quantize(const msa_pool_desc* pool, const float* src,
                               uint8_t* codes, uint8_t* scales, void* stream);
 
 /*
- * Workspace bytes msa_indexer_decode needs (block scores and per-sequence
- * completion counters). The workspace must be zero-filled before its first
- * use; every call leaves its counters at zero again, so one zero-fill at
- * allocation is enough.
+ * Workspace bytes msa_indexer_decode needs: the fp32 block scores
+ * [num_seqs * q_per_seq][max_blocks]. No initial contents are required.
  */
 size_t msa_indexer_workspace_bytes(int32_t num_seqs, int32_t q_per_seq, int32_t max_blocks);
 
@@ -145,8 +144,9 @@ msa_status msa_indexer_decode(const msa_pool_desc* idx, const uint8_t* idx_codes
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Workspace bytes msa_sparse_attn_decode needs (split partial results and
- * completion counters). Same zero-fill rule as the indexer's workspace.
+ * Workspace bytes msa_sparse_attn_decode needs: split partial results
+ * (running max, denominator and unnormalised output per split). No initial
+ * contents are required.
  */
 size_t msa_attn_workspace_bytes(int32_t num_seqs, int32_t q_per_seq, int32_t num_q_heads,
                                 int32_t num_sel);

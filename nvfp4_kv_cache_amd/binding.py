@@ -144,15 +144,15 @@ def msa_attn_workspace_bytes(num_seqs: int, q_per_seq: int, num_q_heads: int, nu
 
 
 def indexer_workspace(num_seqs, q_per_seq, max_blocks, device="cuda"):
-    """Zero-filled workspace for msa_indexer_decode (zeroed once; calls keep it reusable)."""
+    """Workspace for msa_indexer_decode (contents need no initialisation)."""
     n = msa_indexer_workspace_bytes(num_seqs, q_per_seq, max_blocks)
-    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
 def attn_workspace(num_seqs, q_per_seq, num_q_heads, num_sel, device="cuda"):
-    """Zero-filled workspace for msa_sparse_attn_decode."""
+    """Workspace for msa_sparse_attn_decode (contents need no initialisation)."""
     n = msa_attn_workspace_bytes(num_seqs, q_per_seq, num_q_heads, num_sel)
-    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
 def msa_indexer_decode(idx_codes, idx_scales, q_fp8, head_w, block_table, seq_lens, q_per_seq,

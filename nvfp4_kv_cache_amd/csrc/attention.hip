@@ -43,18 +43,10 @@ struct AttnArgs {
   float scale_log2;  // softmax_scale * log2(e)
   float* part_o;     // [T_q * Hq][num_splits][128]
   float* part_ml;    // [T_q * Hq][num_splits][2]
-  uint32_t* counters;  // [T_q * Hq] (one per (query token, KV head) used)
   float* out;
 };
 
-// E4M3 byte -> fp32 (exact), from the format definition.
-__device__ __forceinline__ float fp8_to_float(uint32_t b) {
-  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-  float v = e == 0 ? float(m) * (1.0f / 512.0f)
-                   : __uint_as_float(((e + 120u) << 23) | (m << 20));
-  if (e == 15u && m == 7u) v = __builtin_nanf("");
-  return (b & 0x80u) ? -v : v;
-}
+typedef float v2f __attribute__((ext_vector_type(2)));
 
 constexpr int kAttnThreads = 256;
 
@@ -63,7 +55,7 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(const AttnArg
   __shared__ float vs[kBlockTokens][kHeadDim];   // dequantised V of one block
   __shared__ float zs[kHeadsPerKv][kBlockTokens];  // logits, then probabilities
   __shared__ float alpha_s[kHeadsPerKv];
-  __shared__ int s_last;
+  __shared__ float s_m[kHeadsPerKv][64], s_l[kHeadsPerKv][64];
 
   const int qt = blockIdx.z, kh = blockIdx.y, sp = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, slice = lane >> 4;
@@ -128,19 +120,20 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(const AttnArg
           zs[4 * slice + v][t] = t < ntok ? z[v] * a.scale_log2 : -__builtin_huge_valf();
       }
       // V: 32 channels of token t, restored to natural channel order
+      // (dequant32 yields channels 0,2,4,6 then 1,3,5,7 of each run of 8)
       const v8i vop = dequant32(vc, lut[vsc & 0x7F], lut[(vsc >> 8) & 0x7F]);
       float* dst = &vs[t][slice * 32];
+      const bool live = t < ntok;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const uint32_t ev = uint32_t(vop[2 * u]), od = uint32_t(vop[2 * u + 1]);
-        float f[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          f[2 * i] = t < ntok ? fp8_to_float((ev >> (8 * i)) & 0xFFu) : 0.0f;
-          f[2 * i + 1] = t < ntok ? fp8_to_float((od >> (8 * i)) & 0xFFu) : 0.0f;
-        }
-        *reinterpret_cast<float4*>(dst + 8 * u) = make_float4(f[0], f[1], f[2], f[3]);
-        *reinterpret_cast<float4*>(dst + 8 * u + 4) = make_float4(f[4], f[5], f[6], f[7]);
+        const v2f e01 = __builtin_amdgcn_cvt_pk_f32_fp8(vop[2 * u], false);     // ch 0, 2
+        const v2f e23 = __builtin_amdgcn_cvt_pk_f32_fp8(vop[2 * u], true);      // ch 4, 6
+        const v2f o01 = __builtin_amdgcn_cvt_pk_f32_fp8(vop[2 * u + 1], false); // ch 1, 3
+        const v2f o23 = __builtin_amdgcn_cvt_pk_f32_fp8(vop[2 * u + 1], true);  // ch 5, 7
+        const float4 lo = live ? make_float4(e01.x, o01.x, e01.y, o01.y) : make_float4(0, 0, 0, 0);
+        const float4 hi = live ? make_float4(e23.x, o23.x, e23.y, o23.y) : make_float4(0, 0, 0, 0);
+        *reinterpret_cast<float4*>(dst + 8 * u) = lo;
+        *reinterpret_cast<float4*>(dst + 8 * u + 4) = hi;
       }
     }
     __syncthreads();
@@ -175,52 +168,75 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(const AttnArg
     __syncthreads();
   }
 
-  // this split's partial result
   const int64_t row = int64_t(qt) * Hq + kh * kHeadsPerKv;  // first query head row
-  {
-    float* po = a.part_o + ((row + ph) * a.num_splits + sp) * kHeadDim + pd;
-    *reinterpret_cast<float4*>(po) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    if (lane == 0) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        float* pm = a.part_ml + ((row + 2 * wave + hh) * a.num_splits + sp) * 2;
-        pm[0] = m_run[hh];
-        pm[1] = l_run[hh];
-      }
-    }
+  // per-head (m, l) of this wave's two heads go through LDS to the P x V threads
+  if (lane == 0) {
+    s_m[2 * wave][0] = m_run[0];
+    s_m[2 * wave + 1][0] = m_run[1];
+    s_l[2 * wave][0] = l_run[0];
+    s_l[2 * wave + 1][0] = l_run[1];
   }
-  __threadfence();
   __syncthreads();
-  uint32_t* ctr = a.counters + int64_t(qt) * a.num_kv_heads + kh;
-  if (tid == 0) s_last = atomicAdd(ctr, 1u) == uint32_t(a.num_splits - 1) ? 1 : 0;
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  // merge the splits of head row+ph, channels pd..pd+3
-  {
-    const float* pm = a.part_ml + (row + ph) * a.num_splits * 2;
-    float M = -__builtin_huge_valf();
-    for (int s = 0; s < a.num_splits; ++s) M = fmaxf(M, pm[2 * s]);
-    float o[4] = {0.0f, 0.0f, 0.0f, 0.0f}, den = 0.0f;
-    if (M != -__builtin_huge_valf()) {
-      for (int s = 0; s < a.num_splits; ++s) {
-        const float ms = pm[2 * s];
-        if (ms == -__builtin_huge_valf()) continue;
-        const float f = exp2f(ms - M);
-        den += f * pm[2 * s + 1];
-        const float4 v = *reinterpret_cast<const float4*>(
-            a.part_o + ((row + ph) * a.num_splits + s) * kHeadDim + pd);
-        o[0] += f * v.x;
-        o[1] += f * v.y;
-        o[2] += f * v.z;
-        o[3] += f * v.w;
-      }
-    }
-    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+  if (a.num_splits == 1) {
+    const float l = s_l[ph][0];
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     *reinterpret_cast<float4*>(a.out + (row + ph) * kHeadDim + pd) =
-        make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+        make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+    return;
   }
-  if (tid == 0) *ctr = 0u;
+  float* po = a.part_o + ((row + ph) * a.num_splits + sp) * kHeadDim + pd;
+  *reinterpret_cast<float4*>(po) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  if ((tid & 31) == 0) {
+    float* pm = a.part_ml + ((row + ph) * a.num_splits + sp) * 2;
+    pm[0] = s_m[ph][0];
+    pm[1] = s_l[ph][0];
+  }
+}
+
+// Merge kernel: one workgroup per (query token, KV head); thread (h, 4 ch)
+// combines the splits' (m, l, o) by log-sum-exp. Every (m, l) and every
+// partial o is fetched with independent loads.
+__global__ __launch_bounds__(kAttnThreads) void merge_kernel(const float* __restrict__ part_o,
+                                                             const float* __restrict__ part_ml,
+                                                             int num_splits, float* __restrict__ out) {
+  __shared__ float s_m[kHeadsPerKv][64], s_l[kHeadsPerKv][64];
+  const int tid = threadIdx.x;
+  const int64_t row = int64_t(blockIdx.x) * kHeadsPerKv;  // first query head row
+  for (int i = tid; i < kHeadsPerKv * num_splits; i += kAttnThreads) {
+    const int h = i / num_splits, sidx = i - h * num_splits;
+    const float2 ml = *reinterpret_cast<const float2*>(part_ml + ((row + h) * num_splits + sidx) * 2);
+    s_m[h][sidx] = ml.x;
+    s_l[h][sidx] = ml.y;
+  }
+  __syncthreads();
+  const int ph = tid >> 5, pd = (tid & 31) * 4;
+  float M = -__builtin_huge_valf();
+  for (int sidx = 0; sidx < num_splits; ++sidx) M = fmaxf(M, s_m[ph][sidx]);
+  float o[4] = {0.0f, 0.0f, 0.0f, 0.0f}, den = 0.0f;
+  if (M != -__builtin_huge_valf()) {
+    const float* po = part_o + (row + ph) * num_splits * kHeadDim + pd;
+    for (int s0 = 0; s0 < num_splits; s0 += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        v[k] = s0 + k < num_splits ? *reinterpret_cast<const float4*>(po + (s0 + k) * kHeadDim)
+                                   : make_float4(0, 0, 0, 0);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (s0 + k >= num_splits) break;
+        const float ms = s_m[ph][s0 + k];
+        const float f = ms == -__builtin_huge_valf() ? 0.0f : exp2f(ms - M);
+        den += f * s_l[ph][s0 + k];
+        o[0] += f * v[k].x;
+        o[1] += f * v[k].y;
+        o[2] += f * v[k].z;
+        o[3] += f * v[k].w;
+      }
+    }
+  }
+  const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+  *reinterpret_cast<float4*>(out + (row + ph) * kHeadDim + pd) =
+      make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -239,9 +255,8 @@ extern "C" size_t msa_attn_workspace_bytes(int32_t num_seqs, int32_t q_per_seq,
                                            int32_t num_q_heads, int32_t num_sel) {
   if (num_seqs <= 0 || q_per_seq <= 0 || num_q_heads <= 0 || num_sel <= 0) return 0;
   const size_t rows = size_t(num_seqs) * q_per_seq * num_q_heads;
-  // counters, partial o (up to num_sel splits), partial (m, l)
-  return msa::align256(rows * 4) + msa::align256(rows * num_sel * MSA_HEAD_DIM * 4) +
-         msa::align256(rows * num_sel * 2 * 4);
+  // partial o and partial (m, l) for up to num_sel splits
+  return msa::align256(rows * num_sel * MSA_HEAD_DIM * 4) + msa::align256(rows * num_sel * 2 * 4);
 }
 
 extern "C" msa_status msa_sparse_attn_decode(const msa_pool_desc* kv, const uint8_t* k_codes,
@@ -295,13 +310,17 @@ extern "C" msa_status msa_sparse_attn_decode(const msa_pool_desc* kv, const uint
   attn_splits(tq * kv->num_heads, num_sel, &a.blocks_per_split, &a.num_splits);
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   char* ws = static_cast<char*>(workspace);
-  a.counters = reinterpret_cast<uint32_t*>(ws);
-  a.part_o = reinterpret_cast<float*>(ws + align256(rows * 4));
-  a.part_ml = reinterpret_cast<float*>(ws + align256(rows * 4) +
-                                       align256(rows * num_sel * MSA_HEAD_DIM * 4));
+  a.part_o = reinterpret_cast<float*>(ws);
+  a.part_ml = reinterpret_cast<float*>(ws + align256(rows * num_sel * MSA_HEAD_DIM * 4));
   a.out = out;
   const dim3 grid(a.num_splits, kv->num_heads, unsigned(tq));
-  hipLaunchKernelGGL(sparse_attn_kernel, grid, dim3(kAttnThreads), 0,
-                     static_cast<hipStream_t>(stream), a);
-  return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(sparse_attn_kernel, grid, dim3(kAttnThreads), 0, s, a);
+  if (hipGetLastError() != hipSuccess) return MSA_ERR_HIP;
+  if (a.num_splits > 1) {
+    hipLaunchKernelGGL(merge_kernel, dim3(unsigned(tq * kv->num_heads)), dim3(kAttnThreads), 0, s,
+                       a.part_o, a.part_ml, a.num_splits, out);
+    if (hipGetLastError() != hipSuccess) return MSA_ERR_HIP;
+  }
+  return MSA_OK;
 }

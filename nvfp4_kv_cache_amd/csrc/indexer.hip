@@ -42,7 +42,6 @@ struct IndexerArgs {
   int q_per_seq;
   int blocks_per_wg;
   float* bscore;       // [num_seqs * q_per_seq][max_blocks]
-  uint32_t* counters;  // [num_seqs]
   int32_t* out_ids;
   float* out_scores;
 };
@@ -57,8 +56,10 @@ __device__ __forceinline__ int key_block(uint64_t k) { return int(0xFFFFFFFFu - 
 __device__ __forceinline__ float key_score(uint64_t k) { return __uint_as_float(uint32_t(k >> 32)); }
 
 // Top-16 of blocks 0..nb-2 plus block nb-1, ascending, for one query token;
-// executed by one whole wavefront. buf: 80 wave-private LDS slots.
-__device__ void select_blocks(const float* __restrict__ bs, int nb, int32_t* __restrict__ ids,
+// executed by one whole wavefront. `bs` holds the nb block scores, normally
+// staged in LDS by the workgroup (a generic pointer: LDS or global memory).
+// buf: 80 wave-private LDS slots.
+__device__ void select_blocks(const float* bs, int nb, int32_t* __restrict__ ids,
                               float* __restrict__ scores, uint64_t* buf, int lane) {
   constexpr int K = MSA_TOPK;
   if (nb <= K + 1) {
@@ -73,8 +74,8 @@ __device__ void select_blocks(const float* __restrict__ bs, int nb, int32_t* __r
   //    keys are >= theta, so the top-16 are among the keys >= theta.
   uint64_t best = 0;
   for (int j = lane; j < n; j += 64) {
-    const uint64_t k = score_key(bs[j], j);
-    best = k > best ? k : best;
+    const uint64_t key = score_key(bs[j], j);
+    best = key > best ? key : best;
   }
   int rank = 0;
   for (int src = 0; src < 64; ++src) rank += readlane_u64(best, src) > best ? 1 : 0;
@@ -90,10 +91,10 @@ __device__ void select_blocks(const float* __restrict__ bs, int nb, int32_t* __r
     int base = 0;
     for (int j0 = 0; j0 < n; j0 += 64) {
       const int j = j0 + lane;
-      const uint64_t k = j < n ? score_key(bs[j], j) : 0;
-      const bool p = j < n && k >= theta;
+      const uint64_t key = j < n ? score_key(bs[j], j) : 0ull;
+      const bool p = j < n && key >= theta;
       const uint64_t mask = __ballot(p);
-      if (p) buf[base + __popcll(mask & ((1ull << lane) - 1ull))] = k;
+      if (p) buf[base + __popcll(mask & ((1ull << lane) - 1ull))] = key;
       base += __popcll(mask);
     }
     wave_lds_sync();
@@ -110,8 +111,8 @@ __device__ void select_blocks(const float* __restrict__ bs, int nb, int32_t* __r
     for (int r = 0; r < K; ++r) {
       uint64_t b = 0;
       for (int j = lane; j < n; j += 64) {
-        const uint64_t k = score_key(bs[j], j);
-        if (k < last && k > b) b = k;
+        const uint64_t key = score_key(bs[j], j);
+        if (key < last && key > b) b = key;
       }
       b = wave_max_u64(b);
       if (lane == r) mine = b;
@@ -132,13 +133,43 @@ __device__ void select_blocks(const float* __restrict__ bs, int nb, int32_t* __r
   }
 }
 
+// Block scores of all query tokens of a sequence staged in LDS when they fit.
+constexpr int kStageFloats = 12288;  // 48 KiB of LDS
+
+constexpr int kMaxBlocksPerWg = 16;
+
+// One block's worth of this wave's loads: 8 tiles x (16 code bytes, 2 scale
+// bytes) per lane.
+struct TileLoads {
+  uint4 c[8];
+  uint32_t s[8];
+};
+
+__device__ __forceinline__ void issue_loads(TileLoads& t, const uint8_t* codes_h,
+                                            const uint8_t* scales_h, int page, int64_t page_codes,
+                                            int64_t page_scales) {
+  if (page >= 0) {
+    const uint8_t* cp = codes_h + int64_t(page) * page_codes;
+    const uint8_t* sp = scales_h + int64_t(page) * page_scales;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t.c[j] = *reinterpret_cast<const uint4*>(cp + j * 16 * kCodeRow);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t.s[j] = *reinterpret_cast<const uint16_t*>(sp + j * 16 * kScaleRow);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      t.c[j] = make_uint4(0, 0, 0, 0);
+      t.s[j] = 0;
+    }
+  }
+}
+
 // QG: 16-row MFMA groups per index head = ceil(8 * q_per_seq / 16).
 template <int QG>
 __global__ __launch_bounds__(512) void indexer_kernel(const IndexerArgs a) {
-  extern __shared__ float part[];  // [2][H][Q][128] per-head partial token scores
+  extern __shared__ float part[];  // [2][H][2*QG][128] per-head partial token scores
   __shared__ uint2 lut[128];
-  __shared__ uint64_t topk_buf[MSA_MAX_HEADS][80];
-  __shared__ int s_last;
+  __shared__ int pages[kMaxBlocksPerWg];
 
   const int H = a.num_heads;
   const int Q = a.q_per_seq;
@@ -146,6 +177,7 @@ __global__ __launch_bounds__(512) void indexer_kernel(const IndexerArgs a) {
   const int lane = threadIdx.x & 63;
   const int slice = lane >> 4;  // 32-channel slice of the reduction dimension
   const int b = blockIdx.y;
+  constexpr int QR = 2 * QG;    // query-token rows of the partial buffer
 
   for (int i = threadIdx.x; i < 128; i += blockDim.x) lut[i] = make_uint2(kIdxLut.lo[i], kIdxLut.hi[i]);
 
@@ -156,6 +188,10 @@ __global__ __launch_bounds__(512) void indexer_kernel(const IndexerArgs a) {
   const int blk1 = min(nb_last, blk0 + a.blocks_per_wg);
   const int64_t qrow0 = int64_t(b) * Q;
   const int Hq = a.num_q_heads;
+  if (int(threadIdx.x) < blk1 - blk0) {
+    const int p = a.block_table[int64_t(b) * a.max_blocks + blk0 + threadIdx.x];
+    pages[threadIdx.x] = (p >= 0 && p < a.num_pages) ? p : -1;
+  }
 
   // Query operands (rows: query token R/8, head wave*8 + R%8) and weights.
   v8i qop[QG];
@@ -184,85 +220,112 @@ __global__ __launch_bounds__(512) void indexer_kernel(const IndexerArgs a) {
   const int64_t page_scales = int64_t(H) * kScalePage;
   const uint8_t* codes_h = a.codes + int64_t(wave) * kCodePage + (lane & 15) * kCodeRow + slice * 16;
   const uint8_t* scales_h = a.scales + int64_t(wave) * kScalePage + (lane & 15) * kScaleRow + slice * 2;
-  const int part_stride = H * Q * kBlockTokens;
+  const int part_stride = H * QR * kBlockTokens;
+  // every lane writes its token's partial; lanes l and l^16 hold equal sums
+  const int part_lane = (lane >> 5) * kBlockTokens + (lane & 15);
 
-  int buf = 0;
-  for (int blk = blk0; blk < blk1; ++blk) {
-    const int page = a.block_table[int64_t(b) * a.max_blocks + blk];
-    const bool page_ok = page >= 0 && page < a.num_pages;
-    uint4 cw[8];
-    uint32_t sw[8];
-    if (page_ok) {
-      const uint8_t* cp = codes_h + int64_t(page) * page_codes;
-      const uint8_t* sp = scales_h + int64_t(page) * page_scales;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        cw[j] = *reinterpret_cast<const uint4*>(cp + j * 16 * kCodeRow);
-        sw[j] = *reinterpret_cast<const uint16_t*>(sp + j * 16 * kScaleRow);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        cw[j] = make_uint4(0, 0, 0, 0);
-        sw[j] = 0;
-      }
-    }
-    float* pw = part + buf * part_stride + wave * Q * kBlockTokens;
+  // dequantise, multiply, apply ReLU and weights; per-head partials to LDS
+  auto compute = [&](const TileLoads& t, int buf) {
+    float* pw = part + buf * part_stride + wave * QR * kBlockTokens + part_lane;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const v8i kop = dequant32(cw[j], lut[sw[j] & 0x7F], lut[(sw[j] >> 8) & 0x7F]);
+      const v8i kop = dequant32(t.c[j], lut[t.s[j] & 0x7F], lut[(t.s[j] >> 8) & 0x7F]);
 #pragma unroll
       for (int rg = 0; rg < QG; ++rg) {
         const v4f acc = mfma_fp8_16x16x128(qop[rg], kop, v4f{0.0f, 0.0f, 0.0f, 0.0f});
-        float s = wv[rg][0] * fmaxf(acc[0], 0.0f);
-        s += wv[rg][1] * fmaxf(acc[1], 0.0f);
-        s += wv[rg][2] * fmaxf(acc[2], 0.0f);
-        s += wv[rg][3] * fmaxf(acc[3], 0.0f);
+        float s = wv[rg][0] * (acc[0] > 0.0f ? acc[0] : 0.0f);
+        s += wv[rg][1] * (acc[1] > 0.0f ? acc[1] : 0.0f);
+        s += wv[rg][2] * (acc[2] > 0.0f ? acc[2] : 0.0f);
+        s += wv[rg][3] * (acc[3] > 0.0f ? acc[3] : 0.0f);
         // lanes l and l^16 hold heads 0-3 and 4-7 of the same query token
         s += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(s), 0x401F));
-        const int qi = 2 * rg + (lane >> 5);
-        if (!(lane & 16) && qi < Q) pw[qi * kBlockTokens + 16 * j + (lane & 15)] = s;
+        pw[2 * rg * kBlockTokens + 16 * j] = s;
       }
     }
-    __syncthreads();
+  };
+  // sum the heads, maximise over the block's visible tokens, store B(blk)
+  auto reduce = [&](int blk, int buf) {
+    const bool page_ok = pages[blk - blk0] >= 0;
     for (int qi = wave; qi < Q; qi += H) {
       const int pos = L - Q + qi;
       if (blk * kBlockTokens > pos) continue;  // block not visible to this query token
       const float* pq = part + buf * part_stride + qi * kBlockTokens;
       float m = 0.0f;
+#pragma unroll
       for (int t = lane; t < kBlockTokens; t += 64) {
         float s = 0.0f;
-        for (int h = 0; h < H; ++h) s += pq[h * Q * kBlockTokens + t];
+        for (int h = 0; h < H; ++h) s += pq[h * QR * kBlockTokens + t];
         if (blk * kBlockTokens + t <= pos) m = fmaxf(m, s);
       }
       m = wave_max(m);
       if (lane == 0) a.bscore[(qrow0 + qi) * a.max_blocks + blk] = page_ok ? m : 0.0f;
     }
-    buf ^= 1;
-  }
+  };
 
-  // The last workgroup of this sequence to finish selects its blocks.
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = atomicAdd(&a.counters[b], 1u) == gridDim.x - 1 ? 1 : 0;
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  for (int qi = wave; qi < Q; qi += H) {
-    const int64_t row = qrow0 + qi;
-    int32_t* ids = a.out_ids + row * (MSA_TOPK + 1);
-    float* sc = a.out_scores ? a.out_scores + row * (MSA_TOPK + 1) : nullptr;
-    if (!seq_ok) {
-      if (lane < MSA_TOPK + 1) {
-        ids[lane] = -1;
-        if (sc) sc[lane] = 0.0f;
-      }
-      continue;
-    }
-    const int nb = (L - Q + qi) / kBlockTokens + 1;
-    select_blocks(a.bscore + row * a.max_blocks, nb, ids, sc, topk_buf[wave], lane);
+  // two-stage pipeline: the next block's loads are in flight while the
+  // current block is computed
+  TileLoads ta, tb;
+  if (blk0 < blk1) issue_loads(ta, codes_h, scales_h, pages[0], page_codes, page_scales);
+  for (int blk = blk0; blk < blk1; blk += 2) {
+    if (blk + 1 < blk1)
+      issue_loads(tb, codes_h, scales_h, pages[blk + 1 - blk0], page_codes, page_scales);
+    compute(ta, 0);
+    __syncthreads();
+    reduce(blk, 0);
+    if (blk + 1 >= blk1) break;
+    if (blk + 2 < blk1)
+      issue_loads(ta, codes_h, scales_h, pages[blk + 2 - blk0], page_codes, page_scales);
+    compute(tb, 1);
+    __syncthreads();
+    reduce(blk + 1, 1);
   }
-  if (threadIdx.x == 0) a.counters[b] = 0u;  // ready for the next call
+}
+
+// Selection kernel: one wavefront per query token. The block scores of the
+// query token are staged in LDS with independent loads (up to kStageFloats;
+// longer histories are read from global memory), then select_blocks runs.
+__global__ __launch_bounds__(64) void select_kernel(const float* __restrict__ bscore,
+                                                    const int32_t* __restrict__ seq_lens,
+                                                    int max_blocks, int q_per_seq,
+                                                    int32_t* __restrict__ out_ids,
+                                                    float* __restrict__ out_scores) {
+  extern __shared__ float stage[];
+  __shared__ uint64_t buf[80];
+  const int row = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int Q = q_per_seq;
+  const int b = row / Q, qi = row - b * Q;
+  const int L = seq_lens[b];
+  int32_t* ids = out_ids + int64_t(row) * (MSA_TOPK + 1);
+  float* sc = out_scores ? out_scores + int64_t(row) * (MSA_TOPK + 1) : nullptr;
+  if (L < Q || L > max_blocks * kBlockTokens) {
+    if (lane < MSA_TOPK + 1) {
+      ids[lane] = -1;
+      if (sc) sc[lane] = 0.0f;
+    }
+    return;
+  }
+  const int nb = (L - Q + qi) / kBlockTokens + 1;
+  const float* src = bscore + int64_t(row) * max_blocks;
+  const float* bs = src;
+  if (nb <= kStageFloats) {
+    for (int j0 = 0; j0 < nb; j0 += 8 * 64) {
+      float t[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int j = j0 + lane + 64 * k;
+        t[k] = j < nb ? src[j] : 0.0f;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int j = j0 + lane + 64 * k;
+        if (j < nb) stage[j] = t[k];
+      }
+    }
+    wave_lds_sync();
+    bs = stage;
+  }
+  select_blocks(bs, nb, ids, sc, buf, lane);
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -272,8 +335,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 extern "C" size_t msa_indexer_workspace_bytes(int32_t num_seqs, int32_t q_per_seq,
                                               int32_t max_blocks) {
   if (num_seqs <= 0 || q_per_seq <= 0 || max_blocks <= 0) return 0;
-  return msa::align256(size_t(num_seqs) * 4) +
-         msa::align256(size_t(num_seqs) * q_per_seq * max_blocks * 4);
+  return msa::align256(size_t(num_seqs) * q_per_seq * max_blocks * 4);
 }
 
 extern "C" msa_status msa_indexer_decode(const msa_pool_desc* idx, const uint8_t* idx_codes,
@@ -316,8 +378,7 @@ extern "C" msa_status msa_indexer_decode(const msa_pool_desc* idx, const uint8_t
   a.max_blocks = max_blocks;
   a.seq_lens = seq_lens;
   a.q_per_seq = q_per_seq;
-  a.counters = static_cast<uint32_t*>(workspace);
-  a.bscore = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(size_t(num_seqs) * 4));
+  a.bscore = static_cast<float*>(workspace);
   a.out_ids = out_ids;
   a.out_scores = out_scores;
   // enough workgroups to fill 256 CUs several times over
@@ -326,14 +387,21 @@ extern "C" msa_status msa_indexer_decode(const msa_pool_desc* idx, const uint8_t
   a.blocks_per_wg = bpw;
   const dim3 grid((max_blocks + bpw - 1) / bpw, num_seqs);
   const dim3 block(64 * idx->num_heads);
-  const size_t lds = size_t(2) * idx->num_heads * q_per_seq * MSA_BLOCK_TOKENS * sizeof(float);
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const int qg = (MSA_HEADS_PER_KV * q_per_seq + 15) / 16;
-  if (qg == 1)
+  const int qg_pow2 = qg == 1 ? 1 : (qg == 2 ? 2 : 4);
+  const size_t part_lds = size_t(2) * idx->num_heads * (2 * qg_pow2) * MSA_BLOCK_TOKENS * sizeof(float);
+  const size_t lds = part_lds;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (qg_pow2 == 1)
     hipLaunchKernelGGL(indexer_kernel<1>, grid, block, lds, s, a);
-  else if (qg == 2)
+  else if (qg_pow2 == 2)
     hipLaunchKernelGGL(indexer_kernel<2>, grid, block, lds, s, a);
   else
     hipLaunchKernelGGL(indexer_kernel<4>, grid, block, lds, s, a);
+  if (hipGetLastError() != hipSuccess) return MSA_ERR_HIP;
+  const int stage = max_blocks < kStageFloats ? max_blocks : kStageFloats;
+  hipLaunchKernelGGL(select_kernel, dim3(unsigned(int64_t(num_seqs) * q_per_seq)), dim3(64),
+                     size_t(stage) * sizeof(float), s, a.bscore, seq_lens, max_blocks, q_per_seq,
+                     out_ids, out_scores);
   return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
 }

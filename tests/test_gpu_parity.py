@@ -218,7 +218,6 @@ def test_deterministic_and_reusable_workspace(nb):
         again = _to_np(S.run_step(nb, wl, pools, inp, ws_i, ws_a))
         for x, y in zip(first, again):
             assert np.array_equal(x, y)
-    assert int(ws_i[:256].abs().sum()) == 0       # counters back at zero
 
 
 def test_empty_batch_and_bad_shapes(nb):
