@@ -37,30 +37,30 @@ def parse():
     p.add_argument("--workload", type=int, default=2,
                    help="workload index (0..4); 2 = 8 x 262,144 tokens")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-blocks", type=int, default=256,
-                   help="index blocks of one sequence the CPU oracle scans")
+    p.add_argument("--cpu-blocks", type=int, default=2048,
+                   help="index blocks of one sequence the CPU oracle scans (time is scaled "
+                        "to the whole context when fewer)")
     return p.parse_args()
 
 
 def algorithmic_bytes(wl, ids):
-    """Bytes the method must move per step (never the dense K/V it skips)."""
-    import numpy as np
+    """Bytes the method must move per step (never the dense K/V it skips).
+    Returns (scan, rest of the step, selected-block union)."""
     tq, hq = wl.num_q_tokens, wl.num_q_heads
     nblocks = sum(wl.blocks_of(b) for b in range(wl.num_seqs))
-    idx = (sum(int(L) for L in wl.seq_lens) * wl.num_idx_heads * IDX_BYTES_PER_TOKEN_HEAD
-           + tq * hq * 128          # FP8 index queries
-           + tq * hq * 4            # head weights
-           + nblocks * 4            # block-table entries
-           + tq * (wl.topk + 1) * 4)  # ids written
+    scan = (sum(int(L) for L in wl.seq_lens) * wl.num_idx_heads * IDX_BYTES_PER_TOKEN_HEAD
+            + tq * hq * 128          # FP8 index queries
+            + tq * hq * 4            # head weights
+            + nblocks * 4)           # block-table entries
     union = 0
     for b in range(wl.num_seqs):
         rows = ids[b * wl.q_per_seq:(b + 1) * wl.q_per_seq]
         union += len(set(int(x) for x in rows.reshape(-1) if x >= 0))
-    attn = (union * 2 * wl.num_kv_heads * KV_BYTES_PER_BLOCK_HEAD
+    rest = (tq * (wl.topk + 1) * 4 * 2   # ids written by the selection, read by attention
+            + union * 2 * wl.num_kv_heads * KV_BYTES_PER_BLOCK_HEAD
             + tq * hq * 128             # FP8 attention queries
-            + tq * (wl.topk + 1) * 4    # ids read
             + tq * hq * 128 * 4)        # fp32 output
-    return idx, attn, union
+    return scan, rest, union
 
 
 def cpu_baseline(wl, nblk):
@@ -169,20 +169,26 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # per-kernel durations with HIP events on the launch stream
+    # per-stage durations with HIP events on the launch stream (the library
+    # launches on torch's current stream): the indexer's two stages
+    # (msa_indexer_decode == scan then select) and the attention
     stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    bscores = ws_i[: tq * wl.max_blocks * 4].view(torch.float32).view(tq, wl.max_blocks)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for e in ev:
         e[0].record(stream)
-        nb.msa_indexer_decode(ic, isc, inp["q_idx"], inp["w"], inp["block_table"],
-                              inp["seq_lens"], wl.q_per_seq, ids, ws_i)
+        nb.msa_indexer_scan(ic, isc, inp["q_idx"], inp["w"], inp["block_table"],
+                            inp["seq_lens"], wl.q_per_seq, bscores)
         e[1].record(stream)
+        nb.msa_indexer_select(bscores, inp["seq_lens"], wl.q_per_seq, ids)
+        e[2].record(stream)
         nb.msa_sparse_attn_decode(kc, ks, vc, vs, inp["q_attn"], inp["block_table"],
                                   inp["seq_lens"], wl.q_per_seq, ids, scale, out, ws_a)
-        e[2].record(stream)
+        e[3].record(stream)
     torch.cuda.synchronize()
     t_idx = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
-    t_attn = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
+    t_sel = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
+    t_attn = float(np.mean([e[2].elapsed_time(e[3]) for e in ev])) * 1e-3
 
     ids_np = ids.cpu().numpy()
     idx_bytes, attn_bytes, union = algorithmic_bytes(wl, ids_np)
@@ -211,10 +217,11 @@ def main():
         "achieved_hbm_gbs": round(step_bytes / (ms * 1e-3) / 1e9, 1),
         "hbm_frac_of_peak": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": int(step_bytes),
-        "kernels_us": {"msa_indexer_decode": round(t_idx * 1e6, 2),
+        "kernels_us": {"msa_indexer_scan": round(t_idx * 1e6, 2),
+                       "msa_indexer_select": round(t_sel * 1e6, 2),
                        "msa_sparse_attn_decode": round(t_attn * 1e6, 2)},
         "selected_blocks_union": int(union),
-        "roofline": {"bound": "hbm", "kernel": "indexer_kernel (msa_indexer_decode)",
+        "roofline": {"bound": "hbm", "kernel": "indexer_kernel (msa_indexer_scan)",
                      "achieved": round(idx_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(idx_gbs / HBM_PEAK_GBS, 4),
                      "algorithmic_bytes": int(idx_bytes), "traffic": None},

@@ -144,7 +144,33 @@ msa_status msa_indexer_decode(const msa_pool_desc* idx, const uint8_t* idx_codes
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Workspace bytes msa_sparse_attn_decode needs: split partial results
+ * The indexer in two stages, for callers that keep the block scores (for
+ * example to merge candidates gathered from several context shards).
+ * msa_indexer_decode is exactly msa_indexer_scan followed by
+ * msa_indexer_select on its workspace.
+ *
+ * msa_indexer_scan writes B(j) for every visible block j < nb of every
+ * query token into block_scores float [num_seqs * q_per_seq][max_blocks];
+ * entries past a query token's nb are left untouched. Same arguments and
+ * device-side checks as msa_indexer_decode.
+ */
+msa_status msa_indexer_scan(const msa_pool_desc* idx, const uint8_t* idx_codes,
+                            const uint8_t* idx_scales, const uint8_t* q_fp8, const float* head_w,
+                            int32_t num_q_heads, const int32_t* block_table, int32_t max_blocks,
+                            const int32_t* seq_lens, int32_t num_seqs, int32_t q_per_seq,
+                            float* block_scores, void* stream);
+
+/*
+ * msa_indexer_select reads block_scores (as written by msa_indexer_scan) and
+ * writes out_ids / out_scores exactly as msa_indexer_decode does; scores
+ * must be finite (negative values and -0 rank as 0).
+ */
+msa_status msa_indexer_select(const float* block_scores, const int32_t* seq_lens,
+                              int32_t max_blocks, int32_t num_seqs, int32_t q_per_seq,
+                              int32_t topk, int32_t* out_ids, float* out_scores, void* stream);
+
+/*
+ * Workspace bytes msa_sparse_attn_decode needs for its split partial results
  * (running max, denominator and unnormalised output per split). No initial
  * contents are required.
  */
@@ -163,7 +189,9 @@ size_t msa_attn_workspace_bytes(int32_t num_seqs, int32_t q_per_seq, int32_t num
  *                page is outside [0, num_pages) are ignored
  *   out          float [num_seqs * q_per_seq][num_q_heads][128]; a query
  *                token with no usable block gets zeros
- * 1 <= num_sel <= 64.
+ * 1 <= num_sel <= 64. The softmax weights enter the P x V product as two
+ * FP8 terms, FP8(256 p) + FP8(16 (256 p - FP8(256 p))) / 16 (about 8
+ * significant bits); the denominator sums the same rounded terms.
  */
 msa_status msa_sparse_attn_decode(const msa_pool_desc* kv, const uint8_t* k_codes,
                                   const uint8_t* k_scales, const uint8_t* v_codes,

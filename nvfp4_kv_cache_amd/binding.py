@@ -46,6 +46,9 @@ SIGNATURES = {
     "msa_indexer_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
     "msa_indexer_decode": (ctypes.c_int, [_DESC, _P, _P, _P, _P, _I32, _P, _I32, _P, _I32, _I32,
                                           _I32, _P, _P, _P, _SZ, _P]),
+    "msa_indexer_scan": (ctypes.c_int, [_DESC, _P, _P, _P, _P, _I32, _P, _I32, _P, _I32, _I32,
+                                        _P, _P]),
+    "msa_indexer_select": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _I32, _P, _P, _P]),
     "msa_attn_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
     "msa_sparse_attn_decode": (ctypes.c_int, [_DESC, _P, _P, _P, _P, _P, _I32, _P, _I32, _P,
                                               _I32, _I32, _P, _I32, _F32, _P, _P, _SZ, _P]),
@@ -143,15 +146,15 @@ def msa_attn_workspace_bytes(num_seqs: int, q_per_seq: int, num_q_heads: int, nu
     return int(lib().msa_attn_workspace_bytes(num_seqs, q_per_seq, num_q_heads, num_sel))
 
 
-def indexer_workspace(num_seqs, q_per_seq, max_blocks, device="cuda"):
-    """Workspace for msa_indexer_decode (contents need no initialisation)."""
-    n = msa_indexer_workspace_bytes(num_seqs, q_per_seq, max_blocks)
-    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
-
-
 def attn_workspace(num_seqs, q_per_seq, num_q_heads, num_sel, device="cuda"):
     """Workspace for msa_sparse_attn_decode (contents need no initialisation)."""
     n = msa_attn_workspace_bytes(num_seqs, q_per_seq, num_q_heads, num_sel)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def indexer_workspace(num_seqs, q_per_seq, max_blocks, device="cuda"):
+    """Workspace for msa_indexer_decode (contents need no initialisation)."""
+    n = msa_indexer_workspace_bytes(num_seqs, q_per_seq, max_blocks)
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
@@ -181,6 +184,55 @@ def msa_indexer_decode(idx_codes, idx_scales, q_fp8, head_w, block_table, seq_le
         ctypes.byref(desc), _ptr(idx_codes), _ptr(idx_scales), _ptr(q_fp8), _ptr(head_w), hq,
         _ptr(block_table), max_blocks, _ptr(seq_lens), num_seqs, q_per_seq, topk, _ptr(out_ids),
         _ptr(out_scores), _ptr(workspace), workspace.numel(), _stream()), "msa_indexer_decode")
+
+
+def _check_indexer_inputs(q_fp8, head_w, block_table, seq_lens, q_per_seq):
+    _need(q_fp8, "q_fp8", torch.uint8, 3)
+    _need(head_w, "head_w", torch.float32, 2)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    num_seqs, max_blocks = block_table.shape
+    tq = num_seqs * q_per_seq
+    hq = q_fp8.shape[1]
+    if seq_lens.shape[0] != num_seqs or q_fp8.shape != (tq, hq, HEAD_DIM):
+        raise ValueError("q_fp8 must be [num_seqs*q_per_seq, Hq, 128] and seq_lens [num_seqs]")
+    if head_w.shape != (tq, hq):
+        raise ValueError("head_w must be [T_q, Hq]")
+    return num_seqs, max_blocks, tq, hq
+
+
+def msa_indexer_scan(idx_codes, idx_scales, q_fp8, head_w, block_table, seq_lens, q_per_seq,
+                     block_scores):
+    """Block scores B(j) into block_scores float32 [B*Q, max_blocks]."""
+    _check_pool(idx_codes, idx_scales, "idx")
+    num_seqs, max_blocks, tq, hq = _check_indexer_inputs(q_fp8, head_w, block_table, seq_lens,
+                                                         q_per_seq)
+    _need(block_scores, "block_scores", torch.float32, 2)
+    if block_scores.shape != (tq, max_blocks):
+        raise ValueError("block_scores must be [T_q, max_blocks]")
+    desc = pool_desc(idx_codes)
+    _check(lib().msa_indexer_scan(
+        ctypes.byref(desc), _ptr(idx_codes), _ptr(idx_scales), _ptr(q_fp8), _ptr(head_w), hq,
+        _ptr(block_table), max_blocks, _ptr(seq_lens), num_seqs, q_per_seq, _ptr(block_scores),
+        _stream()), "msa_indexer_scan")
+
+
+def msa_indexer_select(block_scores, seq_lens, q_per_seq, out_ids, out_scores=None, topk=TOPK):
+    """Top-16 + recent block ids from block scores float32 [B*Q, max_blocks]."""
+    _need(block_scores, "block_scores", torch.float32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    _need(out_ids, "out_ids", torch.int32, 2)
+    if out_scores is not None:
+        _need(out_scores, "out_scores", torch.float32, 2)
+    tq, max_blocks = block_scores.shape
+    num_seqs = seq_lens.shape[0]
+    if tq != num_seqs * q_per_seq or out_ids.shape != (tq, topk + 1):
+        raise ValueError("block_scores must be [num_seqs*q_per_seq, max_blocks], out_ids [T_q, 17]")
+    if out_scores is not None and out_scores.shape != out_ids.shape:
+        raise ValueError("out_scores must match out_ids")
+    _check(lib().msa_indexer_select(_ptr(block_scores), _ptr(seq_lens), max_blocks, num_seqs,
+                                    q_per_seq, topk, _ptr(out_ids), _ptr(out_scores), _stream()),
+           "msa_indexer_select")
 
 
 def msa_sparse_attn_decode(k_codes, k_scales, v_codes, v_scales, q_fp8, block_table, seq_lens,

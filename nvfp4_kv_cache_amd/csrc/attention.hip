@@ -8,14 +8,25 @@
 // because the query stays FP8 (MiniMax-M3.1-Flash lands in vLLM on day one,
 // third paragraph).
 //
-// Grid (splits, KV heads, query tokens). A workgroup (4 wavefronts) takes a
-// run of selected blocks of one query token and one KV head (its 8 query
-// heads). Per block: every wave dequantises 2 of the 8 16-token K tiles
-// straight into FP8 MFMA operands and multiplies them with the query
-// (A = 8 heads, B = 16 tokens); it dequantises the same tokens' V rows into
-// LDS as fp32. The softmax runs online in base 2 with fp32 state, and P x V
-// is accumulated in fp32 on the vector ALUs. Each split writes (m, l, o);
-// the last split of a (query token, KV head) to finish merges them.
+// Grid (splits, KV heads, query tokens), 4 wavefronts per workgroup. Split s
+// covers selected slots [s*4R, (s+1)*4R); wave w takes slots s*4R + w + 4k,
+// k < R, each one 128-token block, keeping its own online-softmax state; the
+// waves merge through LDS, and with several splits a second kernel merges
+// the splits' (m, l, o) by log-sum-exp. Per block a wave:
+//   1. dequantises the 8 K tiles into FP8 MFMA operands and computes
+//      S = Q K^T with v_mfma_f32_16x16x128_f8f6f4 (A = the 8 query heads of
+//      this KV head, rows 8..15 zero; B = 16 tokens x 128 channels);
+//   2. dequantises V into LDS as FP8, one 136-byte row per token;
+//   3. runs the softmax in base 2 in fp32, scales P by 2^8 and splits it into
+//      two FP8 terms, P_hi = FP8(256 p) and P_lo = FP8(16 (256 p - P_hi)), so
+//      P_hi + P_lo / 16 carries about 8 significant bits; the denominator sums
+//      the same two terms, so numerator and denominator agree;
+//   4. computes O += P_hi V + 2^-4 P_lo V with the same MFMA (the second with
+//      its E8M0 operand scale set to 2^-4): all operands are read
+//      transposed from LDS with ds_read_b64_tr_b8 (within each 16-lane group,
+//      lane i receives byte i%8 of the 8-byte segments addressed by lanes
+//      i/8, i/8 + 2, ..., i/8 + 14), so lane i ends with 8 consecutive tokens
+//      of one head (P) or one channel (V).
 #include "msa_nvfp4.h"
 #include "nvfp4_tile.h"
 
@@ -38,32 +49,67 @@ struct AttnArgs {
   int q_per_seq;
   const int32_t* sel_ids;
   int num_sel;
-  int blocks_per_split;
+  int slots_per_wave;  // R
   int num_splits;
-  float scale_log2;  // softmax_scale * log2(e)
-  float* part_o;     // [T_q * Hq][num_splits][128]
-  float* part_ml;    // [T_q * Hq][num_splits][2]
+  float scale_log2;    // softmax_scale * log2(e)
+  float* part_o;       // [T_q * Hq][num_splits][128] unnormalised, when num_splits > 1
+  float* part_ml;      // [T_q * Hq][num_splits][2]
   float* out;
 };
 
 typedef float v2f __attribute__((ext_vector_type(2)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i lds_v2i;
 
-constexpr int kAttnThreads = 256;
+constexpr int kVRow = 136;                            // LDS bytes per V row (128 + pad)
+constexpr int kVBytes = kBlockTokens * kVRow;         // 17,408
+constexpr int kPBytes = kBlockTokens * kHeadsPerKv;   // 1,024: P as [token][head] FP8
+constexpr int kWaveLds = kVBytes + 2 * kPBytes;       // per wavefront: V, P_hi, P_lo
+constexpr float kPScale = 256.0f;                     // P_hi = FP8(256 p)
+constexpr float kPLoScale = 16.0f;                    // P_lo = FP8(16 (256 p - P_hi))
+constexpr int kE8M0One = 0x7F7F7F7F;                  // MFMA operand scale 2^0
+constexpr int kE8M0Sixteenth = 0x7B7B7B7B;            // MFMA operand scale 2^-4
 
-__global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(const AttnArgs a) {
+__device__ __forceinline__ float row16_max(float v) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// 32 bytes of an MFMA operand from four transposed 8-byte LDS reads.
+__device__ __forceinline__ v8i tr_operand(const uint8_t* p0, const uint8_t* p1, const uint8_t* p2,
+                                          const uint8_t* p3) {
+  const v2i a = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(p0));
+  const v2i b = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(p1));
+  const v2i c = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(p2));
+  const v2i d = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(p3));
+  return v8i{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
+template <int W>
+__global__ __launch_bounds__(64 * W) void sparse_attn_kernel(const AttnArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // W x (V rows, P) + zeros
   __shared__ uint2 lut[128];
-  __shared__ float vs[kBlockTokens][kHeadDim];   // dequantised V of one block
-  __shared__ float zs[kHeadsPerKv][kBlockTokens];  // logits, then probabilities
-  __shared__ float alpha_s[kHeadsPerKv];
-  __shared__ float s_m[kHeadsPerKv][64], s_l[kHeadsPerKv][64];
 
-  const int qt = blockIdx.z, kh = blockIdx.y, sp = blockIdx.x;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, slice = lane >> 4;
+  const int sp = blockIdx.x, kh = blockIdx.y, qt = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int slice = lane >> 4;  // 32-channel slice (QK) / 32-token group (PV)
+  const int li = lane & 15;     // row of A / column of B inside a 16-lane group
   const int Q = a.q_per_seq;
-  const int b = qt / Q, qi = qt % Q;
+  const int b = qt / Q, qi = qt - b * Q;
   const int Hq = a.num_q_heads;
+  uint8_t* vrows = smem + wave * kWaveLds;
+  uint8_t* prows = vrows + kVBytes;        // P_hi [token][head]
+  uint8_t* plows = prows + kPBytes;        // P_lo [token][head]
+  const uint8_t* zeros = smem + W * kWaveLds;
 
-  for (int i = tid; i < 128; i += kAttnThreads) lut[i] = make_uint2(kAttnLut.lo[i], kAttnLut.hi[i]);
+  for (int i = tid; i < 128; i += 64 * W) lut[i] = make_uint2(kAttnLut.lo[i], kAttnLut.hi[i]);
+  if (tid < 16) reinterpret_cast<uint32_t*>(smem + W * kWaveLds)[tid] = 0u;
 
   const int L = a.seq_lens[b];
   const bool seq_ok = L >= Q && L <= a.max_blocks * kBlockTokens;
@@ -71,27 +117,31 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(const AttnArg
 
   // query operand: rows 0..7 = the 8 query heads of this KV head
   v8i qop = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-  if ((lane & 15) < kHeadsPerKv) {
+  if (li < kHeadsPerKv) {
     const uint4* qp = reinterpret_cast<const uint4*>(
-        a.q + (int64_t(qt) * Hq + kh * kHeadsPerKv + (lane & 15)) * kHeadDim + slice * 32);
+        a.q + (int64_t(qt) * Hq + kh * kHeadsPerKv + li) * kHeadDim + slice * 32);
     qop = q_operand(qp[0], qp[1]);
   }
-  // softmax state of heads 2*wave, 2*wave+1 (wave-uniform)
-  float m_run[2] = {-__builtin_huge_valf(), -__builtin_huge_valf()};
-  float l_run[2] = {0.0f, 0.0f};
-  // P x V accumulator: head tid/32, channels 4*(tid%32) .. +3
-  const int ph = tid >> 5, pd = (tid & 31) * 4;
-  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  // online-softmax state of heads 4*slice + v (meaningful in lanes 0..31)
+  const float ninf = -__builtin_huge_valf();
+  float m_run[4] = {ninf, ninf, ninf, ninf};
+  float l_run[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  v4f o[8];  // rows = heads 4*slice + v, column = channel 16*n + li
+#pragma unroll
+  for (int n = 0; n < 8; ++n) o[n] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   __syncthreads();
 
   const int64_t page_codes = int64_t(a.num_kv_heads) * kCodePage;
   const int64_t page_scales = int64_t(a.num_kv_heads) * kScalePage;
-  const int lane_code = (lane & 15) * kCodeRow + slice * 16;
-  const int lane_scale = (lane & 15) * kScaleRow + slice * 2;
+  const int lane_code = li * kCodeRow + slice * 16;
+  const int lane_scale = li * kScaleRow + slice * 2;
+  // transposed-read addresses: segment of lane i = row (i / 2) of an 8-row
+  // group, left or right 8 bytes (V) / real or zero segment (P)
+  const int seg_row = li >> 1, seg_half = li & 1;
 
-  const int s0 = sp * a.blocks_per_split;
-  const int s1 = min(a.num_sel, s0 + a.blocks_per_split);
-  for (int si = s0; si < s1; ++si) {
+  const int s_begin = sp * W * a.slots_per_wave;
+  const int s_end = min(a.num_sel, s_begin + W * a.slots_per_wave);
+  for (int si = s_begin + wave; si < s_end; si += W) {
     const int blk = a.sel_ids[int64_t(qt) * a.num_sel + si];
     bool ok = seq_ok && blk >= 0 && blk < a.max_blocks && blk * kBlockTokens <= pos;
     int page = -1;
@@ -99,154 +149,227 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(const AttnArg
       page = a.block_table[int64_t(b) * a.max_blocks + blk];
       ok = page >= 0 && page < a.num_pages;
     }
-    if (!ok) continue;  // uniform over the workgroup
+    if (!ok) continue;  // uniform over the wavefront
     const int ntok = min(kBlockTokens, pos + 1 - blk * kBlockTokens);
-    const int64_t head_code = int64_t(page) * page_codes + int64_t(kh) * kCodePage + lane_code;
-    const int64_t head_scale = int64_t(page) * page_scales + int64_t(kh) * kScalePage + lane_scale;
-
+    const int64_t hc = int64_t(page) * page_codes + int64_t(kh) * kCodePage + lane_code;
+    const int64_t hs = int64_t(page) * page_scales + int64_t(kh) * kScalePage + lane_scale;
+    uint4 kc[8], vc[8];
+    uint32_t ks[8], vsc[8];
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int j = 2 * wave + jj;
-      const int t = 16 * j + (lane & 15);
-      const uint4 kc = *reinterpret_cast<const uint4*>(a.k_codes + head_code + j * 16 * kCodeRow);
-      const uint32_t ks = *reinterpret_cast<const uint16_t*>(a.k_scales + head_scale + j * 16 * kScaleRow);
-      const uint4 vc = *reinterpret_cast<const uint4*>(a.v_codes + head_code + j * 16 * kCodeRow);
-      const uint32_t vsc = *reinterpret_cast<const uint16_t*>(a.v_scales + head_scale + j * 16 * kScaleRow);
-      const v8i kop = dequant32(kc, lut[ks & 0x7F], lut[(ks >> 8) & 0x7F]);
-      const v4f z = mfma_fp8_16x16x128(qop, kop, v4f{0.0f, 0.0f, 0.0f, 0.0f});
-      if (lane < 32) {
+    for (int j = 0; j < 8; ++j) {
+      kc[j] = *reinterpret_cast<const uint4*>(a.k_codes + hc + j * 16 * kCodeRow);
+      ks[j] = *reinterpret_cast<const uint16_t*>(a.k_scales + hs + j * 16 * kScaleRow);
+    }
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          zs[4 * slice + v][t] = t < ntok ? z[v] * a.scale_log2 : -__builtin_huge_valf();
-      }
-      // V: 32 channels of token t, restored to natural channel order
-      // (dequant32 yields channels 0,2,4,6 then 1,3,5,7 of each run of 8)
-      const v8i vop = dequant32(vc, lut[vsc & 0x7F], lut[(vsc >> 8) & 0x7F]);
-      float* dst = &vs[t][slice * 32];
-      const bool live = t < ntok;
+    for (int j = 0; j < 8; ++j) {
+      vc[j] = *reinterpret_cast<const uint4*>(a.v_codes + hc + j * 16 * kCodeRow);
+      vsc[j] = *reinterpret_cast<const uint16_t*>(a.v_scales + hs + j * 16 * kScaleRow);
+    }
+    // 1. logits of 16 tokens per tile: lane holds heads 4*slice+v, token 16j+li
+    float z[8][4];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const v8i kop = dequant32(kc[j], lut[ks[j] & 0x7F], lut[(ks[j] >> 8) & 0x7F]);
+      const v4f c = mfma_fp8_16x16x128(qop, kop, v4f{0.0f, 0.0f, 0.0f, 0.0f});
+      const bool live = 16 * j + li < ntok;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) z[j][v] = live ? c[v] * a.scale_log2 : ninf;
+    }
+    // 2. V rows into LDS in natural channel order (masked tokens -> 0)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const v8i vop = dequant32(vc[j], lut[vsc[j] & 0x7F], lut[(vsc[j] >> 8) & 0x7F]);
+      const bool live = 16 * j + li < ntok;
+      uint32_t nat[8];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const v2f e01 = __builtin_amdgcn_cvt_pk_f32_fp8(vop[2 * u], false);     // ch 0, 2
-        const v2f e23 = __builtin_amdgcn_cvt_pk_f32_fp8(vop[2 * u], true);      // ch 4, 6
-        const v2f o01 = __builtin_amdgcn_cvt_pk_f32_fp8(vop[2 * u + 1], false); // ch 1, 3
-        const v2f o23 = __builtin_amdgcn_cvt_pk_f32_fp8(vop[2 * u + 1], true);  // ch 5, 7
-        const float4 lo = live ? make_float4(e01.x, o01.x, e01.y, o01.y) : make_float4(0, 0, 0, 0);
-        const float4 hi = live ? make_float4(e23.x, o23.x, e23.y, o23.y) : make_float4(0, 0, 0, 0);
-        *reinterpret_cast<float4*>(dst + 8 * u) = lo;
-        *reinterpret_cast<float4*>(dst + 8 * u + 4) = hi;
+        const uint32_t ev = uint32_t(vop[2 * u]), od = uint32_t(vop[2 * u + 1]);
+        nat[2 * u] = live ? __builtin_amdgcn_perm(od, ev, 0x05010400u) : 0u;
+        nat[2 * u + 1] = live ? __builtin_amdgcn_perm(od, ev, 0x07030602u) : 0u;
+      }
+      uint8_t* dst = vrows + (16 * j + li) * kVRow + slice * 32;
+      *reinterpret_cast<uint2*>(dst) = make_uint2(nat[0], nat[1]);
+      *reinterpret_cast<uint2*>(dst + 8) = make_uint2(nat[2], nat[3]);
+      *reinterpret_cast<uint2*>(dst + 16) = make_uint2(nat[4], nat[5]);
+      *reinterpret_cast<uint2*>(dst + 24) = make_uint2(nat[6], nat[7]);
+    }
+    // 3. softmax: block max per head, rescale, P = FP8(256 * 2^(z - m))
+    float alpha[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float mb = z[0][v];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) mb = fmaxf(mb, z[j][v]);
+      const float m_new = fmaxf(m_run[v], row16_max(mb));
+      alpha[v] = m_run[v] == ninf ? 0.0f : exp2f(m_run[v] - m_new);
+      m_run[v] = m_new;
+    }
+    float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float p[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) p[v] = z[j][v] == ninf ? 0.0f : exp2f(z[j][v] - m_run[v]) * kPScale;
+      int hi = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+      hi = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], hi, true);
+      const v2f h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
+      const v2f h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+      int lo = __builtin_amdgcn_cvt_pk_fp8_f32((p[0] - h01.x) * kPLoScale,
+                                               (p[1] - h01.y) * kPLoScale, 0, false);
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32((p[2] - h23.x) * kPLoScale,
+                                           (p[3] - h23.y) * kPLoScale, lo, true);
+      const v2f l01 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
+      const v2f l23 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
+      lsum[0] += h01.x + l01.x * (1.0f / kPLoScale);
+      lsum[1] += h01.y + l01.y * (1.0f / kPLoScale);
+      lsum[2] += h23.x + l23.x * (1.0f / kPLoScale);
+      lsum[3] += h23.y + l23.y * (1.0f / kPLoScale);
+      if (lane < 32) {
+        const int off = (16 * j + li) * kHeadsPerKv + 4 * slice;
+        *reinterpret_cast<int*>(prows + off) = hi;
+        *reinterpret_cast<int*>(plows + off) = lo;
       }
     }
-    __syncthreads();
-    // online softmax for heads 2*wave, 2*wave+1
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int h = 2 * wave + hh;
-      const float z0 = zs[h][lane], z1 = zs[h][lane + 64];
-      const float m_new = fmaxf(m_run[hh], wave_max(fmaxf(z0, z1)));
-      const float p0 = exp2f(z0 - m_new), p1 = exp2f(z1 - m_new);
-      zs[h][lane] = p0;
-      zs[h][lane + 64] = p1;
-      const float alpha = exp2f(m_run[hh] - m_new);
-      l_run[hh] = l_run[hh] * alpha + wave_sum(p0 + p1);
-      m_run[hh] = m_new;
-      if (lane == 0) alpha_s[h] = alpha;
+    for (int v = 0; v < 4; ++v) {
+      l_run[v] = l_run[v] * alpha[v] + row16_sum(lsum[v]);
+#pragma unroll
+      for (int n = 0; n < 8; ++n) o[n][v] *= alpha[v];
     }
-    __syncthreads();
+    wave_lds_sync();
+    // 4. O += P_hi V + 2^-4 P_lo V. A: lane li < 8 -> head li, tokens
+    //    32*slice + 8r .. +7; lanes 8..15 read the zero segment (rows 8..15
+    //    of A are zero).
     {
-      const float al = alpha_s[ph];
+      const int t0 = 32 * slice;
+      const int poff = (t0 + seg_row) * kHeadsPerKv;
+      const uint8_t* ph = seg_half ? zeros : prows + poff;
+      const uint8_t* pl = seg_half ? zeros : plows + poff;
+      const int pstep = seg_half ? 0 : 8 * kHeadsPerKv;
+      const v8i pop_hi = tr_operand(ph, ph + pstep, ph + 2 * pstep, ph + 3 * pstep);
+      const v8i pop_lo = tr_operand(pl, pl + pstep, pl + 2 * pstep, pl + 3 * pstep);
+      const uint8_t* vb = vrows + (t0 + seg_row) * kVRow + 8 * seg_half;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] *= al;
-      for (int t = 0; t < ntok; ++t) {
-        const float p = zs[ph][t];
-        const float4 v = *reinterpret_cast<const float4*>(&vs[t][pd]);
-        acc[0] += p * v.x;
-        acc[1] += p * v.y;
-        acc[2] += p * v.z;
-        acc[3] += p * v.w;
+      for (int n = 0; n < 8; ++n) {
+        const uint8_t* vp = vb + 16 * n;
+        const v8i vop = tr_operand(vp, vp + 8 * kVRow, vp + 16 * kVRow, vp + 24 * kVRow);
+        o[n] = mfma_fp8_16x16x128(pop_hi, vop, o[n]);
+        o[n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pop_lo, vop, o[n], 0, 0, 0,
+                                                                 kE8M0Sixteenth, 0, kE8M0One);
       }
     }
-    __syncthreads();
+    wave_lds_sync();
   }
 
-  const int64_t row = int64_t(qt) * Hq + kh * kHeadsPerKv;  // first query head row
-  // per-head (m, l) of this wave's two heads go through LDS to the P x V threads
-  if (lane == 0) {
-    s_m[2 * wave][0] = m_run[0];
-    s_m[2 * wave + 1][0] = m_run[1];
-    s_l[2 * wave][0] = l_run[0];
-    s_l[2 * wave + 1][0] = l_run[1];
+  // merge the waves' partial results through LDS (reusing the V rows)
+  __syncthreads();
+  float* mo = reinterpret_cast<float*>(smem);                  // [W][8 heads][128]
+  float* mml = mo + W * kHeadsPerKv * kHeadDim;                // [W][8 heads][2]
+  if (lane < 32) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int h = 4 * slice + v;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) mo[(wave * kHeadsPerKv + h) * kHeadDim + 16 * n + li] = o[n][v];
+      if (li == 0) {
+        mml[(wave * kHeadsPerKv + h) * 2] = m_run[v];
+        mml[(wave * kHeadsPerKv + h) * 2 + 1] = l_run[v];
+      }
+    }
   }
   __syncthreads();
-  if (a.num_splits == 1) {
-    const float l = s_l[ph][0];
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    *reinterpret_cast<float4*>(a.out + (row + ph) * kHeadDim + pd) =
-        make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
-    return;
-  }
-  float* po = a.part_o + ((row + ph) * a.num_splits + sp) * kHeadDim + pd;
-  *reinterpret_cast<float4*>(po) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-  if ((tid & 31) == 0) {
-    float* pm = a.part_ml + ((row + ph) * a.num_splits + sp) * 2;
-    pm[0] = s_m[ph][0];
-    pm[1] = s_l[ph][0];
+  const int64_t row = int64_t(qt) * Hq + kh * kHeadsPerKv;
+  for (int e = tid; e < kHeadsPerKv * kHeadDim; e += 64 * W) {
+    const int h = e / kHeadDim, d = e - h * kHeadDim;
+    float M = ninf;
+#pragma unroll
+    for (int w = 0; w < W; ++w) M = fmaxf(M, mml[(w * kHeadsPerKv + h) * 2]);
+    float num = 0.0f, den = 0.0f;
+    if (M != ninf) {
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        const float mw = mml[(w * kHeadsPerKv + h) * 2];
+        const float f = mw == ninf ? 0.0f : exp2f(mw - M);
+        den += f * mml[(w * kHeadsPerKv + h) * 2 + 1];
+        num += f * mo[(w * kHeadsPerKv + h) * kHeadDim + d];
+      }
+    }
+    if (a.num_splits == 1) {
+      a.out[(row + h) * kHeadDim + d] = den > 0.0f ? num / den : 0.0f;
+    } else {
+      a.part_o[((row + h) * a.num_splits + sp) * kHeadDim + d] = num;
+      if (d == 0) {
+        a.part_ml[((row + h) * a.num_splits + sp) * 2] = M;
+        a.part_ml[((row + h) * a.num_splits + sp) * 2 + 1] = den;
+      }
+    }
   }
 }
 
 // Merge kernel: one workgroup per (query token, KV head); thread (h, 4 ch)
-// combines the splits' (m, l, o) by log-sum-exp. Every (m, l) and every
-// partial o is fetched with independent loads.
-__global__ __launch_bounds__(kAttnThreads) void merge_kernel(const float* __restrict__ part_o,
-                                                             const float* __restrict__ part_ml,
-                                                             int num_splits, float* __restrict__ out) {
-  __shared__ float s_m[kHeadsPerKv][64], s_l[kHeadsPerKv][64];
+// combines the splits' (m, l, o) by log-sum-exp. Up to kMergeChunk splits
+// are fetched per round of independent loads.
+constexpr int kMergeChunk = 16;
+
+__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part_o,
+                                                    const float* __restrict__ part_ml,
+                                                    int num_splits, float* __restrict__ out) {
   const int tid = threadIdx.x;
-  const int64_t row = int64_t(blockIdx.x) * kHeadsPerKv;  // first query head row
-  for (int i = tid; i < kHeadsPerKv * num_splits; i += kAttnThreads) {
-    const int h = i / num_splits, sidx = i - h * num_splits;
-    const float2 ml = *reinterpret_cast<const float2*>(part_ml + ((row + h) * num_splits + sidx) * 2);
-    s_m[h][sidx] = ml.x;
-    s_l[h][sidx] = ml.y;
-  }
-  __syncthreads();
-  const int ph = tid >> 5, pd = (tid & 31) * 4;
-  float M = -__builtin_huge_valf();
-  for (int sidx = 0; sidx < num_splits; ++sidx) M = fmaxf(M, s_m[ph][sidx]);
-  float o[4] = {0.0f, 0.0f, 0.0f, 0.0f}, den = 0.0f;
-  if (M != -__builtin_huge_valf()) {
-    const float* po = part_o + (row + ph) * num_splits * kHeadDim + pd;
-    for (int s0 = 0; s0 < num_splits; s0 += 8) {
-      float4 v[8];
+  const int64_t row = int64_t(blockIdx.x) * kHeadsPerKv + (tid >> 5);  // query head row
+  const int pd = (tid & 31) * 4;
+  const float* po = part_o + row * num_splits * kHeadDim + pd;
+  const float* pm = part_ml + row * num_splits * 2;
+  const float ninf = -__builtin_huge_valf();
+  float M = ninf, den = 0.0f, o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int s0 = 0; s0 < num_splits; s0 += kMergeChunk) {
+    float4 v[kMergeChunk];
+    float2 ml[kMergeChunk];
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
-        v[k] = s0 + k < num_splits ? *reinterpret_cast<const float4*>(po + (s0 + k) * kHeadDim)
-                                   : make_float4(0, 0, 0, 0);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        if (s0 + k >= num_splits) break;
-        const float ms = s_m[ph][s0 + k];
-        const float f = ms == -__builtin_huge_valf() ? 0.0f : exp2f(ms - M);
-        den += f * s_l[ph][s0 + k];
-        o[0] += f * v[k].x;
-        o[1] += f * v[k].y;
-        o[2] += f * v[k].z;
-        o[3] += f * v[k].w;
-      }
+    for (int k = 0; k < kMergeChunk; ++k) {
+      const bool in = s0 + k < num_splits;
+      v[k] = in ? *reinterpret_cast<const float4*>(po + (s0 + k) * kHeadDim) : make_float4(0, 0, 0, 0);
+      ml[k] = in ? *reinterpret_cast<const float2*>(pm + (s0 + k) * 2) : make_float2(ninf, 0.0f);
     }
+    float Mc = M;
+#pragma unroll
+    for (int k = 0; k < kMergeChunk; ++k) Mc = fmaxf(Mc, ml[k].x);
+    if (Mc == ninf) continue;
+    const float r = M == ninf ? 0.0f : exp2f(M - Mc);
+    den *= r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] *= r;
+#pragma unroll
+    for (int k = 0; k < kMergeChunk; ++k) {
+      const float f = ml[k].x == ninf ? 0.0f : exp2f(ml[k].x - Mc);
+      den += f * ml[k].y;
+      o[0] += f * v[k].x;
+      o[1] += f * v[k].y;
+      o[2] += f * v[k].z;
+      o[3] += f * v[k].w;
+    }
+    M = Mc;
   }
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-  *reinterpret_cast<float4*>(out + (row + ph) * kHeadDim + pd) =
+  *reinterpret_cast<float4*>(out + row * kHeadDim + pd) =
       make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
 }
 
+constexpr int kAttnWaves = 4;
+
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Split count: enough workgroups to cover the chip, never more than num_sel.
-inline void attn_splits(int64_t tq_kv, int num_sel, int* bps, int* nsplit) {
-  int want = int((2048 + tq_kv - 1) / tq_kv);
-  want = want < 1 ? 1 : (want > num_sel ? num_sel : want);
-  *bps = (num_sel + want - 1) / want;
-  *nsplit = (num_sel + *bps - 1) / *bps;
+// Slots per wave R and split count: one block per wave while that keeps the
+// workgroup count under ~1024; otherwise more blocks per wave.
+inline void attn_plan(int64_t pairs, int num_sel, int* r, int* nsplit) {
+  int R = 1;
+  while (R < num_sel && pairs * ((num_sel + kAttnWaves * R - 1) / (kAttnWaves * R)) > 1024) ++R;
+  *r = R;
+  *nsplit = (num_sel + kAttnWaves * R - 1) / (kAttnWaves * R);
+}
+
+template <int W>
+constexpr size_t attn_lds_bytes() {
+  return size_t(W) * kWaveLds + 64;
 }
 
 }  // namespace msa
@@ -254,9 +377,10 @@ inline void attn_splits(int64_t tq_kv, int num_sel, int* bps, int* nsplit) {
 extern "C" size_t msa_attn_workspace_bytes(int32_t num_seqs, int32_t q_per_seq,
                                            int32_t num_q_heads, int32_t num_sel) {
   if (num_seqs <= 0 || q_per_seq <= 0 || num_q_heads <= 0 || num_sel <= 0) return 0;
+  // enough for the largest split count the launch can choose (one block per wave)
   const size_t rows = size_t(num_seqs) * q_per_seq * num_q_heads;
-  // partial o and partial (m, l) for up to num_sel splits
-  return msa::align256(rows * num_sel * MSA_HEAD_DIM * 4) + msa::align256(rows * num_sel * 2 * 4);
+  const size_t splits = size_t(num_sel + msa::kAttnWaves - 1) / msa::kAttnWaves;
+  return msa::align256(rows * splits * MSA_HEAD_DIM * 4) + msa::align256(rows * splits * 2 * 4);
 }
 
 extern "C" msa_status msa_sparse_attn_decode(const msa_pool_desc* kv, const uint8_t* k_codes,
@@ -287,11 +411,8 @@ extern "C" msa_status msa_sparse_attn_decode(const msa_pool_desc* kv, const uint
   if (mis(k_codes, 15) || mis(k_scales, 15) || mis(v_codes, 15) || mis(v_scales, 15) ||
       mis(q_fp8, 15) || mis(block_table, 3) || mis(seq_lens, 3) || mis(sel_ids, 3) || mis(out, 15))
     return MSA_ERR_INVALID_ARG;
-  const size_t need = msa_attn_workspace_bytes(num_seqs, q_per_seq, num_q_heads, num_sel);
-  if (!workspace || workspace_bytes < need || mis(workspace, 255)) return MSA_ERR_WORKSPACE;
 
   const int64_t tq = int64_t(num_seqs) * q_per_seq;
-  const size_t rows = size_t(tq) * num_q_heads;
   AttnArgs a;
   a.k_codes = k_codes;
   a.k_scales = k_scales;
@@ -307,18 +428,27 @@ extern "C" msa_status msa_sparse_attn_decode(const msa_pool_desc* kv, const uint
   a.q_per_seq = q_per_seq;
   a.sel_ids = sel_ids;
   a.num_sel = num_sel;
-  attn_splits(tq * kv->num_heads, num_sel, &a.blocks_per_split, &a.num_splits);
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
-  char* ws = static_cast<char*>(workspace);
-  a.part_o = reinterpret_cast<float*>(ws);
-  a.part_ml = reinterpret_cast<float*>(ws + align256(rows * num_sel * MSA_HEAD_DIM * 4));
   a.out = out;
-  const dim3 grid(a.num_splits, kv->num_heads, unsigned(tq));
+  attn_plan(tq * kv->num_heads, num_sel, &a.slots_per_wave, &a.num_splits);
+  if (a.num_splits > 1) {
+    const size_t need = msa_attn_workspace_bytes(num_seqs, q_per_seq, num_q_heads, num_sel);
+    if (!workspace || workspace_bytes < need || mis(workspace, 255)) return MSA_ERR_WORKSPACE;
+    const size_t rows = size_t(tq) * num_q_heads;
+    char* ws = static_cast<char*>(workspace);
+    a.part_o = reinterpret_cast<float*>(ws);
+    a.part_ml = reinterpret_cast<float*>(ws + align256(rows * a.num_splits * MSA_HEAD_DIM * 4));
+  } else {
+    a.part_o = nullptr;
+    a.part_ml = nullptr;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(sparse_attn_kernel, grid, dim3(kAttnThreads), 0, s, a);
+  const dim3 grid(a.num_splits, kv->num_heads, unsigned(tq));
+  hipLaunchKernelGGL(sparse_attn_kernel<kAttnWaves>, grid, dim3(64 * kAttnWaves),
+                     attn_lds_bytes<kAttnWaves>(), s, a);
   if (hipGetLastError() != hipSuccess) return MSA_ERR_HIP;
   if (a.num_splits > 1) {
-    hipLaunchKernelGGL(merge_kernel, dim3(unsigned(tq * kv->num_heads)), dim3(kAttnThreads), 0, s,
+    hipLaunchKernelGGL(merge_kernel, dim3(unsigned(tq * kv->num_heads)), dim3(256), 0, s,
                        a.part_o, a.part_ml, a.num_splits, out);
     if (hipGetLastError() != hipSuccess) return MSA_ERR_HIP;
   }

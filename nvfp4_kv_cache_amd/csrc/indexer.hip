@@ -42,8 +42,6 @@ struct IndexerArgs {
   int q_per_seq;
   int blocks_per_wg;
   float* bscore;       // [num_seqs * q_per_seq][max_blocks]
-  int32_t* out_ids;
-  float* out_scores;
 };
 
 __device__ __forceinline__ float canon_score(float s) { return s > 0.0f ? s : 0.0f; }
@@ -54,84 +52,6 @@ __device__ __forceinline__ uint64_t score_key(float s, int j) {
 }
 __device__ __forceinline__ int key_block(uint64_t k) { return int(0xFFFFFFFFu - uint32_t(k)); }
 __device__ __forceinline__ float key_score(uint64_t k) { return __uint_as_float(uint32_t(k >> 32)); }
-
-// Top-16 of blocks 0..nb-2 plus block nb-1, ascending, for one query token;
-// executed by one whole wavefront. `bs` holds the nb block scores, normally
-// staged in LDS by the workgroup (a generic pointer: LDS or global memory).
-// buf: 80 wave-private LDS slots.
-__device__ void select_blocks(const float* bs, int nb, int32_t* __restrict__ ids,
-                              float* __restrict__ scores, uint64_t* buf, int lane) {
-  constexpr int K = MSA_TOPK;
-  if (nb <= K + 1) {
-    if (lane < K + 1) {
-      ids[lane] = lane < nb ? lane : -1;
-      if (scores) scores[lane] = lane < nb ? canon_score(bs[lane]) : 0.0f;
-    }
-    return;
-  }
-  const int n = nb - 1;  // candidates; the recent block is always kept
-  // 1. each lane's best key; theta = the 16th best lane maximum. At least 16
-  //    keys are >= theta, so the top-16 are among the keys >= theta.
-  uint64_t best = 0;
-  for (int j = lane; j < n; j += 64) {
-    const uint64_t key = score_key(bs[j], j);
-    best = key > best ? key : best;
-  }
-  int rank = 0;
-  for (int src = 0; src < 64; ++src) rank += readlane_u64(best, src) > best ? 1 : 0;
-  const uint64_t m15 = __ballot(rank == K - 1);
-  const uint64_t theta = readlane_u64(best, __builtin_ctzll(m15));
-  int cnt = 0;
-  for (int j = lane; j < n; j += 64) cnt += score_key(bs[j], j) >= theta ? 1 : 0;
-  const int survivors = wave_sum_int(cnt);
-
-  uint64_t mine = 0;  // lanes 0..15 end with the selected keys (any order)
-  if (survivors <= 64) {
-    // 2a. gather the survivors, rank them exactly, keep ranks 0..15
-    int base = 0;
-    for (int j0 = 0; j0 < n; j0 += 64) {
-      const int j = j0 + lane;
-      const uint64_t key = j < n ? score_key(bs[j], j) : 0ull;
-      const bool p = j < n && key >= theta;
-      const uint64_t mask = __ballot(p);
-      if (p) buf[base + __popcll(mask & ((1ull << lane) - 1ull))] = key;
-      base += __popcll(mask);
-    }
-    wave_lds_sync();
-    const uint64_t cand = lane < survivors ? buf[lane] : 0;
-    int r = 0;
-    for (int i = 0; i < survivors; ++i) r += buf[i] > cand ? 1 : 0;
-    if (lane < survivors && r < K) buf[64 + r] = cand;
-    wave_lds_sync();
-    mine = lane < K ? buf[64 + lane] : 0;
-    wave_lds_sync();
-  } else {
-    // 2b. many near-equal candidates: 16 rounds of wavefront arg-max
-    uint64_t last = ~0ull;
-    for (int r = 0; r < K; ++r) {
-      uint64_t b = 0;
-      for (int j = lane; j < n; j += 64) {
-        const uint64_t key = score_key(bs[j], j);
-        if (key < last && key > b) b = key;
-      }
-      b = wave_max_u64(b);
-      if (lane == r) mine = b;
-      last = b;
-    }
-  }
-  // 3. ascending block order
-  const int myblk = key_block(mine);
-  int order = 0;
-  for (int i = 0; i < K; ++i) order += key_block(readlane_u64(mine, i)) < myblk ? 1 : 0;
-  if (lane < K) {
-    ids[order] = myblk;
-    if (scores) scores[order] = key_score(mine);
-  }
-  if (lane == 0) {
-    ids[K] = nb - 1;
-    if (scores) scores[K] = canon_score(bs[nb - 1]);
-  }
-}
 
 // Block scores of all query tokens of a sequence staged in LDS when they fit.
 constexpr int kStageFloats = 12288;  // 48 KiB of LDS
@@ -167,7 +87,7 @@ __device__ __forceinline__ void issue_loads(TileLoads& t, const uint8_t* codes_h
 // QG: 16-row MFMA groups per index head = ceil(8 * q_per_seq / 16).
 template <int QG>
 __global__ __launch_bounds__(512) void indexer_kernel(const IndexerArgs a) {
-  extern __shared__ float part[];  // [2][H][2*QG][128] per-head partial token scores
+  extern __shared__ float part[];  // [2][H][2*QG][2][128] partial token scores per head group half
   __shared__ uint2 lut[128];
   __shared__ int pages[kMaxBlocksPerWg];
 
@@ -220,26 +140,25 @@ __global__ __launch_bounds__(512) void indexer_kernel(const IndexerArgs a) {
   const int64_t page_scales = int64_t(H) * kScalePage;
   const uint8_t* codes_h = a.codes + int64_t(wave) * kCodePage + (lane & 15) * kCodeRow + slice * 16;
   const uint8_t* scales_h = a.scales + int64_t(wave) * kScalePage + (lane & 15) * kScaleRow + slice * 2;
-  const int part_stride = H * QR * kBlockTokens;
-  // every lane writes its token's partial; lanes l and l^16 hold equal sums
-  const int part_lane = (lane >> 5) * kBlockTokens + (lane & 15);
+  const int part_stride = H * QR * 2 * kBlockTokens;
+  // lane l holds query token 2rg + l/32, heads 4*((l/16)&1) .. +3 of the
+  // group, token 16j + l%16: each lane writes its own partial
+  const int part_lane = ((lane >> 5) * 2 + ((lane >> 4) & 1)) * kBlockTokens + (lane & 15);
 
   // dequantise, multiply, apply ReLU and weights; per-head partials to LDS
   auto compute = [&](const TileLoads& t, int buf) {
-    float* pw = part + buf * part_stride + wave * QR * kBlockTokens + part_lane;
+    float* pw = part + buf * part_stride + wave * QR * 2 * kBlockTokens + part_lane;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const v8i kop = dequant32(t.c[j], lut[t.s[j] & 0x7F], lut[(t.s[j] >> 8) & 0x7F]);
 #pragma unroll
       for (int rg = 0; rg < QG; ++rg) {
         const v4f acc = mfma_fp8_16x16x128(qop[rg], kop, v4f{0.0f, 0.0f, 0.0f, 0.0f});
-        float s = wv[rg][0] * (acc[0] > 0.0f ? acc[0] : 0.0f);
-        s += wv[rg][1] * (acc[1] > 0.0f ? acc[1] : 0.0f);
-        s += wv[rg][2] * (acc[2] > 0.0f ? acc[2] : 0.0f);
-        s += wv[rg][3] * (acc[3] > 0.0f ? acc[3] : 0.0f);
-        // lanes l and l^16 hold heads 0-3 and 4-7 of the same query token
-        s += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(s), 0x401F));
-        pw[2 * rg * kBlockTokens + 16 * j] = s;
+        float s = wv[rg][0] * fmaxf(acc[0], 0.0f);
+        s += wv[rg][1] * fmaxf(acc[1], 0.0f);
+        s += wv[rg][2] * fmaxf(acc[2], 0.0f);
+        s += wv[rg][3] * fmaxf(acc[3], 0.0f);
+        pw[2 * rg * 2 * kBlockTokens + 16 * j] = s;
       }
     }
   };
@@ -249,12 +168,13 @@ __global__ __launch_bounds__(512) void indexer_kernel(const IndexerArgs a) {
     for (int qi = wave; qi < Q; qi += H) {
       const int pos = L - Q + qi;
       if (blk * kBlockTokens > pos) continue;  // block not visible to this query token
-      const float* pq = part + buf * part_stride + qi * kBlockTokens;
+      const float* pq = part + buf * part_stride + qi * 2 * kBlockTokens;
       float m = 0.0f;
 #pragma unroll
       for (int t = lane; t < kBlockTokens; t += 64) {
         float s = 0.0f;
-        for (int h = 0; h < H; ++h) s += pq[h * QR * kBlockTokens + t];
+        for (int h = 0; h < H; ++h)
+          s += pq[h * QR * 2 * kBlockTokens + t] + pq[h * QR * 2 * kBlockTokens + kBlockTokens + t];
         if (blk * kBlockTokens + t <= pos) m = fmaxf(m, s);
       }
       m = wave_max(m);
@@ -281,56 +201,276 @@ __global__ __launch_bounds__(512) void indexer_kernel(const IndexerArgs a) {
   }
 }
 
-// Selection kernel: one wavefront per query token. The block scores of the
-// query token are staged in LDS with independent loads (up to kStageFloats;
-// longer histories are read from global memory), then select_blocks runs.
-__global__ __launch_bounds__(64) void select_kernel(const float* __restrict__ bscore,
-                                                    const int32_t* __restrict__ seq_lens,
-                                                    int max_blocks, int q_per_seq,
-                                                    int32_t* __restrict__ out_ids,
-                                                    float* __restrict__ out_scores) {
+// Selection kernel: one 256-thread workgroup per query token. The block
+// scores are staged in LDS with independent loads. theta = the 16th best of
+// the 256 threads' maxima (each wave contributes its 16 best, wave 0 ranks
+// those 64), so at least 16 keys lie at or above theta and the survivors
+// (keys >= theta) contain the top-16; wave 0 ranks the survivors exactly.
+// Ranks are counted against values broadcast with lane reads, not LDS. More
+// than 64 survivors (many near-equal scores) fall back to 16 rounds of
+// arg-max in wave 0.
+constexpr int kSelThreads = 256;
+constexpr int kSelPerThread = 8;
+constexpr int kSelChunk = kSelThreads * kSelPerThread;
+
+// number of lanes whose key is larger than this lane's key
+__device__ __forceinline__ int lane_rank(uint64_t key) {
+  int r = 0;
+#pragma unroll
+  for (int src = 0; src < 64; ++src) r += readlane_u64(key, src) > key ? 1 : 0;
+  return r;
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __restrict__ bscore,
+                                                             const int32_t* __restrict__ seq_lens,
+                                                             int max_blocks, int q_per_seq,
+                                                             int32_t* __restrict__ out_ids,
+                                                             float* __restrict__ out_scores) {
   extern __shared__ float stage[];
-  __shared__ uint64_t buf[80];
+  __shared__ uint64_t s_keys[64];
+  __shared__ uint64_t s_sel[MSA_TOPK];
+  __shared__ uint64_t s_top[kSelThreads / 64 * MSA_TOPK];
+  __shared__ uint64_t s_theta;
+  __shared__ int s_count[kSelThreads / 64];
+  __shared__ int s_fill;
+  constexpr int K = MSA_TOPK;
   const int row = blockIdx.x;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int Q = q_per_seq;
   const int b = row / Q, qi = row - b * Q;
   const int L = seq_lens[b];
-  int32_t* ids = out_ids + int64_t(row) * (MSA_TOPK + 1);
-  float* sc = out_scores ? out_scores + int64_t(row) * (MSA_TOPK + 1) : nullptr;
+  int32_t* ids = out_ids + int64_t(row) * (K + 1);
+  float* sc = out_scores ? out_scores + int64_t(row) * (K + 1) : nullptr;
   if (L < Q || L > max_blocks * kBlockTokens) {
-    if (lane < MSA_TOPK + 1) {
-      ids[lane] = -1;
-      if (sc) sc[lane] = 0.0f;
+    if (tid < K + 1) {
+      ids[tid] = -1;
+      if (sc) sc[tid] = 0.0f;
     }
     return;
   }
   const int nb = (L - Q + qi) / kBlockTokens + 1;
   const float* src = bscore + int64_t(row) * max_blocks;
-  const float* bs = src;
-  if (nb <= kStageFloats) {
-    for (int j0 = 0; j0 < nb; j0 += 8 * 64) {
-      float t[8];
+  if (nb <= K + 1) {
+    if (tid < K + 1) {
+      ids[tid] = tid < nb ? tid : -1;
+      if (sc) sc[tid] = tid < nb ? canon_score(src[tid]) : 0.0f;
+    }
+    return;
+  }
+  const bool staged = nb <= kStageFloats;
+  if (staged) {
+    for (int j0 = 0; j0 < nb; j0 += kSelChunk) {
+      float t[kSelPerThread];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int j = j0 + lane + 64 * k;
+      for (int k = 0; k < kSelPerThread; ++k) {
+        const int j = j0 + tid + kSelThreads * k;
         t[k] = j < nb ? src[j] : 0.0f;
       }
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int j = j0 + lane + 64 * k;
+      for (int k = 0; k < kSelPerThread; ++k) {
+        const int j = j0 + tid + kSelThreads * k;
         if (j < nb) stage[j] = t[k];
       }
     }
-    wave_lds_sync();
-    bs = stage;
   }
-  select_blocks(bs, nb, ids, sc, buf, lane);
+  if (tid < kSelThreads / 64 * K) s_top[tid] = 0ull;
+  if (tid == 0) s_fill = 0;
+  __syncthreads();
+  const int n = nb - 1;  // candidates; the recent block is always kept
+  auto score_at = [&](int j) { return staged ? stage[j] : src[j]; };
+  // 1. thread maxima; each wave's 16 best; theta over the 64
+  uint64_t best = 0;
+  for (int j0 = 0; j0 < n; j0 += kSelChunk) {
+#pragma unroll
+    for (int k = 0; k < kSelPerThread; ++k) {
+      const int j = j0 + tid + kSelThreads * k;
+      if (j < n) {
+        const uint64_t key = score_key(score_at(j), j);
+        best = key > best ? key : best;
+      }
+    }
+  }
+  const int wr = lane_rank(best);
+  if (wr < K && best != 0ull) s_top[wave * K + wr] = best;
+  __syncthreads();
+  if (wave == 0) {
+    const uint64_t mk = s_top[lane];
+    const int r = lane_rank(mk);
+    const uint64_t m15 = __ballot(r == K - 1 && mk != 0ull);
+    if (lane == 0) s_theta = m15 ? s_top[__builtin_ctzll(m15)] : 0ull;
+  }
+  __syncthreads();
+  const uint64_t theta = s_theta;
+  // 2. survivors (keys >= theta)
+  int cnt = 0;
+  for (int j0 = 0; j0 < n; j0 += kSelChunk) {
+#pragma unroll
+    for (int k = 0; k < kSelPerThread; ++k) {
+      const int j = j0 + tid + kSelThreads * k;
+      if (j < n) cnt += score_key(score_at(j), j) >= theta ? 1 : 0;
+    }
+  }
+  cnt = wave_sum_int(cnt);
+  if (lane == 0) s_count[wave] = cnt;
+  __syncthreads();
+  int survivors = 0;
+#pragma unroll
+  for (int w = 0; w < kSelThreads / 64; ++w) survivors += s_count[w];
+  uint64_t mine = 0;  // wave 0: lanes 0..15 end with the selected keys
+  if (survivors <= 64) {
+    for (int j0 = 0; j0 < n; j0 += kSelChunk) {
+#pragma unroll
+      for (int k = 0; k < kSelPerThread; ++k) {
+        const int j = j0 + tid + kSelThreads * k;
+        if (j < n) {
+          const uint64_t key = score_key(score_at(j), j);
+          if (key >= theta) s_keys[atomicAdd(&s_fill, 1)] = key;
+        }
+      }
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    const uint64_t cand = lane < survivors ? s_keys[lane] : 0ull;
+    const int r = lane_rank(cand);
+    if (lane < survivors && r < K) s_sel[r] = cand;
+    wave_lds_sync();
+    mine = lane < K ? s_sel[lane] : 0ull;
+  } else {
+    if (wave != 0) return;
+    uint64_t last = ~0ull;
+    for (int r = 0; r < K; ++r) {
+      uint64_t bb = 0;
+      for (int j = lane; j < n; j += 64) {
+        const uint64_t key = score_key(score_at(j), j);
+        if (key < last && key > bb) bb = key;
+      }
+      bb = wave_max_u64(bb);
+      if (lane == r) mine = bb;
+      last = bb;
+    }
+  }
+  // 3. ascending block order
+  const int myblk = key_block(mine);
+  int order = 0;
+#pragma unroll
+  for (int i = 0; i < K; ++i) order += key_block(readlane_u64(mine, i)) < myblk ? 1 : 0;
+  if (lane < K) {
+    ids[order] = myblk;
+    if (sc) sc[order] = key_score(mine);
+  }
+  if (lane == 0) {
+    ids[K] = nb - 1;
+    if (sc) sc[K] = canon_score(score_at(nb - 1));
+  }
 }
 
-inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+}  // namespace msa
+
+namespace msa {
+
+// Host-side checks shared by the indexer entry points.
+static msa_status check_indexer_shape(int32_t num_seqs, int32_t q_per_seq, int32_t max_blocks) {
+  if (num_seqs < 0 || max_blocks <= 0 || q_per_seq <= 0) return MSA_ERR_INVALID_ARG;
+  if (q_per_seq > MSA_MAX_Q_PER_SEQ) return MSA_ERR_UNSUPPORTED;
+  if (int64_t(max_blocks) * MSA_BLOCK_TOKENS > 0x7FFFFFFF) return MSA_ERR_UNSUPPORTED;
+  if (num_seqs > 65535) return MSA_ERR_UNSUPPORTED;
+  return MSA_OK;
+}
+
+static bool misaligned(const void* p, uintptr_t m) { return (reinterpret_cast<uintptr_t>(p) & m) != 0; }
+
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+static msa_status launch_scan(const msa_pool_desc* idx, const uint8_t* idx_codes,
+                              const uint8_t* idx_scales, const uint8_t* q_fp8, const float* head_w,
+                              int32_t num_q_heads, const int32_t* block_table, int32_t max_blocks,
+                              const int32_t* seq_lens, int32_t num_seqs, int32_t q_per_seq,
+                              float* block_scores, hipStream_t s) {
+  IndexerArgs a;
+  a.codes = idx_codes;
+  a.scales = idx_scales;
+  a.num_pages = idx->num_pages;
+  a.num_heads = idx->num_heads;
+  a.q = q_fp8;
+  a.w = head_w;
+  a.num_q_heads = num_q_heads;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks;
+  a.seq_lens = seq_lens;
+  a.q_per_seq = q_per_seq;
+  a.bscore = block_scores;
+  const int qg = (MSA_HEADS_PER_KV * q_per_seq + 15) / 16;
+  int bpw = 8;
+  while (bpw > 1 && int64_t(num_seqs) * ((max_blocks + bpw - 1) / bpw) < 2048) bpw >>= 1;
+  a.blocks_per_wg = bpw;
+  const dim3 grid((max_blocks + bpw - 1) / bpw, num_seqs);
+  const dim3 block(64 * idx->num_heads);
+  const int qg_pow2 = qg == 1 ? 1 : (qg == 2 ? 2 : 4);
+  const size_t lds = size_t(2) * idx->num_heads * (2 * qg_pow2) * 2 * MSA_BLOCK_TOKENS * sizeof(float);
+  if (qg_pow2 == 1)
+    hipLaunchKernelGGL(indexer_kernel<1>, grid, block, lds, s, a);
+  else if (qg_pow2 == 2)
+    hipLaunchKernelGGL(indexer_kernel<2>, grid, block, lds, s, a);
+  else
+    hipLaunchKernelGGL(indexer_kernel<4>, grid, block, lds, s, a);
+  return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
+}
+
+static msa_status launch_select(const float* block_scores, const int32_t* seq_lens,
+                                int32_t max_blocks, int32_t num_seqs, int32_t q_per_seq,
+                                int32_t* out_ids, float* out_scores, hipStream_t s) {
+  const int stage = max_blocks < kStageFloats ? max_blocks : kStageFloats;
+  hipLaunchKernelGGL(select_kernel, dim3(unsigned(int64_t(num_seqs) * q_per_seq)),
+                     dim3(kSelThreads), size_t(stage) * sizeof(float), s, block_scores, seq_lens,
+                     max_blocks, q_per_seq, out_ids, out_scores);
+  return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
+}
 
 }  // namespace msa
+
+extern "C" msa_status msa_indexer_scan(const msa_pool_desc* idx, const uint8_t* idx_codes,
+                                       const uint8_t* idx_scales, const uint8_t* q_fp8,
+                                       const float* head_w, int32_t num_q_heads,
+                                       const int32_t* block_table, int32_t max_blocks,
+                                       const int32_t* seq_lens, int32_t num_seqs,
+                                       int32_t q_per_seq, float* block_scores, void* stream) {
+  using namespace msa;
+  if (!idx) return MSA_ERR_INVALID_ARG;
+  msa_status st = check_indexer_shape(num_seqs, q_per_seq, max_blocks);
+  if (st != MSA_OK) return st;
+  if (idx->head_dim != MSA_HEAD_DIM || idx->block_tokens != MSA_BLOCK_TOKENS)
+    return MSA_ERR_UNSUPPORTED;
+  if (idx->num_heads < 1 || idx->num_heads > MSA_MAX_HEADS) return MSA_ERR_UNSUPPORTED;
+  if (num_q_heads != MSA_HEADS_PER_KV * idx->num_heads) return MSA_ERR_UNSUPPORTED;
+  if (idx->num_pages <= 0 || idx->num_pages > 0x7FFFFFFF) return MSA_ERR_INVALID_ARG;
+  if (num_seqs == 0) return MSA_OK;
+  if (!idx_codes || !idx_scales || !q_fp8 || !head_w || !block_table || !seq_lens || !block_scores)
+    return MSA_ERR_INVALID_ARG;
+  if (misaligned(idx_codes, 15) || misaligned(idx_scales, 15) || misaligned(q_fp8, 15) ||
+      misaligned(head_w, 3) || misaligned(block_table, 3) || misaligned(seq_lens, 3) ||
+      misaligned(block_scores, 3))
+    return MSA_ERR_INVALID_ARG;
+  return launch_scan(idx, idx_codes, idx_scales, q_fp8, head_w, num_q_heads, block_table,
+                     max_blocks, seq_lens, num_seqs, q_per_seq, block_scores,
+                     static_cast<hipStream_t>(stream));
+}
+
+extern "C" msa_status msa_indexer_select(const float* block_scores, const int32_t* seq_lens,
+                                         int32_t max_blocks, int32_t num_seqs, int32_t q_per_seq,
+                                         int32_t topk, int32_t* out_ids, float* out_scores,
+                                         void* stream) {
+  using namespace msa;
+  msa_status st = check_indexer_shape(num_seqs, q_per_seq, max_blocks);
+  if (st != MSA_OK) return st;
+  if (topk != MSA_TOPK) return MSA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return MSA_OK;
+  if (!block_scores || !seq_lens || !out_ids) return MSA_ERR_INVALID_ARG;
+  if (misaligned(block_scores, 3) || misaligned(seq_lens, 3) || misaligned(out_ids, 3) ||
+      misaligned(out_scores, 3))
+    return MSA_ERR_INVALID_ARG;
+  return launch_select(block_scores, seq_lens, max_blocks, num_seqs, q_per_seq, out_ids,
+                       out_scores, static_cast<hipStream_t>(stream));
+}
 
 extern "C" size_t msa_indexer_workspace_bytes(int32_t num_seqs, int32_t q_per_seq,
                                               int32_t max_blocks) {
@@ -347,61 +487,28 @@ extern "C" msa_status msa_indexer_decode(const msa_pool_desc* idx, const uint8_t
                                          float* out_scores, void* workspace,
                                          size_t workspace_bytes, void* stream) {
   using namespace msa;
-  if (!idx || num_seqs < 0 || max_blocks <= 0 || q_per_seq <= 0) return MSA_ERR_INVALID_ARG;
+  if (!idx) return MSA_ERR_INVALID_ARG;
+  msa_status st = check_indexer_shape(num_seqs, q_per_seq, max_blocks);
+  if (st != MSA_OK) return st;
+  if (topk != MSA_TOPK) return MSA_ERR_UNSUPPORTED;
   if (idx->head_dim != MSA_HEAD_DIM || idx->block_tokens != MSA_BLOCK_TOKENS)
     return MSA_ERR_UNSUPPORTED;
   if (idx->num_heads < 1 || idx->num_heads > MSA_MAX_HEADS) return MSA_ERR_UNSUPPORTED;
   if (num_q_heads != MSA_HEADS_PER_KV * idx->num_heads) return MSA_ERR_UNSUPPORTED;
-  if (topk != MSA_TOPK || q_per_seq > MSA_MAX_Q_PER_SEQ) return MSA_ERR_UNSUPPORTED;
   if (idx->num_pages <= 0 || idx->num_pages > 0x7FFFFFFF) return MSA_ERR_INVALID_ARG;
-  if (int64_t(max_blocks) * MSA_BLOCK_TOKENS > 0x7FFFFFFF) return MSA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return MSA_OK;
-  if (num_seqs > 65535) return MSA_ERR_UNSUPPORTED;
   if (!idx_codes || !idx_scales || !q_fp8 || !head_w || !block_table || !seq_lens || !out_ids)
     return MSA_ERR_INVALID_ARG;
-  auto mis = [](const void* p, uintptr_t m) { return (reinterpret_cast<uintptr_t>(p) & m) != 0; };
-  if (mis(idx_codes, 15) || mis(idx_scales, 15) || mis(q_fp8, 15) || mis(head_w, 3) ||
-      mis(block_table, 3) || mis(seq_lens, 3) || mis(out_ids, 3) || mis(out_scores, 3))
+  if (misaligned(idx_codes, 15) || misaligned(idx_scales, 15) || misaligned(q_fp8, 15) ||
+      misaligned(head_w, 3) || misaligned(block_table, 3) || misaligned(seq_lens, 3) ||
+      misaligned(out_ids, 3) || misaligned(out_scores, 3))
     return MSA_ERR_INVALID_ARG;
   const size_t need = msa_indexer_workspace_bytes(num_seqs, q_per_seq, max_blocks);
-  if (!workspace || workspace_bytes < need || mis(workspace, 255)) return MSA_ERR_WORKSPACE;
-
-  IndexerArgs a;
-  a.codes = idx_codes;
-  a.scales = idx_scales;
-  a.num_pages = idx->num_pages;
-  a.num_heads = idx->num_heads;
-  a.q = q_fp8;
-  a.w = head_w;
-  a.num_q_heads = num_q_heads;
-  a.block_table = block_table;
-  a.max_blocks = max_blocks;
-  a.seq_lens = seq_lens;
-  a.q_per_seq = q_per_seq;
-  a.bscore = static_cast<float*>(workspace);
-  a.out_ids = out_ids;
-  a.out_scores = out_scores;
-  // enough workgroups to fill 256 CUs several times over
-  int bpw = 8;
-  while (bpw > 1 && int64_t(num_seqs) * ((max_blocks + bpw - 1) / bpw) < 2048) bpw >>= 1;
-  a.blocks_per_wg = bpw;
-  const dim3 grid((max_blocks + bpw - 1) / bpw, num_seqs);
-  const dim3 block(64 * idx->num_heads);
-  const int qg = (MSA_HEADS_PER_KV * q_per_seq + 15) / 16;
-  const int qg_pow2 = qg == 1 ? 1 : (qg == 2 ? 2 : 4);
-  const size_t part_lds = size_t(2) * idx->num_heads * (2 * qg_pow2) * MSA_BLOCK_TOKENS * sizeof(float);
-  const size_t lds = part_lds;
+  if (!workspace || workspace_bytes < need || misaligned(workspace, 255)) return MSA_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (qg_pow2 == 1)
-    hipLaunchKernelGGL(indexer_kernel<1>, grid, block, lds, s, a);
-  else if (qg_pow2 == 2)
-    hipLaunchKernelGGL(indexer_kernel<2>, grid, block, lds, s, a);
-  else
-    hipLaunchKernelGGL(indexer_kernel<4>, grid, block, lds, s, a);
-  if (hipGetLastError() != hipSuccess) return MSA_ERR_HIP;
-  const int stage = max_blocks < kStageFloats ? max_blocks : kStageFloats;
-  hipLaunchKernelGGL(select_kernel, dim3(unsigned(int64_t(num_seqs) * q_per_seq)), dim3(64),
-                     size_t(stage) * sizeof(float), s, a.bscore, seq_lens, max_blocks, q_per_seq,
-                     out_ids, out_scores);
-  return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
+  float* scores = static_cast<float*>(workspace);
+  st = launch_scan(idx, idx_codes, idx_scales, q_fp8, head_w, num_q_heads, block_table, max_blocks,
+                   seq_lens, num_seqs, q_per_seq, scores, s);
+  if (st != MSA_OK) return st;
+  return launch_select(scores, seq_lens, max_blocks, num_seqs, q_per_seq, out_ids, out_scores, s);
 }

@@ -220,6 +220,54 @@ def test_deterministic_and_reusable_workspace(nb):
             assert np.array_equal(x, y)
 
 
+def test_two_stage_indexer_equals_decode(nb):
+    say("scan + select == decode")
+    wl = tiny_config([5000, 3001, 129, 2200], 3, seed=4)
+    pools = S.fill_pools(wl, nb)
+    inp = S.device_inputs(wl)
+    ic, isc = pools[synth.STREAM_IDX]
+    tq = wl.num_q_tokens
+    ws = nb.indexer_workspace(wl.num_seqs, wl.q_per_seq, wl.max_blocks)
+    ids1 = torch.empty((tq, 17), dtype=torch.int32, device="cuda")
+    sc1 = torch.empty((tq, 17), dtype=torch.float32, device="cuda")
+    nb.msa_indexer_decode(ic, isc, inp["q_idx"], inp["w"], inp["block_table"], inp["seq_lens"],
+                          wl.q_per_seq, ids1, ws, out_scores=sc1)
+    bscores = torch.full((tq, wl.max_blocks), -7.0, dtype=torch.float32, device="cuda")
+    nb.msa_indexer_scan(ic, isc, inp["q_idx"], inp["w"], inp["block_table"], inp["seq_lens"],
+                        wl.q_per_seq, bscores)
+    ids2 = torch.empty_like(ids1)
+    sc2 = torch.empty_like(sc1)
+    nb.msa_indexer_select(bscores, inp["seq_lens"], wl.q_per_seq, ids2, sc2)
+    torch.cuda.synchronize()
+    assert torch.equal(ids1, ids2) and torch.equal(sc1, sc2)
+    # entries past each query token's visible blocks are left untouched
+    bs = bscores.cpu().numpy()
+    for b in range(wl.num_seqs):
+        for i, pos in enumerate(wl.positions(b)):
+            row = b * wl.q_per_seq + i
+            nbk = pos // 128 + 1
+            assert np.all(bs[row, nbk:] == -7.0) and np.all(bs[row, :nbk] >= 0)
+
+
+def test_select_many_equal_scores(nb):
+    say("selection with all-equal and adversarial scores")
+    tq, mb = 4, 3000
+    lens = torch.tensor([mb * 128] * tq, dtype=torch.int32, device="cuda")
+    rng = np.random.default_rng(2)
+    bs = np.zeros((tq, mb), dtype=np.float32)
+    bs[1] = np.tile(np.arange(64, dtype=np.float32)[::-1], mb // 64 + 1)[:mb]   # periodic
+    bs[2] = rng.integers(0, 3, mb).astype(np.float32)                            # few levels
+    bs[3] = -0.0
+    ids = torch.empty((tq, 17), dtype=torch.int32, device="cuda")
+    sc = torch.empty((tq, 17), dtype=torch.float32, device="cuda")
+    nb.msa_indexer_select(torch.from_numpy(bs).cuda(), lens, 1, ids, sc)
+    torch.cuda.synchronize()
+    from oracle import msa
+    for r in range(tq):
+        want = msa.select_blocks(np.maximum(bs[r].astype(np.float64), 0.0))
+        assert ids[r].cpu().numpy().tolist() == want.tolist(), r
+
+
 def test_empty_batch_and_bad_shapes(nb):
     wl = tiny_config([300], 1)
     pools = S.fill_pools(wl, nb)

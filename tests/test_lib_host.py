@@ -44,7 +44,8 @@ def test_workspace_sizes(L):
     assert nb.msa_indexer_workspace_bytes(8, 1, 2048) == 8 * 2048 * 4
     assert nb.msa_indexer_workspace_bytes(0, 1, 10) == 0
     rows = 16 * 8 * 32
-    want = rows * 17 * 128 * 4 + rows * 17 * 2 * 4
+    splits = (17 + 3) // 4
+    want = rows * splits * 128 * 4 + rows * splits * 2 * 4
     got = nb.msa_attn_workspace_bytes(16, 8, 32, 17)
     assert want <= got <= want + 2 * 255
 
@@ -98,4 +99,20 @@ def test_attention_rejects_before_launch(L):
     assert call(scale=0.0) == 1 and call(scale=float("nan")) == 1
     assert call(ns=0) == 0
     assert call(ptr=None) == 1
-    assert call(ws=None) == 3
+    assert call(ptr=4096 + 4) == 1              # misaligned
+    assert call(ws=None) == 3                    # 17 blocks need split partials
+
+
+def test_two_stage_indexer_rejects_before_launch(L):
+    d = ctypes.byref(_desc())
+    scan = L.msa_indexer_scan
+    assert scan(None, 256, 256, 256, 256, 32, 256, 4, 256, 1, 1, 256, None) == 1
+    assert scan(d, 256, 256, 256, 256, 24, 256, 4, 256, 1, 1, 256, None) == 2
+    assert scan(d, 256, 256, 256, 256, 32, 256, 4, 256, 0, 1, None, None) == 0
+    assert scan(d, 256, 256, 256, 256, 32, 256, 4, 256, 1, 1, None, None) == 1
+    sel = L.msa_indexer_select
+    assert sel(256, 256, 4, 1, 1, 15, 256, None, None) == 2
+    assert sel(None, 256, 4, 1, 1, 16, 256, None, None) == 1
+    assert sel(256, 256, 0, 1, 1, 16, 256, None, None) == 1
+    assert sel(256, 256, 4, 0, 1, 16, None, None, None) == 0
+    assert sel(256, 256, 4, 1, 9, 16, 256, None, None) == 2
