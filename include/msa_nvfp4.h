@@ -42,8 +42,10 @@
  *   codes  uint8 [num_pages][num_heads][128 rows][64]  two E2M1 codes per byte,
  *          channel 2j in the low nibble of byte j, 2j+1 in the high nibble;
  *          code = sign << 3 | magnitude index (0, .5, 1, 1.5, 2, 3, 4, 6)
- *   scales uint8 [num_pages][num_heads][128 rows][8]   E4M3 scale of channels
- *          16g .. 16g+15 in byte g
+ *   scales uint8 [num_pages][num_heads][1024]  E4M3 scale of row r, channels
+ *          16g .. 16g+15 (g = 0..7) at byte ((g/2)*16 + r%16)*16 + (r/16)*2 + g%2
+ *          of its (page, head): tile-major, so one 16-byte load gives a
+ *          lane all 8 row-tiles' scales of its rows and 32-channel slice
  *
  * Sequences: sequence b has seq_lens[b] tokens in its pages, including its
  * q_per_seq query tokens (their keys are already written). Query token i of

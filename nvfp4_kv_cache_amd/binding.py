@@ -107,20 +107,33 @@ def pool_desc(codes: torch.Tensor) -> PoolDesc:
     return PoolDesc(codes.shape[1], HEAD_DIM, BLOCK_TOKENS, 0, codes.shape[0])
 
 
+SCALE_PAGE = BLOCK_TOKENS * HEAD_DIM // 16   # 1 KiB of scales per (page, head)
+
+
 def _check_pool(codes, scales, name):
     _need(codes, f"{name}_codes", torch.uint8, 4)
-    _need(scales, f"{name}_scales", torch.uint8, 4)
-    if tuple(scales.shape) != tuple(codes.shape[:3]) + (HEAD_DIM // 16,):
+    _need(scales, f"{name}_scales", torch.uint8, 3)
+    if tuple(scales.shape) != tuple(codes.shape[:2]) + (SCALE_PAGE,):
         raise ValueError(f"{name}_scales shape {tuple(scales.shape)} does not match codes")
 
 
 def empty_pool(num_pages: int, num_heads: int, device="cuda"):
-    """Uninitialised (codes, scales) pool tensors in the library's layout."""
+    """Uninitialised (codes, scales) pool tensors in the library's layout:
+    codes [pages, heads, 128, 64], scales [pages, heads, 1024] (tile-major)."""
     codes = torch.empty((num_pages, num_heads, BLOCK_TOKENS, HEAD_DIM // 2), dtype=torch.uint8,
                         device=device)
-    scales = torch.empty((num_pages, num_heads, BLOCK_TOKENS, HEAD_DIM // 16), dtype=torch.uint8,
-                         device=device)
+    scales = torch.empty((num_pages, num_heads, SCALE_PAGE), dtype=torch.uint8, device=device)
     return codes, scales
+
+
+def scales_rows(scales: torch.Tensor) -> torch.Tensor:
+    """Row-major view [pages, heads, 128 rows, 8 groups] of tile-major scales.
+
+    Byte ((g/2)*16 + r%16)*16 + (r/16)*2 + g%2 of a (page, head) holds the
+    scale of row r, group g (include/msa_nvfp4.h)."""
+    p, h = scales.shape[:2]
+    x = scales.reshape(p, h, 4, 16, 8, 2)          # [slice c][row i][tile j][e]
+    return x.permute(0, 1, 4, 3, 2, 5).reshape(p, h, BLOCK_TOKENS, HEAD_DIM // 16)
 
 
 def msa_nvfp4_quantize(src, slot_mapping, codes, scales):

@@ -134,7 +134,7 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(const AttnArgs a) {
   const int64_t page_codes = int64_t(a.num_kv_heads) * kCodePage;
   const int64_t page_scales = int64_t(a.num_kv_heads) * kScalePage;
   const int lane_code = li * kCodeRow + slice * 16;
-  const int lane_scale = li * kScaleRow + slice * 2;
+  const int lane_scale = scale_word_offset(slice, li);
   // transposed-read addresses: segment of lane i = row (i / 2) of an 8-row
   // group, left or right 8 bytes (V) / real or zero segment (P)
   const int seg_row = li >> 1, seg_half = li & 1;
@@ -154,22 +154,18 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(const AttnArgs a) {
     const int64_t hc = int64_t(page) * page_codes + int64_t(kh) * kCodePage + lane_code;
     const int64_t hs = int64_t(page) * page_scales + int64_t(kh) * kScalePage + lane_scale;
     uint4 kc[8], vc[8];
-    uint32_t ks[8], vsc[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      kc[j] = *reinterpret_cast<const uint4*>(a.k_codes + hc + j * 16 * kCodeRow);
-      ks[j] = *reinterpret_cast<const uint16_t*>(a.k_scales + hs + j * 16 * kScaleRow);
-    }
+    for (int j = 0; j < 8; ++j) kc[j] = load_stream16(a.k_codes + hc + j * 16 * kCodeRow);
+    const uint4 ksw = load_stream16(a.k_scales + hs);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      vc[j] = *reinterpret_cast<const uint4*>(a.v_codes + hc + j * 16 * kCodeRow);
-      vsc[j] = *reinterpret_cast<const uint16_t*>(a.v_scales + hs + j * 16 * kScaleRow);
-    }
+    for (int j = 0; j < 8; ++j) vc[j] = load_stream16(a.v_codes + hc + j * 16 * kCodeRow);
+    const uint4 vsw = load_stream16(a.v_scales + hs);
     // 1. logits of 16 tokens per tile: lane holds heads 4*slice+v, token 16j+li
     float z[8][4];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const v8i kop = dequant32(kc[j], lut[ks[j] & 0x7F], lut[(ks[j] >> 8) & 0x7F]);
+      const uint32_t ks = tile_scales(ksw, j);
+      const v8i kop = dequant32(kc[j], lut[ks & 0x7F], lut[(ks >> 8) & 0x7F]);
       const v4f c = mfma_fp8_16x16x128(qop, kop, v4f{0.0f, 0.0f, 0.0f, 0.0f});
       const bool live = 16 * j + li < ntok;
 #pragma unroll
@@ -178,7 +174,8 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(const AttnArgs a) {
     // 2. V rows into LDS in natural channel order (masked tokens -> 0)
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const v8i vop = dequant32(vc[j], lut[vsc[j] & 0x7F], lut[(vsc[j] >> 8) & 0x7F]);
+      const uint32_t vsc = tile_scales(vsw, j);
+      const v8i vop = dequant32(vc[j], lut[vsc & 0x7F], lut[(vsc >> 8) & 0x7F]);
       const bool live = 16 * j + li < ntok;
       uint32_t nat[8];
 #pragma unroll

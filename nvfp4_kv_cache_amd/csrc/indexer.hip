@@ -57,12 +57,17 @@ __device__ __forceinline__ float key_score(uint64_t k) { return __uint_as_float(
 constexpr int kStageFloats = 12288;  // 48 KiB of LDS
 
 constexpr int kMaxBlocksPerWg = 16;
+#ifndef MSA_SCAN_BLOCKS_PER_WG
+#define MSA_SCAN_BLOCKS_PER_WG 16
+#endif
+constexpr int kScanBlocksPerWg = MSA_SCAN_BLOCKS_PER_WG;
+static_assert(kScanBlocksPerWg <= kMaxBlocksPerWg, "page list size");
 
-// One block's worth of this wave's loads: 8 tiles x (16 code bytes, 2 scale
-// bytes) per lane.
+// One block's worth of this wave's loads: 8 tiles x 16 code bytes and the
+// 16-byte scale word (2 scale bytes per tile) per lane.
 struct TileLoads {
   uint4 c[8];
-  uint32_t s[8];
+  uint4 s;
 };
 
 __device__ __forceinline__ void issue_loads(TileLoads& t, const uint8_t* codes_h,
@@ -72,15 +77,12 @@ __device__ __forceinline__ void issue_loads(TileLoads& t, const uint8_t* codes_h
     const uint8_t* cp = codes_h + int64_t(page) * page_codes;
     const uint8_t* sp = scales_h + int64_t(page) * page_scales;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) t.c[j] = *reinterpret_cast<const uint4*>(cp + j * 16 * kCodeRow);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) t.s[j] = *reinterpret_cast<const uint16_t*>(sp + j * 16 * kScaleRow);
+    for (int j = 0; j < 8; ++j) t.c[j] = load_stream16(cp + j * 16 * kCodeRow);
+    t.s = load_stream16(sp);
   } else {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      t.c[j] = make_uint4(0, 0, 0, 0);
-      t.s[j] = 0;
-    }
+    for (int j = 0; j < 8; ++j) t.c[j] = make_uint4(0, 0, 0, 0);
+    t.s = make_uint4(0, 0, 0, 0);
   }
 }
 
@@ -104,12 +106,15 @@ __global__ __launch_bounds__(512) void indexer_kernel(const IndexerArgs a) {
   const int L = a.seq_lens[b];
   const bool seq_ok = L >= Q && L <= a.max_blocks * kBlockTokens;
   const int nb_last = seq_ok ? (L - 1) / kBlockTokens + 1 : 0;
-  const int blk0 = blockIdx.x * a.blocks_per_wg;
-  const int blk1 = min(nb_last, blk0 + a.blocks_per_wg);
+  // workgroup x of a sequence takes blocks x, x + G, x + 2G, ... (G = grid
+  // width), so the workgroups running at any moment read neighbouring pages
+  const int G = gridDim.x;
+  const int first = blockIdx.x;
+  const int count = nb_last > first ? min(a.blocks_per_wg, (nb_last - first + G - 1) / G) : 0;
   const int64_t qrow0 = int64_t(b) * Q;
   const int Hq = a.num_q_heads;
-  if (int(threadIdx.x) < blk1 - blk0) {
-    const int p = a.block_table[int64_t(b) * a.max_blocks + blk0 + threadIdx.x];
+  if (int(threadIdx.x) < count) {
+    const int p = a.block_table[int64_t(b) * a.max_blocks + first + threadIdx.x * G];
     pages[threadIdx.x] = (p >= 0 && p < a.num_pages) ? p : -1;
   }
 
@@ -139,7 +144,7 @@ __global__ __launch_bounds__(512) void indexer_kernel(const IndexerArgs a) {
   const int64_t page_codes = int64_t(H) * kCodePage;
   const int64_t page_scales = int64_t(H) * kScalePage;
   const uint8_t* codes_h = a.codes + int64_t(wave) * kCodePage + (lane & 15) * kCodeRow + slice * 16;
-  const uint8_t* scales_h = a.scales + int64_t(wave) * kScalePage + (lane & 15) * kScaleRow + slice * 2;
+  const uint8_t* scales_h = a.scales + int64_t(wave) * kScalePage + scale_word_offset(slice, lane & 15);
   const int part_stride = H * QR * 2 * kBlockTokens;
   // lane l holds query token 2rg + l/32, heads 4*((l/16)&1) .. +3 of the
   // group, token 16j + l%16: each lane writes its own partial
@@ -150,7 +155,8 @@ __global__ __launch_bounds__(512) void indexer_kernel(const IndexerArgs a) {
     float* pw = part + buf * part_stride + wave * QR * 2 * kBlockTokens + part_lane;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const v8i kop = dequant32(t.c[j], lut[t.s[j] & 0x7F], lut[(t.s[j] >> 8) & 0x7F]);
+      const uint32_t sj = tile_scales(t.s, j);
+      const v8i kop = dequant32(t.c[j], lut[sj & 0x7F], lut[(sj >> 8) & 0x7F]);
 #pragma unroll
       for (int rg = 0; rg < QG; ++rg) {
         const v4f acc = mfma_fp8_16x16x128(qop[rg], kop, v4f{0.0f, 0.0f, 0.0f, 0.0f});
@@ -163,8 +169,9 @@ __global__ __launch_bounds__(512) void indexer_kernel(const IndexerArgs a) {
     }
   };
   // sum the heads, maximise over the block's visible tokens, store B(blk)
-  auto reduce = [&](int blk, int buf) {
-    const bool page_ok = pages[blk - blk0] >= 0;
+  auto reduce = [&](int k, int buf) {
+    const bool page_ok = pages[k] >= 0;
+    const int blk = first + k * G;
     for (int qi = wave; qi < Q; qi += H) {
       const int pos = L - Q + qi;
       if (blk * kBlockTokens > pos) continue;  // block not visible to this query token
@@ -185,19 +192,17 @@ __global__ __launch_bounds__(512) void indexer_kernel(const IndexerArgs a) {
   // two-stage pipeline: the next block's loads are in flight while the
   // current block is computed
   TileLoads ta, tb;
-  if (blk0 < blk1) issue_loads(ta, codes_h, scales_h, pages[0], page_codes, page_scales);
-  for (int blk = blk0; blk < blk1; blk += 2) {
-    if (blk + 1 < blk1)
-      issue_loads(tb, codes_h, scales_h, pages[blk + 1 - blk0], page_codes, page_scales);
+  if (count > 0) issue_loads(ta, codes_h, scales_h, pages[0], page_codes, page_scales);
+  for (int k = 0; k < count; k += 2) {
+    if (k + 1 < count) issue_loads(tb, codes_h, scales_h, pages[k + 1], page_codes, page_scales);
     compute(ta, 0);
     __syncthreads();
-    reduce(blk, 0);
-    if (blk + 1 >= blk1) break;
-    if (blk + 2 < blk1)
-      issue_loads(ta, codes_h, scales_h, pages[blk + 2 - blk0], page_codes, page_scales);
+    reduce(k, 0);
+    if (k + 1 >= count) break;
+    if (k + 2 < count) issue_loads(ta, codes_h, scales_h, pages[k + 2], page_codes, page_scales);
     compute(tb, 1);
     __syncthreads();
-    reduce(blk + 1, 1);
+    reduce(k + 1, 1);
   }
 }
 

@@ -72,9 +72,10 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_kernel(
 
   const int64_t page = slot / kBlockTokens;
   const int row = int(slot % kBlockTokens);
-  const int64_t head_row = (page * num_heads + h) * kBlockTokens + row;
-  *reinterpret_cast<uint2*>(codes + head_row * kCodeRow + g * 8) = make_uint2(packed[0], packed[1]);
-  scales[head_row * kScaleRow + g] = uint8_t(sb);
+  const int64_t page_head = page * num_heads + h;
+  *reinterpret_cast<uint2*>(codes + (page_head * kBlockTokens + row) * kCodeRow + g * 8) =
+      make_uint2(packed[0], packed[1]);
+  scales[page_head * kScalePage + scale_offset(row, g)] = uint8_t(sb);
 }
 
 }  // namespace msa

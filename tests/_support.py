@@ -153,6 +153,7 @@ def check_page_bytes(wl, pools, pages, overrides=None):
     """Bit-exact comparison of the GPU pool bytes of `pages` (written rows
     only) with the oracle's quantisation of the same sources."""
     from oracle import nvfp4
+    from nvfp4_kv_cache_amd import scales_rows
     rows = page_rows(wl)
     fails = []
     for st, (codes, scales) in pools.items():
@@ -166,7 +167,7 @@ def check_page_bytes(wl, pools, pages, overrides=None):
                 src = overrides(st, np.array([p]), src)
             c, s = nvfp4.quantize(src.numpy())          # [128, H, 64], [128, H, 8]
             gc = codes[p].cpu().numpy().transpose(1, 0, 2)[:n]
-            gs = scales[p].cpu().numpy().transpose(1, 0, 2)[:n]
+            gs = scales_rows(scales[p:p + 1])[0].cpu().numpy().transpose(1, 0, 2)[:n]
             if not np.array_equal(gc, c[:n]) or not np.array_equal(gs, s[:n]):
                 bad = int(np.sum(gc != c[:n]) + np.sum(gs != s[:n]))
                 fails.append(f"stream {st} page {p}: {bad} bytes differ")

@@ -116,3 +116,15 @@ def test_two_stage_indexer_rejects_before_launch(L):
     assert sel(256, 256, 0, 1, 1, 16, 256, None, None) == 1
     assert sel(256, 256, 4, 0, 1, 16, None, None, None) == 0
     assert sel(256, 256, 4, 1, 9, 16, 256, None, None) == 2
+
+
+def test_scale_layout_view_matches_header_formula():
+    import torch
+    from nvfp4_kv_cache_amd import scales_rows
+    p_, h_ = 2, 3
+    phys = torch.arange(p_ * h_ * 1024, dtype=torch.int64).reshape(p_, h_, 1024)
+    rows = scales_rows(phys)
+    for r in range(128):
+        for g in range(8):
+            off = ((g // 2) * 16 + r % 16) * 16 + (r // 16) * 2 + g % 2
+            assert int(rows[1, 2, r, g]) == (1 * h_ + 2) * 1024 + off
