@@ -9,18 +9,19 @@
 // query tokens are batched to fill the matrix units (serving summary,
 // section "Parallelize index work across context").
 //
-// One kernel, grid (block chunks, sequences); one wavefront per index-key
-// head. Per 128-token block a wave streams its head's 8 KiB of codes and
-// 1 KiB of scales in coalesced 16-byte loads (lane l: token row 16j + l%16,
-// 32-channel slice l/16), turns them into FP8 MFMA operands through the LDS
-// lookup table, and multiplies them with the FP8 index queries held in
-// registers: A = queries (16 rows = 8 heads x up to 2 query tokens),
-// B = 16 tokens x 128 channels. The epilogue applies ReLU and the head
-// weights, sums the 8 heads of the group across the two 16-lane halves,
-// and leaves per-token partial scores in LDS; the waves' partials are summed
-// over heads and maximised over the block's visible tokens. When every
-// workgroup of a sequence has written its block scores, the last one selects
-// the blocks (wavefront ballots and lane reads, no sort).
+// Two kernels. The scan kernel has grid (block chunks, sequences) and one
+// wavefront per index-key head; workgroup x of a sequence takes blocks x,
+// x + G, x + 2G, ... (G = grid width). Per 128-token block a wave streams its
+// head's 8 KiB of codes and 1 KiB of scales in coalesced 16-byte
+// non-temporal loads (lane l: token row 16j + l%16, 32-channel slice l/16),
+// turns them into FP8 MFMA operands through the LDS lookup table, and
+// multiplies them with the FP8 index queries held in registers:
+// A = queries (16 rows = 8 heads x up to 2 query tokens), B = 16 tokens x 128
+// channels. The epilogue applies ReLU and the head weights and leaves
+// per-token partial scores in LDS; the waves' partials are summed over heads
+// and maximised over the block's visible tokens, giving one fp32 block score
+// per (query token, block). The selection kernel then picks, per query
+// token, the top-16 blocks plus the most recent one.
 #include "msa_nvfp4.h"
 #include "nvfp4_tile.h"
 
@@ -56,12 +57,7 @@ __device__ __forceinline__ float key_score(uint64_t k) { return __uint_as_float(
 // Block scores of all query tokens of a sequence staged in LDS when they fit.
 constexpr int kStageFloats = 12288;  // 48 KiB of LDS
 
-constexpr int kMaxBlocksPerWg = 16;
-#ifndef MSA_SCAN_BLOCKS_PER_WG
-#define MSA_SCAN_BLOCKS_PER_WG 16
-#endif
-constexpr int kScanBlocksPerWg = MSA_SCAN_BLOCKS_PER_WG;
-static_assert(kScanBlocksPerWg <= kMaxBlocksPerWg, "page list size");
+constexpr int kMaxBlocksPerWg = 8;  // blocks per scan workgroup (page list size)
 
 // One block's worth of this wave's loads: 8 tiles x 16 code bytes and the
 // 16-byte scale word (2 scale bytes per tile) per lane.
@@ -405,7 +401,7 @@ static msa_status launch_scan(const msa_pool_desc* idx, const uint8_t* idx_codes
   a.q_per_seq = q_per_seq;
   a.bscore = block_scores;
   const int qg = (MSA_HEADS_PER_KV * q_per_seq + 15) / 16;
-  int bpw = 8;
+  int bpw = kMaxBlocksPerWg;
   while (bpw > 1 && int64_t(num_seqs) * ((max_blocks + bpw - 1) / bpw) < 2048) bpw >>= 1;
   a.blocks_per_wg = bpw;
   const dim3 grid((max_blocks + bpw - 1) / bpw, num_seqs);
