@@ -204,6 +204,36 @@ msa_status msa_sparse_attn_decode(const msa_pool_desc* kv, const uint8_t* k_code
                                   float softmax_scale, float* out, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+/*
+ * Selection and sparse attention in one launch: the blocks of each query
+ * token are selected from block_scores (as written by msa_indexer_scan)
+ * inside the attention kernel, then attended as by msa_sparse_attn_decode.
+ * For the same block scores the result equals msa_indexer_select followed by
+ * msa_sparse_attn_decode with num_sel = topk + 1: the same ids and the same
+ * output bits. It saves the selection kernel's launch and the round trip of
+ * the ids through memory at low concurrency (the pages' mono-kernel for small
+ * batches: MiniMax-M3.1-Flash serving summary, section "AMD uses different
+ * conversion and communication mechanisms").
+ *   block_scores float [num_seqs * q_per_seq][max_blocks]; finite
+ *   topk         must be 16
+ *   out_ids      int32 [num_seqs * q_per_seq][topk + 1] or NULL: the
+ *                selected ids, as msa_indexer_select writes them
+ *   workspace    msa_attn_workspace_bytes(num_seqs, q_per_seq, num_q_heads,
+ *                topk + 1) bytes, no initial contents
+ * Other arguments and device-side checks as msa_sparse_attn_decode; a
+ * sequence with seq_lens < q_per_seq or seq_lens > max_blocks * 128 gets ids
+ * -1 and zero output.
+ */
+msa_status msa_sparse_attn_select_decode(const msa_pool_desc* kv, const uint8_t* k_codes,
+                                         const uint8_t* k_scales, const uint8_t* v_codes,
+                                         const uint8_t* v_scales, const uint8_t* q_fp8,
+                                         int32_t num_q_heads, const int32_t* block_table,
+                                         int32_t max_blocks, const int32_t* seq_lens,
+                                         int32_t num_seqs, int32_t q_per_seq,
+                                         const float* block_scores, int32_t topk,
+                                         int32_t* out_ids, float softmax_scale, float* out,
+                                         void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

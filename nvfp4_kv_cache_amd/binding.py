@@ -52,6 +52,9 @@ SIGNATURES = {
     "msa_attn_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
     "msa_sparse_attn_decode": (ctypes.c_int, [_DESC, _P, _P, _P, _P, _P, _I32, _P, _I32, _P,
                                               _I32, _I32, _P, _I32, _F32, _P, _P, _SZ, _P]),
+    "msa_sparse_attn_select_decode": (ctypes.c_int, [_DESC, _P, _P, _P, _P, _P, _I32, _P, _I32,
+                                                     _P, _I32, _I32, _P, _I32, _P, _F32, _P, _P,
+                                                     _SZ, _P]),
 }
 
 
@@ -248,9 +251,8 @@ def msa_indexer_select(block_scores, seq_lens, q_per_seq, out_ids, out_scores=No
            "msa_indexer_select")
 
 
-def msa_sparse_attn_decode(k_codes, k_scales, v_codes, v_scales, q_fp8, block_table, seq_lens,
-                           q_per_seq, sel_ids, softmax_scale, out, workspace):
-    """Attention over the selected blocks into out float32 [B*Q, Hq, 128]."""
+def _check_attn_inputs(k_codes, k_scales, v_codes, v_scales, q_fp8, block_table, seq_lens,
+                       q_per_seq, out, workspace):
     _check_pool(k_codes, k_scales, "k")
     _check_pool(v_codes, v_scales, "v")
     if k_codes.shape != v_codes.shape:
@@ -258,7 +260,6 @@ def msa_sparse_attn_decode(k_codes, k_scales, v_codes, v_scales, q_fp8, block_ta
     _need(q_fp8, "q_fp8", torch.uint8, 3)
     _need(block_table, "block_table", torch.int32, 2)
     _need(seq_lens, "seq_lens", torch.int32, 1)
-    _need(sel_ids, "sel_ids", torch.int32, 2)
     _need(out, "out", torch.float32, 3)
     _need(workspace, "workspace", torch.uint8, 1)
     num_seqs, max_blocks = block_table.shape
@@ -266,11 +267,46 @@ def msa_sparse_attn_decode(k_codes, k_scales, v_codes, v_scales, q_fp8, block_ta
     hq = q_fp8.shape[1]
     if q_fp8.shape != (tq, hq, HEAD_DIM) or out.shape != (tq, hq, HEAD_DIM):
         raise ValueError("q_fp8 and out must be [num_seqs*q_per_seq, Hq, 128]")
-    if sel_ids.shape[0] != tq or seq_lens.shape[0] != num_seqs:
-        raise ValueError("sel_ids must be [T_q, num_sel] and seq_lens [num_seqs]")
+    if seq_lens.shape[0] != num_seqs:
+        raise ValueError("seq_lens must be [num_seqs]")
+    return num_seqs, max_blocks, tq, hq
+
+
+def msa_sparse_attn_decode(k_codes, k_scales, v_codes, v_scales, q_fp8, block_table, seq_lens,
+                           q_per_seq, sel_ids, softmax_scale, out, workspace):
+    """Attention over the selected blocks into out float32 [B*Q, Hq, 128]."""
+    num_seqs, max_blocks, tq, hq = _check_attn_inputs(k_codes, k_scales, v_codes, v_scales, q_fp8,
+                                                      block_table, seq_lens, q_per_seq, out,
+                                                      workspace)
+    _need(sel_ids, "sel_ids", torch.int32, 2)
+    if sel_ids.shape[0] != tq:
+        raise ValueError("sel_ids must be [T_q, num_sel]")
     desc = pool_desc(k_codes)
     _check(lib().msa_sparse_attn_decode(
         ctypes.byref(desc), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales),
         _ptr(q_fp8), hq, _ptr(block_table), max_blocks, _ptr(seq_lens), num_seqs, q_per_seq,
         _ptr(sel_ids), sel_ids.shape[1], float(softmax_scale), _ptr(out), _ptr(workspace),
         workspace.numel(), _stream()), "msa_sparse_attn_decode")
+
+
+def msa_sparse_attn_select_decode(k_codes, k_scales, v_codes, v_scales, q_fp8, block_table,
+                                  seq_lens, q_per_seq, block_scores, softmax_scale, out, workspace,
+                                  out_ids=None, topk=TOPK):
+    """Selection from block scores [B*Q, max_blocks] and attention in one launch; the selected
+    ids go to out_ids int32 [B*Q, 17] when given."""
+    num_seqs, max_blocks, tq, hq = _check_attn_inputs(k_codes, k_scales, v_codes, v_scales, q_fp8,
+                                                      block_table, seq_lens, q_per_seq, out,
+                                                      workspace)
+    _need(block_scores, "block_scores", torch.float32, 2)
+    if block_scores.shape != (tq, max_blocks):
+        raise ValueError("block_scores must be [T_q, max_blocks]")
+    if out_ids is not None:
+        _need(out_ids, "out_ids", torch.int32, 2)
+        if out_ids.shape != (tq, topk + 1):
+            raise ValueError("out_ids must be [T_q, topk + 1]")
+    desc = pool_desc(k_codes)
+    _check(lib().msa_sparse_attn_select_decode(
+        ctypes.byref(desc), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales),
+        _ptr(q_fp8), hq, _ptr(block_table), max_blocks, _ptr(seq_lens), num_seqs, q_per_seq,
+        _ptr(block_scores), topk, _ptr(out_ids), float(softmax_scale), _ptr(out),
+        _ptr(workspace), workspace.numel(), _stream()), "msa_sparse_attn_select_decode")

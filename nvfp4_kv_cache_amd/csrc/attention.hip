@@ -29,6 +29,7 @@
 //      of one head (P) or one channel (V).
 #include "msa_nvfp4.h"
 #include "nvfp4_tile.h"
+#include "topk_select.h"
 
 namespace msa {
 
@@ -47,7 +48,9 @@ struct AttnArgs {
   int max_blocks;
   const int32_t* seq_lens;
   int q_per_seq;
-  const int32_t* sel_ids;
+  const int32_t* sel_ids;  // caller's selection [T_q][num_sel], or
+  const float* bscore;     // block scores [T_q][max_blocks] to select from
+  int32_t* out_ids;        // selection output [T_q][17] (optional, selecting kernel)
   int num_sel;
   int slots_per_wave;  // R
   int num_splits;
@@ -91,8 +94,12 @@ __device__ __forceinline__ v8i tr_operand(const uint8_t* p0, const uint8_t* p1, 
   return v8i{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
-template <int W>
+// SELECT: the kernel selects the blocks itself from the indexer's block
+// scores (every wavefront runs the same selection, so no barrier is needed);
+// otherwise the caller's ids are used.
+template <int W, bool SELECT>
 __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(const AttnArgs a) {
+  static_assert(W == 4, "the workgroup merge maps 256 threads onto 8 heads x 32 channel quads");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // W x (V rows, P) + zeros
   __shared__ uint2 lut[128];
 
@@ -108,19 +115,45 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(const AttnArgs a) {
   uint8_t* plows = prows + kPBytes;        // P_lo [token][head]
   const uint8_t* zeros = smem + W * kWaveLds;
 
-  for (int i = tid; i < 128; i += 64 * W) lut[i] = make_uint2(kAttnLut.lo[i], kAttnLut.hi[i]);
-  if (tid < 16) reinterpret_cast<uint32_t*>(smem + W * kWaveLds)[tid] = 0u;
-
+  // selection input in flight first: this query token's block scores, or
+  // the caller's ids (lane l: slot l)
+  float x0[kSelPerLane];
+  int sel = -1;
+  if constexpr (SELECT) {
+    load_score_chunk(a.bscore + int64_t(qt) * a.max_blocks, a.max_blocks, 0, lane, x0);
+  } else {
+    if (lane < a.num_sel) sel = a.sel_ids[int64_t(qt) * a.num_sel + lane];
+  }
   const int L = a.seq_lens[b];
   const bool seq_ok = L >= Q && L <= a.max_blocks * kBlockTokens;
   const int pos = L - Q + qi;
 
+  for (int i = tid; i < 128; i += 64 * W) lut[i] = make_uint2(kAttnLut.lo[i], kAttnLut.hi[i]);
+  if (tid < 16) reinterpret_cast<uint32_t*>(smem + W * kWaveLds)[tid] = 0u;
   // query operand: rows 0..7 = the 8 query heads of this KV head
   v8i qop = v8i{0, 0, 0, 0, 0, 0, 0, 0};
   if (li < kHeadsPerKv) {
     const uint4* qp = reinterpret_cast<const uint4*>(
         a.q + (int64_t(qt) * Hq + kh * kHeadsPerKv + li) * kHeadDim + slice * 32);
     qop = q_operand(qp[0], qp[1]);
+  }
+
+  // lane l: block of selected slot l and its physical page (-1: skip). Every
+  // wavefront runs the same selection (no barrier, scratch in its own LDS).
+  if constexpr (SELECT) {
+    if (seq_ok) {
+      float score;
+      sel = select_blocks(a.bscore + int64_t(qt) * a.max_blocks, a.max_blocks,
+                          pos / kBlockTokens + 1, x0, *reinterpret_cast<SelectScratch*>(vrows),
+                          lane, &score);
+    }
+    if (a.out_ids && sp == 0 && kh == 0 && wave == 0 && lane <= kTopK)
+      a.out_ids[int64_t(qt) * (kTopK + 1) + lane] = sel;
+  }
+  int pg = -1;
+  if (seq_ok && sel >= 0 && sel < a.max_blocks && sel * kBlockTokens <= pos) {
+    const int p = a.block_table[int64_t(b) * a.max_blocks + sel];
+    pg = (p >= 0 && p < a.num_pages) ? p : -1;
   }
   // online-softmax state of heads 4*slice + v (meaningful in lanes 0..31)
   const float ninf = -__builtin_huge_valf();
@@ -141,15 +174,11 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(const AttnArgs a) {
 
   const int s_begin = sp * W * a.slots_per_wave;
   const int s_end = min(a.num_sel, s_begin + W * a.slots_per_wave);
-  for (int si = s_begin + wave; si < s_end; si += W) {
-    const int blk = a.sel_ids[int64_t(qt) * a.num_sel + si];
-    bool ok = seq_ok && blk >= 0 && blk < a.max_blocks && blk * kBlockTokens <= pos;
-    int page = -1;
-    if (ok) {
-      page = a.block_table[int64_t(b) * a.max_blocks + blk];
-      ok = page >= 0 && page < a.num_pages;
-    }
-    if (!ok) continue;  // uniform over the wavefront
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  for (int si = s_begin + wave_u; si < s_end; si += W) {
+    const int page = __builtin_amdgcn_readlane(pg, si);
+    if (page < 0) continue;  // uniform over the wavefront
+    const int blk = __builtin_amdgcn_readlane(sel, si);
     const int ntok = min(kBlockTokens, pos + 1 - blk * kBlockTokens);
     const int64_t hc = int64_t(page) * page_codes + int64_t(kh) * kCodePage + lane_code;
     const int64_t hs = int64_t(page) * page_scales + int64_t(kh) * kScalePage + lane_scale;
@@ -275,31 +304,35 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(const AttnArgs a) {
     }
   }
   __syncthreads();
+  // thread: head h, channels 4 c .. 4 c + 3
   const int64_t row = int64_t(qt) * Hq + kh * kHeadsPerKv;
-  for (int e = tid; e < kHeadsPerKv * kHeadDim; e += 64 * W) {
-    const int h = e / kHeadDim, d = e - h * kHeadDim;
-    float M = ninf;
+  const int h = tid >> 5, d0 = (tid & 31) * 4;
+  float M = ninf;
 #pragma unroll
-    for (int w = 0; w < W; ++w) M = fmaxf(M, mml[(w * kHeadsPerKv + h) * 2]);
-    float num = 0.0f, den = 0.0f;
-    if (M != ninf) {
+  for (int w = 0; w < W; ++w) M = fmaxf(M, mml[(w * kHeadsPerKv + h) * 2]);
+  float4 num = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  float den = 0.0f;
+  if (M != ninf) {
 #pragma unroll
-      for (int w = 0; w < W; ++w) {
-        const float mw = mml[(w * kHeadsPerKv + h) * 2];
-        const float f = mw == ninf ? 0.0f : exp2f(mw - M);
-        den += f * mml[(w * kHeadsPerKv + h) * 2 + 1];
-        num += f * mo[(w * kHeadsPerKv + h) * kHeadDim + d];
-      }
+    for (int w = 0; w < W; ++w) {
+      const float mw = mml[(w * kHeadsPerKv + h) * 2];
+      const float f = mw == ninf ? 0.0f : exp2f(mw - M);
+      den += f * mml[(w * kHeadsPerKv + h) * 2 + 1];
+      const float4 ov = *reinterpret_cast<const float4*>(&mo[(w * kHeadsPerKv + h) * kHeadDim + d0]);
+      num.x += f * ov.x;
+      num.y += f * ov.y;
+      num.z += f * ov.z;
+      num.w += f * ov.w;
     }
-    if (a.num_splits == 1) {
-      a.out[(row + h) * kHeadDim + d] = den > 0.0f ? num / den : 0.0f;
-    } else {
-      a.part_o[((row + h) * a.num_splits + sp) * kHeadDim + d] = num;
-      if (d == 0) {
-        a.part_ml[((row + h) * a.num_splits + sp) * 2] = M;
-        a.part_ml[((row + h) * a.num_splits + sp) * 2 + 1] = den;
-      }
-    }
+  }
+  if (a.num_splits == 1) {
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+    *reinterpret_cast<float4*>(&a.out[(row + h) * kHeadDim + d0]) =
+        make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv);
+  } else {
+    *reinterpret_cast<float4*>(&a.part_o[((row + h) * a.num_splits + sp) * kHeadDim + d0]) = num;
+    if (d0 == 0)
+      *reinterpret_cast<float2*>(&a.part_ml[((row + h) * a.num_splits + sp) * 2]) = make_float2(M, den);
   }
 }
 
@@ -354,6 +387,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
 constexpr int kAttnWaves = 4;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+inline bool misaligned(const void* p, uintptr_t m) { return (reinterpret_cast<uintptr_t>(p) & m) != 0; }
 
 // Slots per wave R and split count: one block per wave while that keeps the
 // workgroup count under ~1024; otherwise more blocks per wave.
@@ -380,37 +414,71 @@ extern "C" size_t msa_attn_workspace_bytes(int32_t num_seqs, int32_t q_per_seq,
   return msa::align256(rows * splits * MSA_HEAD_DIM * 4) + msa::align256(rows * splits * 2 * 4);
 }
 
-extern "C" msa_status msa_sparse_attn_decode(const msa_pool_desc* kv, const uint8_t* k_codes,
-                                             const uint8_t* k_scales, const uint8_t* v_codes,
-                                             const uint8_t* v_scales, const uint8_t* q_fp8,
-                                             int32_t num_q_heads, const int32_t* block_table,
-                                             int32_t max_blocks, const int32_t* seq_lens,
-                                             int32_t num_seqs, int32_t q_per_seq,
-                                             const int32_t* sel_ids, int32_t num_sel,
-                                             float softmax_scale, float* out, void* workspace,
-                                             size_t workspace_bytes, void* stream) {
-  using namespace msa;
+namespace msa {
+
+// Host checks shared by both attention entry points.
+static msa_status check_attn(const msa_pool_desc* kv, const uint8_t* k_codes,
+                             const uint8_t* k_scales, const uint8_t* v_codes,
+                             const uint8_t* v_scales, const uint8_t* q_fp8, int32_t num_q_heads,
+                             const int32_t* block_table, int32_t max_blocks,
+                             const int32_t* seq_lens, int32_t num_seqs, int32_t q_per_seq,
+                             float softmax_scale, const float* out) {
   if (!kv || num_seqs < 0 || max_blocks <= 0 || q_per_seq <= 0) return MSA_ERR_INVALID_ARG;
   if (kv->head_dim != MSA_HEAD_DIM || kv->block_tokens != MSA_BLOCK_TOKENS)
     return MSA_ERR_UNSUPPORTED;
   if (kv->num_heads < 1 || kv->num_heads > MSA_MAX_HEADS) return MSA_ERR_UNSUPPORTED;
   if (num_q_heads != MSA_HEADS_PER_KV * kv->num_heads) return MSA_ERR_UNSUPPORTED;
-  if (q_per_seq > MSA_MAX_Q_PER_SEQ || num_sel < 1 || num_sel > 64) return MSA_ERR_UNSUPPORTED;
+  if (q_per_seq > MSA_MAX_Q_PER_SEQ) return MSA_ERR_UNSUPPORTED;
   if (kv->num_pages <= 0 || kv->num_pages > 0x7FFFFFFF) return MSA_ERR_INVALID_ARG;
   if (int64_t(max_blocks) * MSA_BLOCK_TOKENS > 0x7FFFFFFF) return MSA_ERR_UNSUPPORTED;
   if (!(softmax_scale > 0.0f) || softmax_scale > 1e30f) return MSA_ERR_INVALID_ARG;
   if (num_seqs == 0) return MSA_OK;
   if (int64_t(num_seqs) * q_per_seq > 65535) return MSA_ERR_UNSUPPORTED;
-  if (!k_codes || !k_scales || !v_codes || !v_scales || !q_fp8 || !block_table || !seq_lens ||
-      !sel_ids || !out)
+  if (!k_codes || !k_scales || !v_codes || !v_scales || !q_fp8 || !block_table || !seq_lens || !out)
     return MSA_ERR_INVALID_ARG;
-  auto mis = [](const void* p, uintptr_t m) { return (reinterpret_cast<uintptr_t>(p) & m) != 0; };
-  if (mis(k_codes, 15) || mis(k_scales, 15) || mis(v_codes, 15) || mis(v_scales, 15) ||
-      mis(q_fp8, 15) || mis(block_table, 3) || mis(seq_lens, 3) || mis(sel_ids, 3) || mis(out, 15))
+  if (misaligned(k_codes, 15) || misaligned(k_scales, 15) || misaligned(v_codes, 15) ||
+      misaligned(v_scales, 15) || misaligned(q_fp8, 15) || misaligned(block_table, 3) ||
+      misaligned(seq_lens, 3) || misaligned(out, 15))
     return MSA_ERR_INVALID_ARG;
+  return MSA_OK;
+}
 
+// Plan, workspace carving and launches (attention, then the split merge).
+template <bool SELECT>
+static msa_status run_attn(AttnArgs a, const msa_pool_desc* kv, int32_t num_seqs,
+                           int32_t q_per_seq, int32_t num_q_heads, void* workspace,
+                           size_t workspace_bytes, hipStream_t s) {
   const int64_t tq = int64_t(num_seqs) * q_per_seq;
-  AttnArgs a;
+  attn_plan(tq * kv->num_heads, a.num_sel, &a.slots_per_wave, &a.num_splits);
+  if (a.num_splits > 1) {
+    const size_t need = msa_attn_workspace_bytes(num_seqs, q_per_seq, num_q_heads, a.num_sel);
+    if (!workspace || workspace_bytes < need || misaligned(workspace, 255)) return MSA_ERR_WORKSPACE;
+    const size_t rows = size_t(tq) * num_q_heads;
+    char* ws = static_cast<char*>(workspace);
+    a.part_o = reinterpret_cast<float*>(ws);
+    a.part_ml = reinterpret_cast<float*>(ws + align256(rows * a.num_splits * MSA_HEAD_DIM * 4));
+  } else {
+    a.part_o = nullptr;
+    a.part_ml = nullptr;
+  }
+  const dim3 grid(a.num_splits, kv->num_heads, unsigned(tq));
+  hipLaunchKernelGGL((sparse_attn_kernel<kAttnWaves, SELECT>), grid, dim3(64 * kAttnWaves),
+                     attn_lds_bytes<kAttnWaves>(), s, a);
+  if (hipGetLastError() != hipSuccess) return MSA_ERR_HIP;
+  if (a.num_splits > 1) {
+    hipLaunchKernelGGL(merge_kernel, dim3(unsigned(tq * kv->num_heads)), dim3(256), 0, s,
+                       a.part_o, a.part_ml, a.num_splits, a.out);
+    if (hipGetLastError() != hipSuccess) return MSA_ERR_HIP;
+  }
+  return MSA_OK;
+}
+
+static AttnArgs base_args(const msa_pool_desc* kv, const uint8_t* k_codes, const uint8_t* k_scales,
+                          const uint8_t* v_codes, const uint8_t* v_scales, const uint8_t* q_fp8,
+                          int32_t num_q_heads, const int32_t* block_table, int32_t max_blocks,
+                          const int32_t* seq_lens, int32_t q_per_seq, float softmax_scale,
+                          float* out) {
+  AttnArgs a{};
   a.k_codes = k_codes;
   a.k_scales = k_scales;
   a.v_codes = v_codes;
@@ -423,31 +491,58 @@ extern "C" msa_status msa_sparse_attn_decode(const msa_pool_desc* kv, const uint
   a.max_blocks = max_blocks;
   a.seq_lens = seq_lens;
   a.q_per_seq = q_per_seq;
-  a.sel_ids = sel_ids;
-  a.num_sel = num_sel;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.out = out;
-  attn_plan(tq * kv->num_heads, num_sel, &a.slots_per_wave, &a.num_splits);
-  if (a.num_splits > 1) {
-    const size_t need = msa_attn_workspace_bytes(num_seqs, q_per_seq, num_q_heads, num_sel);
-    if (!workspace || workspace_bytes < need || mis(workspace, 255)) return MSA_ERR_WORKSPACE;
-    const size_t rows = size_t(tq) * num_q_heads;
-    char* ws = static_cast<char*>(workspace);
-    a.part_o = reinterpret_cast<float*>(ws);
-    a.part_ml = reinterpret_cast<float*>(ws + align256(rows * a.num_splits * MSA_HEAD_DIM * 4));
-  } else {
-    a.part_o = nullptr;
-    a.part_ml = nullptr;
-  }
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid(a.num_splits, kv->num_heads, unsigned(tq));
-  hipLaunchKernelGGL(sparse_attn_kernel<kAttnWaves>, grid, dim3(64 * kAttnWaves),
-                     attn_lds_bytes<kAttnWaves>(), s, a);
-  if (hipGetLastError() != hipSuccess) return MSA_ERR_HIP;
-  if (a.num_splits > 1) {
-    hipLaunchKernelGGL(merge_kernel, dim3(unsigned(tq * kv->num_heads)), dim3(256), 0, s,
-                       a.part_o, a.part_ml, a.num_splits, out);
-    if (hipGetLastError() != hipSuccess) return MSA_ERR_HIP;
-  }
-  return MSA_OK;
+  return a;
+}
+
+}  // namespace msa
+
+extern "C" msa_status msa_sparse_attn_decode(const msa_pool_desc* kv, const uint8_t* k_codes,
+                                             const uint8_t* k_scales, const uint8_t* v_codes,
+                                             const uint8_t* v_scales, const uint8_t* q_fp8,
+                                             int32_t num_q_heads, const int32_t* block_table,
+                                             int32_t max_blocks, const int32_t* seq_lens,
+                                             int32_t num_seqs, int32_t q_per_seq,
+                                             const int32_t* sel_ids, int32_t num_sel,
+                                             float softmax_scale, float* out, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
+  using namespace msa;
+  msa_status st = check_attn(kv, k_codes, k_scales, v_codes, v_scales, q_fp8, num_q_heads,
+                             block_table, max_blocks, seq_lens, num_seqs, q_per_seq, softmax_scale,
+                             out);
+  if (st != MSA_OK) return st;
+  if (num_sel < 1 || num_sel > 64) return MSA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return MSA_OK;
+  if (!sel_ids || misaligned(sel_ids, 3)) return MSA_ERR_INVALID_ARG;
+  AttnArgs a = base_args(kv, k_codes, k_scales, v_codes, v_scales, q_fp8, num_q_heads, block_table,
+                         max_blocks, seq_lens, q_per_seq, softmax_scale, out);
+  a.sel_ids = sel_ids;
+  a.num_sel = num_sel;
+  return run_attn<false>(a, kv, num_seqs, q_per_seq, num_q_heads, workspace, workspace_bytes,
+                         static_cast<hipStream_t>(stream));
+}
+
+extern "C" msa_status msa_sparse_attn_select_decode(
+    const msa_pool_desc* kv, const uint8_t* k_codes, const uint8_t* k_scales,
+    const uint8_t* v_codes, const uint8_t* v_scales, const uint8_t* q_fp8, int32_t num_q_heads,
+    const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens, int32_t num_seqs,
+    int32_t q_per_seq, const float* block_scores, int32_t topk, int32_t* out_ids,
+    float softmax_scale, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  using namespace msa;
+  msa_status st = check_attn(kv, k_codes, k_scales, v_codes, v_scales, q_fp8, num_q_heads,
+                             block_table, max_blocks, seq_lens, num_seqs, q_per_seq, softmax_scale,
+                             out);
+  if (st != MSA_OK) return st;
+  if (topk != MSA_TOPK) return MSA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return MSA_OK;
+  if (!block_scores || misaligned(block_scores, 3) || misaligned(out_ids, 3))
+    return MSA_ERR_INVALID_ARG;
+  AttnArgs a = base_args(kv, k_codes, k_scales, v_codes, v_scales, q_fp8, num_q_heads, block_table,
+                         max_blocks, seq_lens, q_per_seq, softmax_scale, out);
+  a.bscore = block_scores;
+  a.out_ids = out_ids;
+  a.num_sel = MSA_TOPK + 1;
+  return run_attn<true>(a, kv, num_seqs, q_per_seq, num_q_heads, workspace, workspace_bytes,
+                        static_cast<hipStream_t>(stream));
 }

@@ -24,8 +24,11 @@
 // token, the top-16 blocks plus the most recent one.
 #include "msa_nvfp4.h"
 #include "nvfp4_tile.h"
+#include "topk_select.h"
 
 namespace msa {
+
+static_assert(kTopK == MSA_TOPK, "selection size");
 
 __constant__ Fp8Lut kIdxLut = make_fp8_lut();
 
@@ -44,18 +47,6 @@ struct IndexerArgs {
   int blocks_per_wg;
   float* bscore;       // [num_seqs * q_per_seq][max_blocks]
 };
-
-__device__ __forceinline__ float canon_score(float s) { return s > 0.0f ? s : 0.0f; }
-
-// Unique ordering key: larger score first, then lower block index.
-__device__ __forceinline__ uint64_t score_key(float s, int j) {
-  return (uint64_t(__float_as_uint(canon_score(s))) << 32) | uint32_t(0xFFFFFFFFu - uint32_t(j));
-}
-__device__ __forceinline__ int key_block(uint64_t k) { return int(0xFFFFFFFFu - uint32_t(k)); }
-__device__ __forceinline__ float key_score(uint64_t k) { return __uint_as_float(uint32_t(k >> 32)); }
-
-// Block scores of all query tokens of a sequence staged in LDS when they fit.
-constexpr int kStageFloats = 12288;  // 48 KiB of LDS
 
 constexpr int kMaxBlocksPerWg = 8;  // blocks per scan workgroup (page list size)
 
@@ -83,7 +74,11 @@ __device__ __forceinline__ void issue_loads(TileLoads& t, const uint8_t* codes_h
 }
 
 // QG: 16-row MFMA groups per index head = ceil(8 * q_per_seq / 16).
-template <int QG>
+// STAGES: blocks in flight per wave. With QG = 1 the kernel is bound by HBM
+// and more resident waves hide the latency better than a second register
+// buffer (measured ~3% faster); with QG >= 2 the MFMA epilogue is long
+// enough that the next block's loads must overlap it.
+template <int QG, int STAGES>
 __global__ __launch_bounds__(512) void indexer_kernel(const IndexerArgs a) {
   extern __shared__ float part[];  // [2][H][2*QG][2][128] partial token scores per head group half
   __shared__ uint2 lut[128];
@@ -185,6 +180,16 @@ __global__ __launch_bounds__(512) void indexer_kernel(const IndexerArgs a) {
     }
   };
 
+  if constexpr (STAGES == 1) {
+    for (int k = 0; k < count; ++k) {
+      TileLoads t;
+      issue_loads(t, codes_h, scales_h, pages[k], page_codes, page_scales);
+      compute(t, k & 1);
+      __syncthreads();
+      reduce(k, k & 1);
+    }
+    return;
+  }
   // two-stage pipeline: the next block's loads are in flight while the
   // current block is computed
   TileLoads ta, tb;
@@ -202,166 +207,36 @@ __global__ __launch_bounds__(512) void indexer_kernel(const IndexerArgs a) {
   }
 }
 
-// Selection kernel: one 256-thread workgroup per query token. The block
-// scores are staged in LDS with independent loads. theta = the 16th best of
-// the 256 threads' maxima (each wave contributes its 16 best, wave 0 ranks
-// those 64), so at least 16 keys lie at or above theta and the survivors
-// (keys >= theta) contain the top-16; wave 0 ranks the survivors exactly.
-// Ranks are counted against values broadcast with lane reads, not LDS. More
-// than 64 survivors (many near-equal scores) fall back to 16 rounds of
-// arg-max in wave 0.
-constexpr int kSelThreads = 256;
-constexpr int kSelPerThread = 8;
-constexpr int kSelChunk = kSelThreads * kSelPerThread;
-
-// number of lanes whose key is larger than this lane's key
-__device__ __forceinline__ int lane_rank(uint64_t key) {
-  int r = 0;
-#pragma unroll
-  for (int src = 0; src < 64; ++src) r += readlane_u64(key, src) > key ? 1 : 0;
-  return r;
-}
-
-__global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __restrict__ bscore,
-                                                             const int32_t* __restrict__ seq_lens,
-                                                             int max_blocks, int q_per_seq,
-                                                             int32_t* __restrict__ out_ids,
-                                                             float* __restrict__ out_scores) {
-  extern __shared__ float stage[];
-  __shared__ uint64_t s_keys[64];
-  __shared__ uint64_t s_sel[MSA_TOPK];
-  __shared__ uint64_t s_top[kSelThreads / 64 * MSA_TOPK];
-  __shared__ uint64_t s_theta;
-  __shared__ int s_count[kSelThreads / 64];
-  __shared__ int s_fill;
-  constexpr int K = MSA_TOPK;
+// Selection kernel: one wavefront per query token (topk_select.h).
+__global__ __launch_bounds__(64) void select_kernel(const float* __restrict__ bscore,
+                                                    const int32_t* __restrict__ seq_lens,
+                                                    int max_blocks, int q_per_seq,
+                                                    int32_t* __restrict__ out_ids,
+                                                    float* __restrict__ out_scores) {
+  __shared__ SelectScratch scratch;
   const int row = blockIdx.x;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lane = threadIdx.x;
+  const float* src = bscore + int64_t(row) * max_blocks;
+  float x0[kSelPerLane];
+  load_score_chunk(src, max_blocks, 0, lane, x0);  // in flight while the length is read
   const int Q = q_per_seq;
   const int b = row / Q, qi = row - b * Q;
   const int L = seq_lens[b];
-  int32_t* ids = out_ids + int64_t(row) * (K + 1);
-  float* sc = out_scores ? out_scores + int64_t(row) * (K + 1) : nullptr;
+  int32_t* ids = out_ids + int64_t(row) * (kTopK + 1);
+  float* sc = out_scores ? out_scores + int64_t(row) * (kTopK + 1) : nullptr;
   if (L < Q || L > max_blocks * kBlockTokens) {
-    if (tid < K + 1) {
-      ids[tid] = -1;
-      if (sc) sc[tid] = 0.0f;
+    if (lane <= kTopK) {
+      ids[lane] = -1;
+      if (sc) sc[lane] = 0.0f;
     }
     return;
   }
   const int nb = (L - Q + qi) / kBlockTokens + 1;
-  const float* src = bscore + int64_t(row) * max_blocks;
-  if (nb <= K + 1) {
-    if (tid < K + 1) {
-      ids[tid] = tid < nb ? tid : -1;
-      if (sc) sc[tid] = tid < nb ? canon_score(src[tid]) : 0.0f;
-    }
-    return;
-  }
-  const bool staged = nb <= kStageFloats;
-  if (staged) {
-    for (int j0 = 0; j0 < nb; j0 += kSelChunk) {
-      float t[kSelPerThread];
-#pragma unroll
-      for (int k = 0; k < kSelPerThread; ++k) {
-        const int j = j0 + tid + kSelThreads * k;
-        t[k] = j < nb ? src[j] : 0.0f;
-      }
-#pragma unroll
-      for (int k = 0; k < kSelPerThread; ++k) {
-        const int j = j0 + tid + kSelThreads * k;
-        if (j < nb) stage[j] = t[k];
-      }
-    }
-  }
-  if (tid < kSelThreads / 64 * K) s_top[tid] = 0ull;
-  if (tid == 0) s_fill = 0;
-  __syncthreads();
-  const int n = nb - 1;  // candidates; the recent block is always kept
-  auto score_at = [&](int j) { return staged ? stage[j] : src[j]; };
-  // 1. thread maxima; each wave's 16 best; theta over the 64
-  uint64_t best = 0;
-  for (int j0 = 0; j0 < n; j0 += kSelChunk) {
-#pragma unroll
-    for (int k = 0; k < kSelPerThread; ++k) {
-      const int j = j0 + tid + kSelThreads * k;
-      if (j < n) {
-        const uint64_t key = score_key(score_at(j), j);
-        best = key > best ? key : best;
-      }
-    }
-  }
-  const int wr = lane_rank(best);
-  if (wr < K && best != 0ull) s_top[wave * K + wr] = best;
-  __syncthreads();
-  if (wave == 0) {
-    const uint64_t mk = s_top[lane];
-    const int r = lane_rank(mk);
-    const uint64_t m15 = __ballot(r == K - 1 && mk != 0ull);
-    if (lane == 0) s_theta = m15 ? s_top[__builtin_ctzll(m15)] : 0ull;
-  }
-  __syncthreads();
-  const uint64_t theta = s_theta;
-  // 2. survivors (keys >= theta)
-  int cnt = 0;
-  for (int j0 = 0; j0 < n; j0 += kSelChunk) {
-#pragma unroll
-    for (int k = 0; k < kSelPerThread; ++k) {
-      const int j = j0 + tid + kSelThreads * k;
-      if (j < n) cnt += score_key(score_at(j), j) >= theta ? 1 : 0;
-    }
-  }
-  cnt = wave_sum_int(cnt);
-  if (lane == 0) s_count[wave] = cnt;
-  __syncthreads();
-  int survivors = 0;
-#pragma unroll
-  for (int w = 0; w < kSelThreads / 64; ++w) survivors += s_count[w];
-  uint64_t mine = 0;  // wave 0: lanes 0..15 end with the selected keys
-  if (survivors <= 64) {
-    for (int j0 = 0; j0 < n; j0 += kSelChunk) {
-#pragma unroll
-      for (int k = 0; k < kSelPerThread; ++k) {
-        const int j = j0 + tid + kSelThreads * k;
-        if (j < n) {
-          const uint64_t key = score_key(score_at(j), j);
-          if (key >= theta) s_keys[atomicAdd(&s_fill, 1)] = key;
-        }
-      }
-    }
-    __syncthreads();
-    if (wave != 0) return;
-    const uint64_t cand = lane < survivors ? s_keys[lane] : 0ull;
-    const int r = lane_rank(cand);
-    if (lane < survivors && r < K) s_sel[r] = cand;
-    wave_lds_sync();
-    mine = lane < K ? s_sel[lane] : 0ull;
-  } else {
-    if (wave != 0) return;
-    uint64_t last = ~0ull;
-    for (int r = 0; r < K; ++r) {
-      uint64_t bb = 0;
-      for (int j = lane; j < n; j += 64) {
-        const uint64_t key = score_key(score_at(j), j);
-        if (key < last && key > bb) bb = key;
-      }
-      bb = wave_max_u64(bb);
-      if (lane == r) mine = bb;
-      last = bb;
-    }
-  }
-  // 3. ascending block order
-  const int myblk = key_block(mine);
-  int order = 0;
-#pragma unroll
-  for (int i = 0; i < K; ++i) order += key_block(readlane_u64(mine, i)) < myblk ? 1 : 0;
-  if (lane < K) {
-    ids[order] = myblk;
-    if (sc) sc[order] = key_score(mine);
-  }
-  if (lane == 0) {
-    ids[K] = nb - 1;
-    if (sc) sc[K] = canon_score(score_at(nb - 1));
+  float score;
+  const int id = select_blocks(src, max_blocks, nb, x0, scratch, lane, &score);
+  if (lane <= kTopK) {
+    ids[lane] = id;
+    if (sc) sc[lane] = score;
   }
 }
 
@@ -401,29 +276,30 @@ static msa_status launch_scan(const msa_pool_desc* idx, const uint8_t* idx_codes
   a.q_per_seq = q_per_seq;
   a.bscore = block_scores;
   const int qg = (MSA_HEADS_PER_KV * q_per_seq + 15) / 16;
-  int bpw = kMaxBlocksPerWg;
-  while (bpw > 1 && int64_t(num_seqs) * ((max_blocks + bpw - 1) / bpw) < 2048) bpw >>= 1;
+  // blocks per workgroup: 4 (one stage) or 8 (two stages), halved while the
+  // grid would not cover the chip several times over
+  int bpw = qg == 1 ? 4 : 8;
+  const int64_t min_wgs = qg == 1 ? 4096 : 2048;
+  while (bpw > 1 && int64_t(num_seqs) * ((max_blocks + bpw - 1) / bpw) < min_wgs) bpw >>= 1;
   a.blocks_per_wg = bpw;
   const dim3 grid((max_blocks + bpw - 1) / bpw, num_seqs);
   const dim3 block(64 * idx->num_heads);
   const int qg_pow2 = qg == 1 ? 1 : (qg == 2 ? 2 : 4);
   const size_t lds = size_t(2) * idx->num_heads * (2 * qg_pow2) * 2 * MSA_BLOCK_TOKENS * sizeof(float);
   if (qg_pow2 == 1)
-    hipLaunchKernelGGL(indexer_kernel<1>, grid, block, lds, s, a);
+    hipLaunchKernelGGL((indexer_kernel<1, 1>), grid, block, lds, s, a);
   else if (qg_pow2 == 2)
-    hipLaunchKernelGGL(indexer_kernel<2>, grid, block, lds, s, a);
+    hipLaunchKernelGGL((indexer_kernel<2, 2>), grid, block, lds, s, a);
   else
-    hipLaunchKernelGGL(indexer_kernel<4>, grid, block, lds, s, a);
+    hipLaunchKernelGGL((indexer_kernel<4, 2>), grid, block, lds, s, a);
   return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
 }
 
 static msa_status launch_select(const float* block_scores, const int32_t* seq_lens,
                                 int32_t max_blocks, int32_t num_seqs, int32_t q_per_seq,
                                 int32_t* out_ids, float* out_scores, hipStream_t s) {
-  const int stage = max_blocks < kStageFloats ? max_blocks : kStageFloats;
-  hipLaunchKernelGGL(select_kernel, dim3(unsigned(int64_t(num_seqs) * q_per_seq)),
-                     dim3(kSelThreads), size_t(stage) * sizeof(float), s, block_scores, seq_lens,
-                     max_blocks, q_per_seq, out_ids, out_scores);
+  hipLaunchKernelGGL(select_kernel, dim3(unsigned(int64_t(num_seqs) * q_per_seq)), dim3(64), 0, s,
+                     block_scores, seq_lens, max_blocks, q_per_seq, out_ids, out_scores);
   return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
 }
 

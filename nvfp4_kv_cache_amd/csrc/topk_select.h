@@ -1,0 +1,184 @@
+// topk_select.h -- block selection of one query token by one wavefront:
+// the 16 best blocks among 0..nb-2 by (score descending, block ascending),
+// plus the most recent block nb-1, in ascending block order (MiniMax-M3.1-Flash
+// serving summary, section "Sparse attention still scans an index": top-16
+// blocks plus the recent block, about 2,048 keys).
+//
+// No sort and no workgroup barrier. A block's key is (score bits << 32 |
+// ~block): scores are non-negative, so their fp32 bit patterns order like
+// the values, and the low word makes every key distinct and breaks ties
+// toward the lower block. Steps:
+//   1. lane l holds the scores of blocks l, l+64, ..., l+64*31 of a chunk of
+//      2,048 (one chunk in registers; longer contexts loop over chunks) and
+//      their maximum;
+//   2. theta = the 16th largest of the 64 lane maxima, built bit by bit from
+//      the top with ballot counts: the 16 lanes holding the largest maxima
+//      each own a block scoring >= theta, so at least 16 candidates reach
+//      theta and the top-16 are among them;
+//   3. the candidates >= theta (typically 16..25) are compacted into LDS at
+//      offsets from a DPP prefix sum of per-lane counts and ranked exactly by
+//      counting; with more than 64 of them (many equal scores) 16 rounds of
+//      wavefront arg-max take over;
+//   4. the 16 winners are put in ascending block order, the recent block last.
+#pragma once
+
+#include "nvfp4_tile.h"
+
+namespace msa {
+
+constexpr int kTopK = 16;
+constexpr int kSelPerLane = 32;               // scores per lane per chunk
+constexpr int kSelChunk = 64 * kSelPerLane;   // 2,048 candidates per chunk
+
+struct SelectScratch {
+  uint64_t cand[64];  // compacted candidates (keys)
+  uint64_t win[kTopK];
+  int32_t id[kTopK];
+  float score[kTopK];
+};
+
+__device__ __forceinline__ uint32_t score_bits(float s) { return __float_as_uint(s > 0.0f ? s : 0.0f); }
+__device__ __forceinline__ uint64_t make_key(uint32_t bits, int j) {
+  return (uint64_t(bits) << 32) | uint32_t(0xFFFFFFFFu - uint32_t(j));
+}
+__device__ __forceinline__ int key_block_id(uint64_t k) { return int(0xFFFFFFFFu - uint32_t(k)); }
+__device__ __forceinline__ float key_score_value(uint64_t k) { return __uint_as_float(uint32_t(k >> 32)); }
+
+// One chunk of a query token's block scores: lane l gets entries
+// c0 + l + 64 k. Loads are clamped to the row (row_len > 0 entries) instead
+// of predicated, so all of them are in flight at once; entries past the
+// candidates are masked by index later.
+__device__ __forceinline__ void load_score_chunk(const float* row, int row_len, int c0, int lane,
+                                                 float (&x)[kSelPerLane]) {
+#pragma unroll
+  for (int k = 0; k < kSelPerLane; ++k) x[k] = row[min(c0 + lane + 64 * k, row_len - 1)];
+}
+
+// Inclusive prefix sum over the wavefront: DPP row shifts inside rows of 16
+// lanes (out-of-row lanes read 0), then the totals of the preceding rows.
+__device__ __forceinline__ int wave_inclusive_sum(int v, int lane) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = lane >> 4;
+  return v + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+}
+
+// Selection for one query token with nb visible blocks whose scores are
+// row[0 .. nb-1] (row_len >= nb readable entries); x0 holds chunk 0 as
+// load_score_chunk(row, row_len, 0, lane, x0) returns it. Every lane of the
+// wavefront must call it. Lane l < 17 receives the l-th selected block
+// (ascending; the recent block last when nb > 17) and its score; other lanes,
+// and lanes past nb when nb <= 17, receive -1 and 0.
+__device__ __forceinline__ int select_blocks(const float* row, int row_len, int nb,
+                                             const float (&x0)[kSelPerLane], SelectScratch& sc,
+                                             int lane, float* score_out) {
+  if (nb <= kTopK + 1) {
+    const bool in = lane < nb;
+    *score_out = in ? __uint_as_float(score_bits(row[min(lane, row_len - 1)])) : 0.0f;
+    return in ? lane : -1;
+  }
+  const int n = nb - 1;  // candidates; the recent block is always kept
+  const int nchunks = (n + kSelChunk - 1) / kSelChunk;
+  uint32_t v[kSelPerLane];
+  auto chunk_bits = [&](int c) {
+    const int c0 = c * kSelChunk;
+    float x[kSelPerLane];
+    if (c == 0) {
+#pragma unroll
+      for (int k = 0; k < kSelPerLane; ++k) x[k] = x0[k];
+    } else {
+      load_score_chunk(row, row_len, c0, lane, x);
+    }
+#pragma unroll
+    for (int k = 0; k < kSelPerLane; ++k) v[k] = c0 + lane + 64 * k < n ? score_bits(x[k]) : 0u;
+  };
+  // 1. lane maxima
+  uint32_t m = 0;
+  for (int c = 0; c < nchunks; ++c) {
+    chunk_bits(c);
+#pragma unroll
+    for (int k = 0; k < kSelPerLane; ++k) m = max(m, v[k]);
+  }
+  // 2. theta: the largest t with at least 16 lane maxima >= t
+  uint32_t theta = 0;
+#pragma unroll
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t t = theta | (1u << bit);
+    if (__popcll(__ballot(m >= t)) >= kTopK) theta = t;
+  }
+  // 3. compact the candidates reaching theta
+  int cnt = 0;  // uniform
+  for (int c = 0; c < nchunks; ++c) {
+    if (nchunks > 1) chunk_bits(c);
+    const int c0 = c * kSelChunk;
+    int mine = 0;
+#pragma unroll
+    for (int k = 0; k < kSelPerLane; ++k) mine += (c0 + lane + 64 * k < n && v[k] >= theta) ? 1 : 0;
+    const int incl = wave_inclusive_sum(mine, lane);
+    int pos = cnt + incl - mine;
+#pragma unroll
+    for (int k = 0; k < kSelPerLane; ++k) {
+      const int j = c0 + lane + 64 * k;
+      if (j < n && v[k] >= theta) {
+        if (pos < 64) sc.cand[pos] = make_key(v[k], j);
+        ++pos;
+      }
+    }
+    cnt += __builtin_amdgcn_readlane(incl, 63);
+  }
+  wave_lds_sync();
+  if (cnt <= 64) {
+    const uint64_t key = lane < cnt ? sc.cand[lane] : 0ull;
+    int r = 0;
+    for (int s = 0; s < cnt; ++s) r += readlane_u64(key, s) > key ? 1 : 0;
+    if (lane < cnt && r < kTopK) sc.win[r] = key;
+  } else {
+    // many candidates reach theta (equal scores): exact arg-max rounds
+    uint64_t last = ~0ull;
+#pragma unroll 1
+    for (int r = 0; r < kTopK; ++r) {
+      uint64_t best = 0;
+      for (int c = 0; c < nchunks; ++c) {
+        if (nchunks > 1) chunk_bits(c);
+        const int c0 = c * kSelChunk;
+#pragma unroll
+        for (int k = 0; k < kSelPerLane; ++k) {
+          const int j = c0 + lane + 64 * k;
+          const uint64_t key = make_key(v[k], j);
+          if (j < n && key < last && key > best) best = key;
+        }
+      }
+      best = wave_max_u64(best);
+      if (lane == 0) sc.win[r] = best;
+      last = best;
+    }
+  }
+  wave_lds_sync();
+  // 4. ascending block order
+  const uint64_t wk = lane < kTopK ? sc.win[lane] : 0ull;
+  const int wid = key_block_id(wk);
+  int order = 0;
+#pragma unroll
+  for (int i = 0; i < kTopK; ++i) order += key_block_id(readlane_u64(wk, i)) < wid ? 1 : 0;
+  if (lane < kTopK) {
+    sc.id[order] = wid;
+    sc.score[order] = key_score_value(wk);
+  }
+  wave_lds_sync();
+  if (lane < kTopK) {
+    *score_out = sc.score[lane];
+    return sc.id[lane];
+  }
+  if (lane == kTopK) {
+    *score_out = __uint_as_float(score_bits(row[nb - 1]));
+    return nb - 1;
+  }
+  *score_out = 0.0f;
+  return -1;
+}
+
+}  // namespace msa

@@ -23,8 +23,14 @@ from msa_workloads import synth  # noqa: E402
 from msa_workloads.device import STREAMS, device_inputs, fill_pools, page_rows  # noqa: E402,F401
 
 
-def run_step(nb, wl, pools, inp, ws_idx=None, ws_attn=None, out=None):
-    """One decode step on the GPU: indexer then sparse attention."""
+def run_step(nb, wl, pools, inp, ws_idx=None, ws_attn=None, out=None, fused=True):
+    """One decode step on the GPU.
+
+    fused=True is the launch sequence bench.py times: msa_indexer_scan, then
+    msa_sparse_attn_select_decode (selection inside the attention launch);
+    msa_indexer_select on the same block scores then supplies the selected
+    blocks' scores and must reproduce the ids. fused=False runs
+    msa_indexer_decode, then msa_sparse_attn_decode on its ids."""
     dev = inp["q_idx"].device
     tq = wl.num_q_tokens
     if ws_idx is None:
@@ -39,11 +45,23 @@ def run_step(nb, wl, pools, inp, ws_idx=None, ws_attn=None, out=None):
     ic, isc = pools[synth.STREAM_IDX]
     kc, ks = pools[synth.STREAM_K]
     vc, vs = pools[synth.STREAM_V]
+    scale = 1.0 / math.sqrt(128)
+    if fused:
+        bscores = ws_idx[: tq * wl.max_blocks * 4].view(torch.float32).view(tq, wl.max_blocks)
+        nb.msa_indexer_scan(ic, isc, inp["q_idx"], inp["w"], inp["block_table"], inp["seq_lens"],
+                            wl.q_per_seq, bscores)
+        nb.msa_sparse_attn_select_decode(kc, ks, vc, vs, inp["q_attn"], inp["block_table"],
+                                         inp["seq_lens"], wl.q_per_seq, bscores, scale, out["o"],
+                                         ws_attn, out_ids=out["ids"])
+        ids2 = torch.empty_like(out["ids"])
+        nb.msa_indexer_select(bscores, inp["seq_lens"], wl.q_per_seq, ids2, out["scores"])
+        torch.cuda.synchronize()
+        assert torch.equal(ids2, out["ids"]), "selection inside attention differs from select"
+        return out
     nb.msa_indexer_decode(ic, isc, inp["q_idx"], inp["w"], inp["block_table"], inp["seq_lens"],
                           wl.q_per_seq, out["ids"], ws_idx, out_scores=out["scores"])
     nb.msa_sparse_attn_decode(kc, ks, vc, vs, inp["q_attn"], inp["block_table"],
-                              inp["seq_lens"], wl.q_per_seq, out["ids"], 1.0 / math.sqrt(128),
-                              out["o"], ws_attn)
+                              inp["seq_lens"], wl.q_per_seq, out["ids"], scale, out["o"], ws_attn)
     return out
 
 

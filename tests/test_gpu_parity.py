@@ -120,13 +120,14 @@ TINY = [
 ]
 
 
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "separate"])
 @pytest.mark.parametrize("lens,q", TINY)
-def test_tiny_parity(nb, lens, q):
-    say(f"tiny parity lens={lens} q={q}")
+def test_tiny_parity(nb, lens, q, fused):
+    say(f"tiny parity lens={lens} q={q} fused={fused}")
     wl = tiny_config(lens, q, seed=sum(lens) + q)
     pools = S.fill_pools(wl, nb)
     inp = S.device_inputs(wl)
-    ids, sc, o = _to_np(S.run_step(nb, wl, pools, inp))
+    ids, sc, o = _to_np(S.run_step(nb, wl, pools, inp, fused=fused))
     _structural(wl, ids)
     fails = S.check_page_bytes(wl, pools, np.unique(wl.block_table[wl.block_table >= 0]))
     for b in range(wl.num_seqs):
@@ -249,15 +250,78 @@ def test_two_stage_indexer_equals_decode(nb):
             assert np.all(bs[row, nbk:] == -7.0) and np.all(bs[row, :nbk] >= 0)
 
 
-def test_select_many_equal_scores(nb):
-    say("selection with all-equal and adversarial scores")
-    tq, mb = 4, 3000
+@pytest.mark.parametrize("lens,q", [TINY[1], TINY[3], TINY[7]])
+def test_fused_select_attention_equals_separate(nb, lens, q):
+    say(f"selection inside attention == select + attention, lens={lens} q={q}")
+    wl = tiny_config(lens, q, seed=11 + q, spare_pages=5, permute=True)
+    pools = S.fill_pools(wl, nb)
+    inp = S.device_inputs(wl)
+    a = _to_np(S.run_step(nb, wl, pools, inp, fused=False))
+    b = _to_np(S.run_step(nb, wl, pools, inp, fused=True))
+    assert np.array_equal(a[0], b[0])
+    assert np.array_equal(a[1], b[1])
+    assert np.array_equal(a[2], b[2])          # the same blocks in the same order: same bits
+
+
+def test_fused_select_attention_without_ids_and_invalid_rows(nb):
+    say("selection inside attention: no id output, invalid lengths and pages")
+    wl = tiny_config([2500, 3000, 40, 2600], 2, seed=12)
+    pools = S.fill_pools(wl, nb)
+    inp = S.device_inputs(wl)
+    lens = inp["seq_lens"].clone()
+    lens[1] = wl.max_blocks * 128 + 1            # longer than the block table
+    lens[2] = 1                                  # shorter than q_per_seq
+    bt = inp["block_table"].clone()
+    bt[3, 3] = -5
+    bt[3, 7] = 1 << 30
+    inp = dict(inp, seq_lens=lens, block_table=bt)
+    kc, ks = pools[synth.STREAM_K]
+    vc, vs = pools[synth.STREAM_V]
+    ic, isc = pools[synth.STREAM_IDX]
+    tq = wl.num_q_tokens
+    bscores = torch.zeros((tq, wl.max_blocks), dtype=torch.float32, device="cuda")
+    nb.msa_indexer_scan(ic, isc, inp["q_idx"], inp["w"], bt, lens, wl.q_per_seq, bscores)
+    ws = nb.attn_workspace(wl.num_seqs, wl.q_per_seq, wl.num_q_heads, 17)
+    o1 = torch.full((tq, 32, 128), 5.0, device="cuda")
+    o2 = torch.full((tq, 32, 128), 5.0, device="cuda")
+    ids = torch.full((tq, 17), 99, dtype=torch.int32, device="cuda")
+    scale = 1.0 / math.sqrt(128)
+    nb.msa_sparse_attn_select_decode(kc, ks, vc, vs, inp["q_attn"], bt, lens, wl.q_per_seq,
+                                     bscores, scale, o1, ws)
+    nb.msa_sparse_attn_select_decode(kc, ks, vc, vs, inp["q_attn"], bt, lens, wl.q_per_seq,
+                                     bscores, scale, o2, ws, out_ids=ids)
+    ids_ref = torch.empty_like(ids)
+    nb.msa_indexer_select(bscores, lens, wl.q_per_seq, ids_ref)
+    o3 = torch.empty_like(o1)
+    nb.msa_sparse_attn_decode(kc, ks, vc, vs, inp["q_attn"], bt, lens, wl.q_per_seq, ids_ref,
+                              scale, o3, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(o1, o3)
+    assert torch.equal(ids, ids_ref)
+    idn = ids.cpu().numpy()
+    on = o1.cpu().numpy()
+    for b in (1, 2):
+        assert np.all(idn[2 * b:2 * b + 2] == -1)
+        assert np.all(on[2 * b:2 * b + 2] == 0)
+    assert np.all(np.isfinite(on))
+
+
+@pytest.mark.parametrize("mb", [3000, 2050, 2049, 1500, 18])
+def test_select_many_equal_scores(nb, mb):
+    # 2049 blocks = 2048 candidates, the most held in registers; 2050 and up
+    # re-read the scores from memory
+    say(f"selection with random, all-equal and adversarial scores, {mb} blocks")
+    tq = 6
     lens = torch.tensor([mb * 128] * tq, dtype=torch.int32, device="cuda")
-    rng = np.random.default_rng(2)
+    rng = np.random.default_rng(2 + mb)
     bs = np.zeros((tq, mb), dtype=np.float32)
+    bs[0] = rng.random(mb, dtype=np.float32)
     bs[1] = np.tile(np.arange(64, dtype=np.float32)[::-1], mb // 64 + 1)[:mb]   # periodic
     bs[2] = rng.integers(0, 3, mb).astype(np.float32)                            # few levels
     bs[3] = -0.0
+    bs[4] = np.arange(mb, dtype=np.float32)                                      # ascending
+    bs[5] = rng.random(mb, dtype=np.float32)
+    bs[5, rng.choice(mb - 1, min(40, mb - 1), replace=False)] = 2.0             # 40-way tie on top
     ids = torch.empty((tq, 17), dtype=torch.int32, device="cuda")
     sc = torch.empty((tq, 17), dtype=torch.float32, device="cuda")
     nb.msa_indexer_select(torch.from_numpy(bs).cuda(), lens, 1, ids, sc)
@@ -266,6 +330,9 @@ def test_select_many_equal_scores(nb):
     for r in range(tq):
         want = msa.select_blocks(np.maximum(bs[r].astype(np.float64), 0.0))
         assert ids[r].cpu().numpy().tolist() == want.tolist(), r
+        got_sc = sc[r].cpu().numpy()
+        want_sc = np.where(want >= 0, np.maximum(bs[r], 0)[np.maximum(want, 0)], 0)
+        assert np.array_equal(got_sc, want_sc.astype(np.float32)), r
 
 
 def test_empty_batch_and_bad_shapes(nb):

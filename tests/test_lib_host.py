@@ -103,6 +103,28 @@ def test_attention_rejects_before_launch(L):
     assert call(ws=None) == 3                    # 17 blocks need split partials
 
 
+def test_select_attention_rejects_before_launch(L):
+    f = L.msa_sparse_attn_select_decode
+    d = ctypes.byref(_desc())
+
+    def call(desc=d, q=32, mb=4, ns=1, qps=1, bs=256, topk=16, ids=None, scale=0.088, ptr=256,
+             ws=None, wsb=0):
+        return f(desc, ptr, ptr, ptr, ptr, ptr, q, ptr, mb, ptr, ns, qps, bs, topk, ids, scale,
+                 ptr, ws, wsb, None)
+    assert call(desc=None) == 1
+    assert call(q=24) == 2
+    assert call(topk=17) == 2
+    assert call(qps=9) == 2
+    assert call(scale=-1.0) == 1
+    assert call(ns=0) == 0
+    assert call(bs=None) == 1                    # no block scores
+    assert call(bs=4096 + 2) == 1                # misaligned scores
+    assert call(ids=4096 + 2) == 1               # misaligned ids
+    assert call(ptr=None) == 1
+    assert call(ws=None) == 3                    # 17 blocks need split partials
+    assert call(ws=4096, wsb=64) == 3
+
+
 def test_two_stage_indexer_rejects_before_launch(L):
     d = ctypes.byref(_desc())
     scan = L.msa_indexer_scan
