@@ -11,14 +11,14 @@
 //   1. lane l holds the scores of blocks l, l+64, ..., l+64*31 of a chunk of
 //      2,048 (one chunk in registers; longer contexts loop over chunks) and
 //      their maximum;
-//   2. theta = the 16th largest of the 64 lane maxima, built bit by bit from
-//      the top with ballot counts: the 16 lanes holding the largest maxima
+//   2. theta = the 16th largest of the 64 lane maxima (ranked by counting
+//      against broadcast LDS reads): the 16 lanes holding the largest maxima
 //      each own a block scoring >= theta, so at least 16 candidates reach
 //      theta and the top-16 are among them;
 //   3. the candidates >= theta (typically 16..25) are compacted into LDS at
-//      offsets from a DPP prefix sum of per-lane counts and ranked exactly by
-//      counting; with more than 64 of them (many equal scores) 16 rounds of
-//      wavefront arg-max take over;
+//      offsets from a DPP prefix sum of per-lane hit counts and ranked exactly
+//      by counting against broadcast LDS reads; with more than 64 of them
+//      (many equal scores) 16 rounds of wavefront arg-max take over;
 //   4. the 16 winners are put in ascending block order, the recent block last.
 #pragma once
 
@@ -30,11 +30,14 @@ constexpr int kTopK = 16;
 constexpr int kSelPerLane = 32;               // scores per lane per chunk
 constexpr int kSelChunk = 64 * kSelPerLane;   // 2,048 candidates per chunk
 
-struct SelectScratch {
-  uint64_t cand[64];  // compacted candidates (keys)
+struct __align__(16) SelectScratch {
+  uint32_t stage[kSelChunk];  // the current chunk's score bits, [k][lane]
+  uint64_t lanemax[64];       // (lane maximum << 6 | 63 - lane)
+  uint64_t cand[64];          // compacted candidates (keys)
   uint64_t win[kTopK];
   int32_t id[kTopK];
   float score[kTopK];
+  uint32_t theta;
 };
 
 __device__ __forceinline__ uint32_t score_bits(float s) { return __float_as_uint(s > 0.0f ? s : 0.0f); }
@@ -96,6 +99,10 @@ __device__ __forceinline__ int select_blocks(const float* row, int row_len, int 
 #pragma unroll
     for (int k = 0; k < kSelPerLane; ++k) v[k] = c0 + lane + 64 * k < n ? score_bits(x[k]) : 0u;
   };
+  auto stage_chunk = [&]() {
+#pragma unroll
+    for (int k = 0; k < kSelPerLane; ++k) sc.stage[64 * k + lane] = v[k];
+  };
   // 1. lane maxima
   uint32_t m = 0;
   for (int c = 0; c < nchunks; ++c) {
@@ -103,38 +110,54 @@ __device__ __forceinline__ int select_blocks(const float* row, int row_len, int 
 #pragma unroll
     for (int k = 0; k < kSelPerLane; ++k) m = max(m, v[k]);
   }
-  // 2. theta: the largest t with at least 16 lane maxima >= t
-  uint32_t theta = 0;
+  // 2. theta: the lane maximum of rank 15 among the 64, ranked as distinct
+  //    keys (maximum, then lane) by counting against broadcast LDS reads
+  const uint64_t mkey = (uint64_t(m) << 6) | uint64_t(63 - lane);
+  sc.lanemax[lane] = mkey;
+  wave_lds_sync();
+  int mrank = 0;
 #pragma unroll
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t t = theta | (1u << bit);
-    if (__popcll(__ballot(m >= t)) >= kTopK) theta = t;
+  for (int i = 0; i < 64; i += 2) {
+    const ulonglong2 two = *reinterpret_cast<const ulonglong2*>(&sc.lanemax[i]);
+    mrank += (two.x > mkey ? 1 : 0) + (two.y > mkey ? 1 : 0);
   }
-  // 3. compact the candidates reaching theta
+  if (mrank == kTopK - 1) sc.theta = m;
+  wave_lds_sync();
+  const uint32_t theta = sc.theta;
+  // 3. compact the candidates reaching theta: a per-lane bit mask of hits,
+  //    positions from a prefix sum of its population count, hit values read
+  //    back from the LDS copy of the chunk (hits are rare: a lane has 0..2)
   int cnt = 0;  // uniform
   for (int c = 0; c < nchunks; ++c) {
-    if (nchunks > 1) chunk_bits(c);
     const int c0 = c * kSelChunk;
-    int mine = 0;
+    if (nchunks > 1) {
+      chunk_bits(c);
+      stage_chunk();
+    } else if (c == 0) {
+      stage_chunk();
+    }
+    uint32_t hits = 0;
 #pragma unroll
-    for (int k = 0; k < kSelPerLane; ++k) mine += (c0 + lane + 64 * k < n && v[k] >= theta) ? 1 : 0;
+    for (int k = 0; k < kSelPerLane; ++k)
+      hits |= (c0 + lane + 64 * k < n && v[k] >= theta) ? (1u << k) : 0u;
+    const int mine = __popc(hits);
     const int incl = wave_inclusive_sum(mine, lane);
     int pos = cnt + incl - mine;
-#pragma unroll
-    for (int k = 0; k < kSelPerLane; ++k) {
-      const int j = c0 + lane + 64 * k;
-      if (j < n && v[k] >= theta) {
-        if (pos < 64) sc.cand[pos] = make_key(v[k], j);
-        ++pos;
-      }
+    wave_lds_sync();
+    while (hits) {
+      const int k = __builtin_ctz(hits);
+      hits &= hits - 1;
+      if (pos < 64) sc.cand[pos] = make_key(sc.stage[64 * k + lane], c0 + lane + 64 * k);
+      ++pos;
     }
     cnt += __builtin_amdgcn_readlane(incl, 63);
+    wave_lds_sync();
   }
-  wave_lds_sync();
   if (cnt <= 64) {
+    // rank by counting against broadcast LDS reads of the candidates
     const uint64_t key = lane < cnt ? sc.cand[lane] : 0ull;
     int r = 0;
-    for (int s = 0; s < cnt; ++s) r += readlane_u64(key, s) > key ? 1 : 0;
+    for (int s = 0; s < cnt; ++s) r += sc.cand[s] > key ? 1 : 0;
     if (lane < cnt && r < kTopK) sc.win[r] = key;
   } else {
     // many candidates reach theta (equal scores): exact arg-max rounds
@@ -163,7 +186,7 @@ __device__ __forceinline__ int select_blocks(const float* row, int row_len, int 
   const int wid = key_block_id(wk);
   int order = 0;
 #pragma unroll
-  for (int i = 0; i < kTopK; ++i) order += key_block_id(readlane_u64(wk, i)) < wid ? 1 : 0;
+  for (int i = 0; i < kTopK; ++i) order += key_block_id(sc.win[i]) < wid ? 1 : 0;
   if (lane < kTopK) {
     sc.id[order] = wid;
     sc.score[order] = key_score_value(wk);

@@ -306,6 +306,56 @@ def test_fused_select_attention_without_ids_and_invalid_rows(nb):
     assert np.all(np.isfinite(on))
 
 
+def test_graph_replay_matches_eager(nb):
+    say("decode step captured in a HIP graph, replayed between eager work")
+    wl = tiny_config([3000, 2400, 700], 2, seed=31)
+    pools = S.fill_pools(wl, nb)
+    inp = S.device_inputs(wl)
+    ws_i = nb.indexer_workspace(wl.num_seqs, wl.q_per_seq, wl.max_blocks)
+    ws_a = nb.attn_workspace(wl.num_seqs, wl.q_per_seq, wl.num_q_heads, wl.topk + 1)
+    tq = wl.num_q_tokens
+    out = dict(ids=torch.empty((tq, 17), dtype=torch.int32, device="cuda"),
+               scores=torch.empty((tq, 17), dtype=torch.float32, device="cuda"),
+               o=torch.empty((tq, wl.num_q_heads, 128), dtype=torch.float32, device="cuda"))
+    ref = _to_np(S.run_step(nb, wl, pools, inp, ws_i, ws_a, out))
+    ic, isc = pools[synth.STREAM_IDX]
+    kc, ks = pools[synth.STREAM_K]
+    vc, vs = pools[synth.STREAM_V]
+    bscores = ws_i[: tq * wl.max_blocks * 4].view(torch.float32).view(tq, wl.max_blocks)
+
+    def step():
+        nb.msa_indexer_scan(ic, isc, inp["q_idx"], inp["w"], inp["block_table"], inp["seq_lens"],
+                            wl.q_per_seq, bscores)
+        nb.msa_sparse_attn_select_decode(kc, ks, vc, vs, inp["q_attn"], inp["block_table"],
+                                         inp["seq_lens"], wl.q_per_seq, bscores,
+                                         1.0 / math.sqrt(128), out["o"], ws_a, out_ids=out["ids"])
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        step()
+        cap.synchronize()
+        with torch.cuda.graph(g, stream=cap):
+            step()
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    other = tiny_config([1500, 900, 300], 2, seed=32)       # same shapes, other data
+    other_inp = S.device_inputs(other)
+    for rep in range(3):
+        out["o"].fill_(float(rep + 1))
+        out["ids"].fill_(-7)
+        bscores.fill_(3.0)
+        # eager work on other inputs between replays, sharing the workspaces
+        S.run_step(nb, other, pools, other_inp, ws_i, ws_a, dict(
+            ids=torch.empty_like(out["ids"]), scores=torch.empty_like(out["scores"]),
+            o=torch.empty_like(out["o"])))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out["ids"].cpu().numpy(), ref[0]), rep
+        assert np.array_equal(out["o"].cpu().numpy(), ref[2]), rep
+
+
 @pytest.mark.parametrize("mb", [3000, 2050, 2049, 1500, 18])
 def test_select_many_equal_scores(nb, mb):
     # 2049 blocks = 2048 candidates, the most held in registers; 2050 and up
