@@ -73,15 +73,28 @@ constexpr float kPLoScale = 16.0f;                    // P_lo = FP8(16 (256 p - 
 constexpr int kE8M0One = 0x7F7F7F7F;                  // MFMA operand scale 2^0
 constexpr int kE8M0Sixteenth = 0x7B7B7B7B;            // MFMA operand scale 2^-4
 
+// All-reduce over each row of 16 lanes with DPP (no LDS round trips):
+// exchange within quads (xor 1, xor 2), then rotate the row by 4 and by 8,
+// which brings in the other three quads.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_row(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+constexpr int kQuadXor1 = 0xB1;  // quad_perm [1, 0, 3, 2]
+constexpr int kQuadXor2 = 0x4E;  // quad_perm [2, 3, 0, 1]
+constexpr int kRowRor4 = 0x124;
+constexpr int kRowRor8 = 0x128;
 __device__ __forceinline__ float row16_max(float v) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = fmaxf(v, dpp_row<kQuadXor1>(v));
+  v = fmaxf(v, dpp_row<kQuadXor2>(v));
+  v = fmaxf(v, dpp_row<kRowRor4>(v));
+  return fmaxf(v, dpp_row<kRowRor8>(v));
 }
 __device__ __forceinline__ float row16_sum(float v) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += dpp_row<kQuadXor1>(v);
+  v += dpp_row<kQuadXor2>(v);
+  v += dpp_row<kRowRor4>(v);
+  return v + dpp_row<kRowRor8>(v);
 }
 
 // 32 bytes of an MFMA operand from four transposed 8-byte LDS reads.

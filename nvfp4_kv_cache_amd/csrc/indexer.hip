@@ -175,16 +175,23 @@ __global__ __launch_bounds__(512) void indexer_kernel(const IndexerArgs a) {
           s += pq[h * QR * 2 * kBlockTokens + t] + pq[h * QR * 2 * kBlockTokens + kBlockTokens + t];
         if (blk * kBlockTokens + t <= pos) m = fmaxf(m, s);
       }
-      m = wave_max(m);
+      m = __uint_as_float(wave_max_u32(__float_as_uint(m)));  // m >= 0
       if (lane == 0) a.bscore[(qrow0 + qi) * a.max_blocks + blk] = page_ok ? m : 0.0f;
     }
   };
 
   if constexpr (STAGES == 1) {
+    // one register buffer: the next block's loads are issued as soon as the
+    // current block's codes are consumed, so their latency overlaps the
+    // barrier and the block reduction (the scheduling barriers keep the
+    // compiler from hoisting them into a second buffer)
+    TileLoads t;
+    if (count > 0) issue_loads(t, codes_h, scales_h, pages[0], page_codes, page_scales);
     for (int k = 0; k < count; ++k) {
-      TileLoads t;
-      issue_loads(t, codes_h, scales_h, pages[k], page_codes, page_scales);
       compute(t, k & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (k + 1 < count) issue_loads(t, codes_h, scales_h, pages[k + 1], page_codes, page_scales);
+      __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
       reduce(k, k & 1);
     }

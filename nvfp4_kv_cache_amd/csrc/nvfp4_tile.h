@@ -178,20 +178,19 @@ __device__ __forceinline__ uint4 load_stream16(const void* p) {
 }
 
 // ---------------------------------------------------------------- waves
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-__device__ __forceinline__ int wave_sum_int(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+// Maximum of an unsigned value over the wavefront, uniform result: prefix
+// maxima inside each row of 16 lanes with DPP row shifts (out-of-row lanes
+// read 0, the identity), then the four row results through lane reads. No
+// LDS round trips, unlike a shuffle butterfly. Non-negative floats can use it
+// on their bit patterns.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x111, 0xF, 0xF, true)));  // row_shr:1
+  v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x112, 0xF, 0xF, true)));  // row_shr:2
+  v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x114, 0xF, 0xF, true)));  // row_shr:4
+  v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x118, 0xF, 0xF, true)));  // row_shr:8
+  const uint32_t r0 = __builtin_amdgcn_readlane(int(v), 15), r1 = __builtin_amdgcn_readlane(int(v), 31);
+  const uint32_t r2 = __builtin_amdgcn_readlane(int(v), 47), r3 = __builtin_amdgcn_readlane(int(v), 63);
+  return max(max(r0, r1), max(r2, r3));
 }
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 #pragma unroll
@@ -200,11 +199,6 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     v = w > v ? w : v;
   }
   return v;
-}
-__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
-  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, lane);
-  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
-  return (uint64_t(hi) << 32) | lo;
 }
 // LDS visibility between lanes of one wavefront.
 __device__ __forceinline__ void wave_lds_sync() {
