@@ -153,20 +153,23 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(const AttnArgs a) {
 
   // lane l: block of selected slot l and its physical page (-1: skip). Every
   // wavefront runs the same selection (no barrier, scratch in its own LDS).
+  int pg = -1;
   if constexpr (SELECT) {
     if (seq_ok) {
       float score;
+      int page;
       sel = select_blocks(a.bscore + int64_t(qt) * a.max_blocks, a.max_blocks,
                           pos / kBlockTokens + 1, x0, *reinterpret_cast<SelectScratch*>(vrows),
-                          lane, &score);
+                          lane, &score, a.block_table + int64_t(b) * a.max_blocks, &page);
+      pg = (sel >= 0 && page >= 0 && page < a.num_pages) ? page : -1;
     }
     if (a.out_ids && sp == 0 && kh == 0 && wave == 0 && lane <= kTopK)
       a.out_ids[int64_t(qt) * (kTopK + 1) + lane] = sel;
-  }
-  int pg = -1;
-  if (seq_ok && sel >= 0 && sel < a.max_blocks && sel * kBlockTokens <= pos) {
-    const int p = a.block_table[int64_t(b) * a.max_blocks + sel];
-    pg = (p >= 0 && p < a.num_pages) ? p : -1;
+  } else {
+    if (seq_ok && sel >= 0 && sel < a.max_blocks && sel * kBlockTokens <= pos) {
+      const int p = a.block_table[int64_t(b) * a.max_blocks + sel];
+      pg = (p >= 0 && p < a.num_pages) ? p : -1;
+    }
   }
   // online-softmax state of heads 4*slice + v (meaningful in lanes 0..31)
   const float ninf = -__builtin_huge_valf();
@@ -188,6 +191,7 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(const AttnArgs a) {
   const int s_begin = sp * W * a.slots_per_wave;
   const int s_end = min(a.num_sel, s_begin + W * a.slots_per_wave);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  bool fresh = true;  // no block accumulated yet: o is zero and needs no rescale
   for (int si = s_begin + wave_u; si < s_end; si += W) {
     const int page = __builtin_amdgcn_readlane(pg, si);
     if (page < 0) continue;  // uniform over the wavefront
@@ -240,7 +244,7 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(const AttnArgs a) {
 #pragma unroll
       for (int j = 1; j < 8; ++j) mb = fmaxf(mb, z[j][v]);
       const float m_new = fmaxf(m_run[v], row16_max(mb));
-      alpha[v] = m_run[v] == ninf ? 0.0f : exp2f(m_run[v] - m_new);
+      alpha[v] = m_run[v] == ninf ? 0.0f : __builtin_amdgcn_exp2f(m_run[v] - m_new);
       m_run[v] = m_new;
     }
     float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -248,7 +252,8 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(const AttnArgs a) {
     for (int j = 0; j < 8; ++j) {
       float p[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) p[v] = z[j][v] == ninf ? 0.0f : exp2f(z[j][v] - m_run[v]) * kPScale;
+      for (int v = 0; v < 4; ++v)
+        p[v] = z[j][v] == ninf ? 0.0f : __builtin_amdgcn_exp2f(z[j][v] - m_run[v]) * kPScale;
       int hi = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
       hi = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], hi, true);
       const v2f h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
@@ -272,8 +277,10 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(const AttnArgs a) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       l_run[v] = l_run[v] * alpha[v] + row16_sum(lsum[v]);
+      if (!fresh) {
 #pragma unroll
-      for (int n = 0; n < 8; ++n) o[n][v] *= alpha[v];
+        for (int n = 0; n < 8; ++n) o[n][v] *= alpha[v];
+      }
     }
     wave_lds_sync();
     // 4. O += P_hi V + 2^-4 P_lo V. A: lane li < 8 -> head li, tokens
@@ -297,6 +304,7 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(const AttnArgs a) {
                                                                  kE8M0Sixteenth, 0, kE8M0One);
       }
     }
+    fresh = false;
     wave_lds_sync();
   }
 

@@ -35,8 +35,10 @@ struct __align__(16) SelectScratch {
   uint64_t lanemax[64];       // (lane maximum << 6 | 63 - lane)
   uint64_t cand[64];          // compacted candidates (keys)
   uint64_t win[kTopK];
+  int32_t win_page[kTopK];
   int32_t id[kTopK];
   float score[kTopK];
+  int32_t page[kTopK];
   uint32_t theta;
 };
 
@@ -76,14 +78,22 @@ __device__ __forceinline__ int wave_inclusive_sum(int v, int lane) {
 // wavefront must call it. Lane l < 17 receives the l-th selected block
 // (ascending; the recent block last when nb > 17) and its score; other lanes,
 // and lanes past nb when nb <= 17, receive -1 and 0.
+// With a block-table row (table_row[j] = page of block j, j < nb), *page_out
+// receives the selected block's table entry, unchecked (-1 where no block):
+// the lookups are issued as soon as the candidates are known, so their
+// latency overlaps the exact ranking.
 __device__ __forceinline__ int select_blocks(const float* row, int row_len, int nb,
                                              const float (&x0)[kSelPerLane], SelectScratch& sc,
-                                             int lane, float* score_out) {
+                                             int lane, float* score_out,
+                                             const int32_t* table_row = nullptr,
+                                             int* page_out = nullptr) {
   if (nb <= kTopK + 1) {
     const bool in = lane < nb;
     *score_out = in ? __uint_as_float(score_bits(row[min(lane, row_len - 1)])) : 0.0f;
+    if (table_row) *page_out = in ? table_row[min(lane, nb - 1)] : -1;
     return in ? lane : -1;
   }
+  const int recent_page = (table_row && lane == kTopK) ? table_row[nb - 1] : -1;
   const int n = nb - 1;  // candidates; the recent block is always kept
   const int nchunks = (n + kSelChunk - 1) / kSelChunk;
   uint32_t v[kSelPerLane];
@@ -154,11 +164,16 @@ __device__ __forceinline__ int select_blocks(const float* row, int row_len, int 
     wave_lds_sync();
   }
   if (cnt <= 64) {
-    // rank by counting against broadcast LDS reads of the candidates
+    // rank by counting against broadcast LDS reads of the candidates; the
+    // candidates' pages are in flight meanwhile
     const uint64_t key = lane < cnt ? sc.cand[lane] : 0ull;
+    const int cpage = (table_row && lane < cnt) ? table_row[key_block_id(key)] : -1;
     int r = 0;
     for (int s = 0; s < cnt; ++s) r += sc.cand[s] > key ? 1 : 0;
-    if (lane < cnt && r < kTopK) sc.win[r] = key;
+    if (lane < cnt && r < kTopK) {
+      sc.win[r] = key;
+      sc.win_page[r] = cpage;
+    }
   } else {
     // many candidates reach theta (equal scores): exact arg-max rounds
     uint64_t last = ~0ull;
@@ -176,13 +191,17 @@ __device__ __forceinline__ int select_blocks(const float* row, int row_len, int 
         }
       }
       best = wave_max_u64(best);
-      if (lane == 0) sc.win[r] = best;
+      if (lane == 0) {
+        sc.win[r] = best;
+        sc.win_page[r] = table_row ? table_row[key_block_id(best)] : -1;
+      }
       last = best;
     }
   }
   wave_lds_sync();
   // 4. ascending block order
   const uint64_t wk = lane < kTopK ? sc.win[lane] : 0ull;
+  const int wpage = lane < kTopK ? sc.win_page[lane] : -1;
   const int wid = key_block_id(wk);
   int order = 0;
 #pragma unroll
@@ -190,12 +209,15 @@ __device__ __forceinline__ int select_blocks(const float* row, int row_len, int 
   if (lane < kTopK) {
     sc.id[order] = wid;
     sc.score[order] = key_score_value(wk);
+    sc.page[order] = wpage;
   }
   wave_lds_sync();
   if (lane < kTopK) {
     *score_out = sc.score[lane];
+    if (table_row) *page_out = sc.page[lane];
     return sc.id[lane];
   }
+  if (table_row) *page_out = recent_page;
   if (lane == kTopK) {
     *score_out = __uint_as_float(score_bits(row[nb - 1]));
     return nb - 1;
