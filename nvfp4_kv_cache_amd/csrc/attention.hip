@@ -72,6 +72,7 @@ constexpr float kPScale = 256.0f;                     // P_hi = FP8(256 p)
 constexpr float kPLoScale = 16.0f;                    // P_lo = FP8(16 (256 p - P_hi))
 constexpr int kE8M0One = 0x7F7F7F7F;                  // MFMA operand scale 2^0
 constexpr int kE8M0Sixteenth = 0x7B7B7B7B;            // MFMA operand scale 2^-4
+constexpr int kFp8Ones = 0x38383838;                  // four FP8 E4M3 1.0
 
 // All-reduce over each row of 16 lanes with DPP (no LDS round trips):
 // exchange within quads (xor 1, xor 2), then rotate the row by 4 and by 8,
@@ -207,36 +208,37 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(const AttnArgs a) {
     for (int j = 0; j < 8; ++j) vc[j] = load_stream16(a.v_codes + hc + j * 16 * kCodeRow);
     const uint4 vsw = load_stream16(a.v_scales + hs);
     // 1. logits of 16 tokens per tile: lane holds heads 4*slice+v, token 16j+li
+    const bool part = ntok < kBlockTokens;  // the block is only partly visible
     float z[8][4];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const uint32_t ks = tile_scales(ksw, j);
       const v8i kop = dequant32(kc[j], lut[ks & 0x7F], lut[(ks >> 8) & 0x7F]);
       const v4f c = mfma_fp8_16x16x128(qop, kop, v4f{0.0f, 0.0f, 0.0f, 0.0f});
-      const bool live = 16 * j + li < ntok;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) z[j][v] = live ? c[v] * a.scale_log2 : ninf;
+      for (int v = 0; v < 4; ++v) z[j][v] = c[v] * a.scale_log2;
     }
-    // 2. V rows into LDS in natural channel order (masked tokens -> 0)
+    if (part) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) z[j][v] = 16 * j + li < ntok ? z[j][v] : ninf;
+    }
+    // 2. V rows into LDS in the dequantiser's channel order (0,2,4,6,1,3,5,7
+    //    in every run of 8; the output index undoes it); invisible tokens -> 0
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const uint32_t vsc = tile_scales(vsw, j);
-      const v8i vop = dequant32(vc[j], lut[vsc & 0x7F], lut[(vsc >> 8) & 0x7F]);
-      const bool live = 16 * j + li < ntok;
-      uint32_t nat[8];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t ev = uint32_t(vop[2 * u]), od = uint32_t(vop[2 * u + 1]);
-        nat[2 * u] = live ? __builtin_amdgcn_perm(od, ev, 0x05010400u) : 0u;
-        nat[2 * u + 1] = live ? __builtin_amdgcn_perm(od, ev, 0x07030602u) : 0u;
-      }
+      v8i vop = dequant32(vc[j], lut[vsc & 0x7F], lut[(vsc >> 8) & 0x7F]);
+      if (part && 16 * j + li >= ntok) vop = v8i{0, 0, 0, 0, 0, 0, 0, 0};
       uint8_t* dst = vrows + (16 * j + li) * kVRow + slice * 32;
-      *reinterpret_cast<uint2*>(dst) = make_uint2(nat[0], nat[1]);
-      *reinterpret_cast<uint2*>(dst + 8) = make_uint2(nat[2], nat[3]);
-      *reinterpret_cast<uint2*>(dst + 16) = make_uint2(nat[4], nat[5]);
-      *reinterpret_cast<uint2*>(dst + 24) = make_uint2(nat[6], nat[7]);
+      *reinterpret_cast<uint2*>(dst) = make_uint2(uint32_t(vop[0]), uint32_t(vop[1]));
+      *reinterpret_cast<uint2*>(dst + 8) = make_uint2(uint32_t(vop[2]), uint32_t(vop[3]));
+      *reinterpret_cast<uint2*>(dst + 16) = make_uint2(uint32_t(vop[4]), uint32_t(vop[5]));
+      *reinterpret_cast<uint2*>(dst + 24) = make_uint2(uint32_t(vop[6]), uint32_t(vop[7]));
     }
-    // 3. softmax: block max per head, rescale, P = FP8(256 * 2^(z - m))
+    // 3. softmax: block max per head, rescale, P = FP8(256 * 2^(z - m)) as
+    //    two FP8 terms (exp2 of -inf is 0, so invisible tokens drop out)
     float alpha[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -244,16 +246,14 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(const AttnArgs a) {
 #pragma unroll
       for (int j = 1; j < 8; ++j) mb = fmaxf(mb, z[j][v]);
       const float m_new = fmaxf(m_run[v], row16_max(mb));
-      alpha[v] = m_run[v] == ninf ? 0.0f : __builtin_amdgcn_exp2f(m_run[v] - m_new);
+      alpha[v] = __builtin_amdgcn_exp2f(m_run[v] - m_new);
       m_run[v] = m_new;
     }
-    float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       float p[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        p[v] = z[j][v] == ninf ? 0.0f : __builtin_amdgcn_exp2f(z[j][v] - m_run[v]) * kPScale;
+      for (int v = 0; v < 4; ++v) p[v] = __builtin_amdgcn_exp2f(z[j][v] - m_run[v]) * kPScale;
       int hi = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
       hi = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], hi, true);
       const v2f h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
@@ -262,30 +262,23 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(const AttnArgs a) {
                                                (p[1] - h01.y) * kPLoScale, 0, false);
       lo = __builtin_amdgcn_cvt_pk_fp8_f32((p[2] - h23.x) * kPLoScale,
                                            (p[3] - h23.y) * kPLoScale, lo, true);
-      const v2f l01 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
-      const v2f l23 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
-      lsum[0] += h01.x + l01.x * (1.0f / kPLoScale);
-      lsum[1] += h01.y + l01.y * (1.0f / kPLoScale);
-      lsum[2] += h23.x + l23.x * (1.0f / kPLoScale);
-      lsum[3] += h23.y + l23.y * (1.0f / kPLoScale);
       if (lane < 32) {
         const int off = (16 * j + li) * kHeadsPerKv + 4 * slice;
         *reinterpret_cast<int*>(prows + off) = hi;
         *reinterpret_cast<int*>(plows + off) = lo;
       }
     }
+    if (!fresh) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      l_run[v] = l_run[v] * alpha[v] + row16_sum(lsum[v]);
-      if (!fresh) {
+      for (int v = 0; v < 4; ++v)
 #pragma unroll
         for (int n = 0; n < 8; ++n) o[n][v] *= alpha[v];
-      }
     }
     wave_lds_sync();
     // 4. O += P_hi V + 2^-4 P_lo V. A: lane li < 8 -> head li, tokens
     //    32*slice + 8r .. +7; lanes 8..15 read the zero segment (rows 8..15
-    //    of A are zero).
+    //    of A are zero). The softmax denominator is the same product with a
+    //    column of FP8 ones, so it sums exactly the rounded terms of P.
     {
       const int t0 = 32 * slice;
       const int poff = (t0 + seg_row) * kHeadsPerKv;
@@ -294,6 +287,11 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(const AttnArgs a) {
       const int pstep = seg_half ? 0 : 8 * kHeadsPerKv;
       const v8i pop_hi = tr_operand(ph, ph + pstep, ph + 2 * pstep, ph + 3 * pstep);
       const v8i pop_lo = tr_operand(pl, pl + pstep, pl + 2 * pstep, pl + 3 * pstep);
+      const v8i ones = v8i{kFp8Ones, kFp8Ones, kFp8Ones, kFp8Ones,
+                           kFp8Ones, kFp8Ones, kFp8Ones, kFp8Ones};
+      v4f lb = mfma_fp8_16x16x128(pop_hi, ones, v4f{0.0f, 0.0f, 0.0f, 0.0f});
+      lb = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pop_lo, ones, lb, 0, 0, 0,
+                                                           kE8M0Sixteenth, 0, kE8M0One);
       const uint8_t* vb = vrows + (t0 + seg_row) * kVRow + 8 * seg_half;
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
@@ -303,6 +301,8 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(const AttnArgs a) {
         o[n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pop_lo, vop, o[n], 0, 0, 0,
                                                                  kE8M0Sixteenth, 0, kE8M0One);
       }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) l_run[v] = l_run[v] * alpha[v] + lb[v];
     }
     fresh = false;
     wave_lds_sync();
@@ -312,12 +312,15 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(const AttnArgs a) {
   __syncthreads();
   float* mo = reinterpret_cast<float*>(smem);                  // [W][8 heads][128]
   float* mml = mo + W * kHeadsPerKv * kHeadDim;                // [W][8 heads][2]
+  // o[n] column li holds V byte 16 n + li of the rows, i.e. channel
+  // 16 n + (li & 8) + {0, 2, 4, 6, 1, 3, 5, 7}[li & 7]
+  const int chan = (li & 8) + ((li & 7) < 4 ? 2 * (li & 7) : 2 * (li & 7) - 7);
   if (lane < 32) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int h = 4 * slice + v;
 #pragma unroll
-      for (int n = 0; n < 8; ++n) mo[(wave * kHeadsPerKv + h) * kHeadDim + 16 * n + li] = o[n][v];
+      for (int n = 0; n < 8; ++n) mo[(wave * kHeadsPerKv + h) * kHeadDim + 16 * n + chan] = o[n][v];
       if (li == 0) {
         mml[(wave * kHeadsPerKv + h) * 2] = m_run[v];
         mml[(wave * kHeadsPerKv + h) * 2 + 1] = l_run[v];
