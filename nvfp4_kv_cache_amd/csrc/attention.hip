@@ -129,8 +129,15 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(const AttnArgs a) {
   uint8_t* plows = prows + kPBytes;        // P_lo [token][head]
   const uint8_t* zeros = smem + W * kWaveLds;
 
-  // selection input in flight first: this query token's block scores, or
-  // the caller's ids (lane l: slot l)
+  // Loads in flight first, oldest first: the query operand (unconditional,
+  // rows 8..15 masked afterwards), then this query token's block scores or
+  // the caller's ids (lane l: slot l). Load counters retire in order, so a
+  // load issued late would later make its consumer wait for every load
+  // issued before it.
+  const uint4* qp = reinterpret_cast<const uint4*>(
+      a.q + (int64_t(qt) * Hq + kh * kHeadsPerKv + (li & (kHeadsPerKv - 1))) * kHeadDim +
+      slice * 32);
+  uint4 qa = qp[0], qb = qp[1];
   float x0[kSelPerLane];
   int sel = -1;
   if constexpr (SELECT) {
@@ -144,13 +151,13 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(const AttnArgs a) {
 
   for (int i = tid; i < 128; i += 64 * W) lut[i] = make_uint2(kAttnLut.lo[i], kAttnLut.hi[i]);
   if (tid < 16) reinterpret_cast<uint32_t*>(smem + W * kWaveLds)[tid] = 0u;
-  // query operand: rows 0..7 = the 8 query heads of this KV head
-  v8i qop = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-  if (li < kHeadsPerKv) {
-    const uint4* qp = reinterpret_cast<const uint4*>(
-        a.q + (int64_t(qt) * Hq + kh * kHeadsPerKv + li) * kHeadDim + slice * 32);
-    qop = q_operand(qp[0], qp[1]);
-  }
+  // query operand: rows 0..7 = the 8 query heads of this KV head. Consuming
+  // the loads here (before anything waits for the later ones) keeps the
+  // compiler from sinking them past the selection.
+  asm volatile("" : "+v"(qa.x), "+v"(qa.y), "+v"(qa.z), "+v"(qa.w), "+v"(qb.x), "+v"(qb.y),
+               "+v"(qb.z), "+v"(qb.w));
+  v8i qop = q_operand(qa, qb);
+  if (li >= kHeadsPerKv) qop = v8i{0, 0, 0, 0, 0, 0, 0, 0};
 
   // lane l: block of selected slot l and its physical page (-1: skip). Every
   // wavefront runs the same selection (no barrier, scratch in its own LDS).

@@ -19,7 +19,8 @@
 //      offsets from a DPP prefix sum of per-lane hit counts and ranked exactly
 //      by counting against broadcast LDS reads; with more than 64 of them
 //      (many equal scores) 16 rounds of wavefront arg-max take over;
-//   4. the 16 winners are put in ascending block order, the recent block last.
+//   4. each winner finds its place in ascending block order by counting; the
+//      recent block goes last.
 #pragma once
 
 #include "nvfp4_tile.h"
@@ -35,7 +36,6 @@ struct __align__(16) SelectScratch {
   uint64_t lanemax[64];       // (lane maximum << 6 | 63 - lane)
   uint64_t cand[64];          // compacted candidates (keys)
   uint64_t win[kTopK];
-  int32_t win_page[kTopK];
   int32_t id[kTopK];
   float score[kTopK];
   int32_t page[kTopK];
@@ -93,7 +93,8 @@ __device__ __forceinline__ int select_blocks(const float* row, int row_len, int 
     if (table_row) *page_out = in ? table_row[min(lane, nb - 1)] : -1;
     return in ? lane : -1;
   }
-  const int recent_page = (table_row && lane == kTopK) ? table_row[nb - 1] : -1;
+  // uniform address: issued now, consumed at the end
+  const int recent_page = table_row ? table_row[nb - 1] : -1;
   const int n = nb - 1;  // candidates; the recent block is always kept
   const int nchunks = (n + kSelChunk - 1) / kSelChunk;
   uint32_t v[kSelPerLane];
@@ -170,9 +171,19 @@ __device__ __forceinline__ int select_blocks(const float* row, int row_len, int 
     const int cpage = (table_row && lane < cnt) ? table_row[key_block_id(key)] : -1;
     int r = 0;
     for (int s = 0; s < cnt; ++s) r += sc.cand[s] > key ? 1 : 0;
-    if (lane < cnt && r < kTopK) {
-      sc.win[r] = key;
-      sc.win_page[r] = cpage;
+    const bool won = lane < cnt && r < kTopK;
+    if (won) sc.win[r] = key;
+    wave_lds_sync();
+    // 4. each winner finds its place in ascending block order and writes its
+    //    block, score and page there (the page is waited for only now)
+    if (won) {
+      const int id = key_block_id(key);
+      int order = 0;
+#pragma unroll
+      for (int i = 0; i < kTopK; ++i) order += key_block_id(sc.win[i]) < id ? 1 : 0;
+      sc.id[order] = id;
+      sc.score[order] = key_score_value(key);
+      sc.page[order] = cpage;
     }
   } else {
     // many candidates reach theta (equal scores): exact arg-max rounds
@@ -191,25 +202,20 @@ __device__ __forceinline__ int select_blocks(const float* row, int row_len, int 
         }
       }
       best = wave_max_u64(best);
-      if (lane == 0) {
-        sc.win[r] = best;
-        sc.win_page[r] = table_row ? table_row[key_block_id(best)] : -1;
-      }
+      if (lane == 0) sc.win[r] = best;
       last = best;
     }
-  }
-  wave_lds_sync();
-  // 4. ascending block order
-  const uint64_t wk = lane < kTopK ? sc.win[lane] : 0ull;
-  const int wpage = lane < kTopK ? sc.win_page[lane] : -1;
-  const int wid = key_block_id(wk);
-  int order = 0;
+    wave_lds_sync();
+    if (lane < kTopK) {
+      const uint64_t key = sc.win[lane];
+      const int id = key_block_id(key);
+      int order = 0;
 #pragma unroll
-  for (int i = 0; i < kTopK; ++i) order += key_block_id(sc.win[i]) < wid ? 1 : 0;
-  if (lane < kTopK) {
-    sc.id[order] = wid;
-    sc.score[order] = key_score_value(wk);
-    sc.page[order] = wpage;
+      for (int i = 0; i < kTopK; ++i) order += key_block_id(sc.win[i]) < id ? 1 : 0;
+      sc.id[order] = id;
+      sc.score[order] = key_score_value(key);
+      sc.page[order] = table_row ? table_row[id] : -1;
+    }
   }
   wave_lds_sync();
   if (lane < kTopK) {
@@ -217,7 +223,7 @@ __device__ __forceinline__ int select_blocks(const float* row, int row_len, int 
     if (table_row) *page_out = sc.page[lane];
     return sc.id[lane];
   }
-  if (table_row) *page_out = recent_page;
+  if (table_row) *page_out = lane == kTopK ? recent_page : -1;
   if (lane == kTopK) {
     *score_out = __uint_as_float(score_bits(row[nb - 1]));
     return nb - 1;
