@@ -9,9 +9,8 @@ and run exact attention over them, in one launch plus the split merge).
 Inputs are synthetic and already resident in HBM (seeded generator, cache
 written by msa_nvfp4_quantize) before the timed region starts.
 
-The step is captured in a HIP graph (g consecutive steps per graph, g the
-largest divisor of K up to 10) and the timed region replays it K / g times
-(checked bit for bit against the eager step first). Prints one JSON
+The timed region launches K steps back to back through prepared library
+calls (arguments marshalled once); --graph times HIP-graph replays instead. Prints one JSON
 line: query tokens/s (value), achieved HBM GB/s of the step, the indexer
 kernel against the HBM roofline (HIP events on the launch stream, eager
 launches), and the CPU oracle timed on a bounded sample of the same workload.
@@ -41,6 +40,8 @@ def parse():
     p.add_argument("--workload", type=int, default=2,
                    help="workload index (0..4); 2 = 8 x 262,144 tokens")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--graph", action="store_true",
+                   help="time HIP-graph replays of the captured step instead of eager launches")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain 1 GiB device-to-device copy (the reference kernel "
                         "for scaling HBM byte counters) and exit")
@@ -203,18 +204,17 @@ def main():
 
     bscores = ws_i[: tq * wl.max_blocks * 4].view(torch.float32).view(tq, wl.max_blocks)
 
-    def scan():
-        nb.msa_indexer_scan(ic, isc, inp["q_idx"], inp["w"], inp["block_table"], inp["seq_lens"],
-                            wl.q_per_seq, bscores)
-
-    def select_attend():
-        nb.msa_sparse_attn_select_decode(kc, ks, vc, vs, inp["q_attn"], inp["block_table"],
-                                         inp["seq_lens"], wl.q_per_seq, bscores, scale, out,
-                                         ws_a, out_ids=ids)
+    # each library call validated and marshalled once (binding.Prepared):
+    # re-issuing it is one ctypes call, so the host stays far ahead of the GPU
+    scan = nb.msa_indexer_scan(ic, isc, inp["q_idx"], inp["w"], inp["block_table"],
+                               inp["seq_lens"], wl.q_per_seq, bscores, prepare=True)
+    select_attend = nb.msa_sparse_attn_select_decode(
+        kc, ks, vc, vs, inp["q_attn"], inp["block_table"], inp["seq_lens"], wl.q_per_seq,
+        bscores, scale, out, ws_a, out_ids=ids, prepare=True)
 
     def step():
         # the whole hot path: index scan (scores), then selection + sparse
-        # attention in one launch
+        # attention in one launch (plus the split merge)
         scan()
         select_attend()
 
@@ -224,39 +224,50 @@ def main():
     torch.cuda.synchronize()
     eager_out, eager_ids = out.clone(), ids.clone()
 
-    # The step is captured in a HIP graph and replayed: the library only
-    # launches kernels on the caller's stream (no allocation, copy, memset or
-    # synchronisation), so the capture holds exactly the step's kernels and
-    # the timed loop is not bounded by host-side launch overhead. One graph
-    # holds g consecutive steps (g = the largest divisor of K up to 10, as a
-    # multi-layer decode captures all its layers in one graph): every graph
-    # launch costs a fixed gap on the GPU, which g steps share. A replay must
-    # reproduce the eager step bit for bit.
-    g = max(d for d in range(1, 11) if args.steps % d == 0)
-    graph = torch.cuda.CUDAGraph()
-    cap = torch.cuda.Stream()
-    cap.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(cap):
-        step()                                   # warm the capture stream
-        cap.synchronize()
-        with torch.cuda.graph(graph, stream=cap):
-            for _ in range(g):
-                step()
-    torch.cuda.current_stream().wait_stream(cap)
-    out.zero_()
-    ids.zero_()
-    graph.replay()
-    torch.cuda.synchronize()
-    if not (torch.equal(out, eager_out) and torch.equal(ids, eager_ids)):
-        raise RuntimeError("graph replay differs from the eager step")
-
-    # timed region: K back-to-back steps (K / g replays), synchronised on
-    # both sides
-    t0 = time.perf_counter()
-    for _ in range(args.steps // g):
+    # timed region: K back-to-back steps, synchronised on both sides. By
+    # default the steps are launched eagerly (prepared calls). With --graph
+    # they are captured in a HIP graph (g steps per graph, g the largest
+    # divisor of K up to 10) and replayed K/g times, after checking one
+    # replay bit for bit against the eager step; graph kernel nodes measured
+    # ~3 us slower each than stream launches here, so eager is the default.
+    if args.graph:
+        g = max(d for d in range(1, 11) if args.steps % d == 0)
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            g_scan = nb.msa_indexer_scan(ic, isc, inp["q_idx"], inp["w"], inp["block_table"],
+                                         inp["seq_lens"], wl.q_per_seq, bscores, prepare=True)
+            g_attn = nb.msa_sparse_attn_select_decode(
+                kc, ks, vc, vs, inp["q_attn"], inp["block_table"], inp["seq_lens"],
+                wl.q_per_seq, bscores, scale, out, ws_a, out_ids=ids, prepare=True)
+            g_scan()
+            g_attn()
+            cap.synchronize()
+            with torch.cuda.graph(graph, stream=cap):
+                for _ in range(g):
+                    g_scan()
+                    g_attn()
+        torch.cuda.current_stream().wait_stream(cap)
+        out.zero_()
+        ids.zero_()
         graph.replay()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+        torch.cuda.synchronize()
+        if not (torch.equal(out, eager_out) and torch.equal(ids, eager_ids)):
+            raise RuntimeError("graph replay differs from the eager step")
+        launch = f"hip_graph ({g} steps per replay)"
+        t0 = time.perf_counter()
+        for _ in range(args.steps // g):
+            graph.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    else:
+        launch = "eager (prepared calls)"
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
 
     # per-stage durations with HIP events on the launch stream (the library
     # launches on torch's current stream): the scan, then selection + attention
@@ -271,6 +282,31 @@ def main():
     torch.cuda.synchronize()
     t_idx = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
     t_attn = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
+
+    # cache effect: the timed steps re-read the same selected K/V blocks, which
+    # can stay in the 256 MB last-level cache between steps; a decode across
+    # many layers would have evicted them. Median of eager steps timed with
+    # events, without and with a 512 MiB overwrite before each step; a short
+    # spin kernel ahead of the start event keeps the host's launch latency
+    # out of both.
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def eager_step_us(cold):
+        ts = []
+        for _ in range(11):
+            if cold:
+                flush.fill_(1)
+            torch.cuda._sleep(200_000)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        return float(np.median(ts))
+    warm_us, cold_us = eager_step_us(False), eager_step_us(True)
+    del flush
 
     ids_np = ids.cpu().numpy()
     idx_bytes, attn_bytes, union = algorithmic_bytes(wl, ids_np)
@@ -289,7 +325,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8",
-        "launch": f"hip_graph ({g} steps per replay)",
+        "launch": launch,
         "data": "synthetic (seeded N(0,1) fp32 sources quantised to NVFP4 on the GPU; "
                 "FP8 queries; U(0,1) head weights)",
         "config": {"workload": wl.name, "num_seqs": wl.num_seqs,
@@ -303,6 +339,10 @@ def main():
         "kernels_us": {"msa_indexer_scan": round(t_idx * 1e6, 2),
                        "msa_sparse_attn_select_decode": round(t_attn * 1e6, 2)},
         "selected_blocks_union": int(union),
+        "cache_effect": {"method": "median of 11 eager steps timed with HIP events "
+                                   "behind a spin kernel",
+                         "warm_us": round(warm_us, 2), "cold_us": round(cold_us, 2),
+                         "flush_bytes_before_cold_step": 512 << 20},
         "roofline": {"bound": "hbm", "kernel": "indexer_kernel (msa_indexer_scan)",
                      "achieved": round(idx_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(idx_gbs / HBM_PEAK_GBS, 4),

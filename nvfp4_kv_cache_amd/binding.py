@@ -82,6 +82,32 @@ def _check(status: int, what: str):
         raise MsaError(f"{what}: {msa_status_string(status)}")
 
 
+class Prepared:
+    """One library call with its arguments validated and marshalled once
+    (device pointers, sizes, the stream that was current): calling it issues
+    the same launch again, for loops that re-run a step on unchanged buffers.
+    The tensors it was prepared from must stay alive and keep their shapes."""
+
+    def __init__(self, name: str, args: tuple, keep: tuple):
+        self._fn = getattr(lib(), name)
+        self._args = args
+        self._keep = keep
+        self.name = name
+
+    def __call__(self) -> None:
+        status = self._fn(*self._args)
+        if status != MSA_OK:
+            raise MsaError(f"{self.name}: {msa_status_string(status)}")
+
+
+def _issue(name: str, args: tuple, prepare: bool, keep: tuple = ()):
+    """Call the library now, or (prepare=True) return the call as a Prepared."""
+    if prepare:
+        return Prepared(name, args, keep)
+    _check(getattr(lib(), name)(*args), name)
+    return None
+
+
 def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
@@ -139,7 +165,7 @@ def scales_rows(scales: torch.Tensor) -> torch.Tensor:
     return x.permute(0, 1, 4, 3, 2, 5).reshape(p, h, BLOCK_TOKENS, HEAD_DIM // 16)
 
 
-def msa_nvfp4_quantize(src, slot_mapping, codes, scales):
+def msa_nvfp4_quantize(src, slot_mapping, codes, scales, prepare=False):
     """Quantise src float32 [T, H, 128] into the pool at slot_mapping int64 [T]."""
     _check_pool(codes, scales, "pool")
     _need(src, "src", torch.float32, 3)
@@ -149,9 +175,9 @@ def msa_nvfp4_quantize(src, slot_mapping, codes, scales):
         raise ValueError(f"src must be [T, {desc.num_heads}, 128], got {tuple(src.shape)}")
     if slot_mapping.shape[0] != src.shape[0]:
         raise ValueError("slot_mapping length must equal the number of tokens")
-    _check(lib().msa_nvfp4_quantize(ctypes.byref(desc), _ptr(src), _ptr(slot_mapping),
-                                    src.shape[0], _ptr(codes), _ptr(scales), _stream()),
-           "msa_nvfp4_quantize")
+    return _issue("msa_nvfp4_quantize", (
+        ctypes.byref(desc), _ptr(src), _ptr(slot_mapping), src.shape[0], _ptr(codes),
+        _ptr(scales), _stream()), prepare, keep=(desc,))
 
 
 def msa_indexer_workspace_bytes(num_seqs: int, q_per_seq: int, max_blocks: int) -> int:
@@ -175,7 +201,7 @@ def indexer_workspace(num_seqs, q_per_seq, max_blocks, device="cuda"):
 
 
 def msa_indexer_decode(idx_codes, idx_scales, q_fp8, head_w, block_table, seq_lens, q_per_seq,
-                       out_ids, workspace, out_scores=None, topk=TOPK):
+                       out_ids, workspace, out_scores=None, topk=TOPK, prepare=False):
     """Top-16 + recent block ids per query token into out_ids int32 [B*Q, 17]."""
     _check_pool(idx_codes, idx_scales, "idx")
     _need(q_fp8, "q_fp8", torch.uint8, 3)
@@ -196,10 +222,10 @@ def msa_indexer_decode(idx_codes, idx_scales, q_fp8, head_w, block_table, seq_le
     if out_scores is not None and out_scores.shape != out_ids.shape:
         raise ValueError("out_scores must match out_ids")
     desc = pool_desc(idx_codes)
-    _check(lib().msa_indexer_decode(
+    return _issue("msa_indexer_decode", (
         ctypes.byref(desc), _ptr(idx_codes), _ptr(idx_scales), _ptr(q_fp8), _ptr(head_w), hq,
         _ptr(block_table), max_blocks, _ptr(seq_lens), num_seqs, q_per_seq, topk, _ptr(out_ids),
-        _ptr(out_scores), _ptr(workspace), workspace.numel(), _stream()), "msa_indexer_decode")
+        _ptr(out_scores), _ptr(workspace), workspace.numel(), _stream()), prepare, keep=(desc,))
 
 
 def _check_indexer_inputs(q_fp8, head_w, block_table, seq_lens, q_per_seq):
@@ -218,7 +244,7 @@ def _check_indexer_inputs(q_fp8, head_w, block_table, seq_lens, q_per_seq):
 
 
 def msa_indexer_scan(idx_codes, idx_scales, q_fp8, head_w, block_table, seq_lens, q_per_seq,
-                     block_scores):
+                     block_scores, prepare=False):
     """Block scores B(j) into block_scores float32 [B*Q, max_blocks]."""
     _check_pool(idx_codes, idx_scales, "idx")
     num_seqs, max_blocks, tq, hq = _check_indexer_inputs(q_fp8, head_w, block_table, seq_lens,
@@ -227,13 +253,14 @@ def msa_indexer_scan(idx_codes, idx_scales, q_fp8, head_w, block_table, seq_lens
     if block_scores.shape != (tq, max_blocks):
         raise ValueError("block_scores must be [T_q, max_blocks]")
     desc = pool_desc(idx_codes)
-    _check(lib().msa_indexer_scan(
+    return _issue("msa_indexer_scan", (
         ctypes.byref(desc), _ptr(idx_codes), _ptr(idx_scales), _ptr(q_fp8), _ptr(head_w), hq,
         _ptr(block_table), max_blocks, _ptr(seq_lens), num_seqs, q_per_seq, _ptr(block_scores),
-        _stream()), "msa_indexer_scan")
+        _stream()), prepare, keep=(desc,))
 
 
-def msa_indexer_select(block_scores, seq_lens, q_per_seq, out_ids, out_scores=None, topk=TOPK):
+def msa_indexer_select(block_scores, seq_lens, q_per_seq, out_ids, out_scores=None, topk=TOPK,
+                       prepare=False):
     """Top-16 + recent block ids from block scores float32 [B*Q, max_blocks]."""
     _need(block_scores, "block_scores", torch.float32, 2)
     _need(seq_lens, "seq_lens", torch.int32, 1)
@@ -246,9 +273,9 @@ def msa_indexer_select(block_scores, seq_lens, q_per_seq, out_ids, out_scores=No
         raise ValueError("block_scores must be [num_seqs*q_per_seq, max_blocks], out_ids [T_q, 17]")
     if out_scores is not None and out_scores.shape != out_ids.shape:
         raise ValueError("out_scores must match out_ids")
-    _check(lib().msa_indexer_select(_ptr(block_scores), _ptr(seq_lens), max_blocks, num_seqs,
-                                    q_per_seq, topk, _ptr(out_ids), _ptr(out_scores), _stream()),
-           "msa_indexer_select")
+    return _issue("msa_indexer_select", (
+        _ptr(block_scores), _ptr(seq_lens), max_blocks, num_seqs, q_per_seq, topk, _ptr(out_ids),
+        _ptr(out_scores), _stream()), prepare)
 
 
 def _check_attn_inputs(k_codes, k_scales, v_codes, v_scales, q_fp8, block_table, seq_lens,
@@ -273,7 +300,7 @@ def _check_attn_inputs(k_codes, k_scales, v_codes, v_scales, q_fp8, block_table,
 
 
 def msa_sparse_attn_decode(k_codes, k_scales, v_codes, v_scales, q_fp8, block_table, seq_lens,
-                           q_per_seq, sel_ids, softmax_scale, out, workspace):
+                           q_per_seq, sel_ids, softmax_scale, out, workspace, prepare=False):
     """Attention over the selected blocks into out float32 [B*Q, Hq, 128]."""
     num_seqs, max_blocks, tq, hq = _check_attn_inputs(k_codes, k_scales, v_codes, v_scales, q_fp8,
                                                       block_table, seq_lens, q_per_seq, out,
@@ -282,16 +309,16 @@ def msa_sparse_attn_decode(k_codes, k_scales, v_codes, v_scales, q_fp8, block_ta
     if sel_ids.shape[0] != tq:
         raise ValueError("sel_ids must be [T_q, num_sel]")
     desc = pool_desc(k_codes)
-    _check(lib().msa_sparse_attn_decode(
+    return _issue("msa_sparse_attn_decode", (
         ctypes.byref(desc), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales),
         _ptr(q_fp8), hq, _ptr(block_table), max_blocks, _ptr(seq_lens), num_seqs, q_per_seq,
         _ptr(sel_ids), sel_ids.shape[1], float(softmax_scale), _ptr(out), _ptr(workspace),
-        workspace.numel(), _stream()), "msa_sparse_attn_decode")
+        workspace.numel(), _stream()), prepare, keep=(desc,))
 
 
 def msa_sparse_attn_select_decode(k_codes, k_scales, v_codes, v_scales, q_fp8, block_table,
                                   seq_lens, q_per_seq, block_scores, softmax_scale, out, workspace,
-                                  out_ids=None, topk=TOPK):
+                                  out_ids=None, topk=TOPK, prepare=False):
     """Selection from block scores [B*Q, max_blocks] and attention in one launch; the selected
     ids go to out_ids int32 [B*Q, 17] when given."""
     num_seqs, max_blocks, tq, hq = _check_attn_inputs(k_codes, k_scales, v_codes, v_scales, q_fp8,
@@ -305,8 +332,8 @@ def msa_sparse_attn_select_decode(k_codes, k_scales, v_codes, v_scales, q_fp8, b
         if out_ids.shape != (tq, topk + 1):
             raise ValueError("out_ids must be [T_q, topk + 1]")
     desc = pool_desc(k_codes)
-    _check(lib().msa_sparse_attn_select_decode(
+    return _issue("msa_sparse_attn_select_decode", (
         ctypes.byref(desc), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales),
         _ptr(q_fp8), hq, _ptr(block_table), max_blocks, _ptr(seq_lens), num_seqs, q_per_seq,
         _ptr(block_scores), topk, _ptr(out_ids), float(softmax_scale), _ptr(out),
-        _ptr(workspace), workspace.numel(), _stream()), "msa_sparse_attn_select_decode")
+        _ptr(workspace), workspace.numel(), _stream()), prepare, keep=(desc,))

@@ -283,11 +283,13 @@ static msa_status launch_scan(const msa_pool_desc* idx, const uint8_t* idx_codes
   a.q_per_seq = q_per_seq;
   a.bscore = block_scores;
   const int qg = (MSA_HEADS_PER_KV * q_per_seq + 15) / 16;
-  // blocks per workgroup: 4 (one stage) or 8 (two stages), halved while the
-  // grid would not cover the chip several times over
-  int bpw = qg == 1 ? 4 : 8;
-  const int64_t min_wgs = qg == 1 ? 4096 : 2048;
-  while (bpw > 1 && int64_t(num_seqs) * ((max_blocks + bpw - 1) / bpw) < min_wgs) bpw >>= 1;
+  // blocks per workgroup, halved while the grid would not cover the chip
+  // several times over. Measured with one query token: 3 is best for a few
+  // long sequences (8 x 256K), 8 for many sequences of mixed length (45
+  // requests, 30K..210K), where much of the grid bound is empty; the grid
+  // bound num_seqs x max_blocks is what the host knows.
+  int bpw = (qg == 1 && int64_t(num_seqs) * max_blocks <= 32768) ? 3 : 8;
+  while (bpw > 1 && int64_t(num_seqs) * ((max_blocks + bpw - 1) / bpw) < 2048) bpw >>= 1;
   a.blocks_per_wg = bpw;
   const dim3 grid((max_blocks + bpw - 1) / bpw, num_seqs);
   const dim3 block(64 * idx->num_heads);

@@ -306,6 +306,36 @@ def test_fused_select_attention_without_ids_and_invalid_rows(nb):
     assert np.all(np.isfinite(on))
 
 
+def test_prepared_calls_match_direct(nb):
+    say("prepared calls (arguments marshalled once) re-issue the same launches")
+    wl = tiny_config([2600, 900], 1, seed=41)
+    pools = S.fill_pools(wl, nb)
+    inp = S.device_inputs(wl)
+    ref = _to_np(S.run_step(nb, wl, pools, inp))
+    ic, isc = pools[synth.STREAM_IDX]
+    kc, ks = pools[synth.STREAM_K]
+    vc, vs = pools[synth.STREAM_V]
+    tq = wl.num_q_tokens
+    bscores = torch.empty((tq, wl.max_blocks), dtype=torch.float32, device="cuda")
+    ws = nb.attn_workspace(wl.num_seqs, wl.q_per_seq, wl.num_q_heads, 17)
+    o = torch.empty((tq, wl.num_q_heads, 128), dtype=torch.float32, device="cuda")
+    ids = torch.empty((tq, 17), dtype=torch.int32, device="cuda")
+    scan = nb.msa_indexer_scan(ic, isc, inp["q_idx"], inp["w"], inp["block_table"],
+                               inp["seq_lens"], wl.q_per_seq, bscores, prepare=True)
+    attend = nb.msa_sparse_attn_select_decode(kc, ks, vc, vs, inp["q_attn"], inp["block_table"],
+                                              inp["seq_lens"], wl.q_per_seq, bscores,
+                                              1.0 / math.sqrt(128), o, ws, out_ids=ids,
+                                              prepare=True)
+    for rep in range(3):
+        o.fill_(float(rep))
+        ids.fill_(-5)
+        scan()
+        attend()
+        torch.cuda.synchronize()
+        assert np.array_equal(ids.cpu().numpy(), ref[0]), rep
+        assert np.array_equal(o.cpu().numpy(), ref[2]), rep
+
+
 def test_graph_replay_matches_eager(nb):
     say("decode step captured in a HIP graph, replayed between eager work")
     wl = tiny_config([3000, 2400, 700], 2, seed=31)
