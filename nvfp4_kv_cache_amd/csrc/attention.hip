@@ -1,6 +1,8 @@
-// attention.hip -- msa_sparse_attn_decode: exact GQA attention of each query
-// token over the visible tokens of its selected blocks, with the NVFP4 K and
-// V pages converted to FP8 through the lookup table before the products.
+// attention.hip -- msa_sparse_attn_decode and msa_sparse_attn_select_decode:
+// exact GQA attention of each query token over the visible tokens of its
+// selected blocks, with the NVFP4 K and V pages converted to FP8 through the
+// lookup table before the products; the second entry point first selects the
+// blocks itself from the indexer's block scores (topk_select.h).
 //
 // The pages: main attention runs over the roughly 2,048 keys of the selected
 // blocks, exactly (MiniMax-M3.1-Flash serving summary, section "Sparse
@@ -16,17 +18,19 @@
 //   1. dequantises the 8 K tiles into FP8 MFMA operands and computes
 //      S = Q K^T with v_mfma_f32_16x16x128_f8f6f4 (A = the 8 query heads of
 //      this KV head, rows 8..15 zero; B = 16 tokens x 128 channels);
-//   2. dequantises V into LDS as FP8, one 136-byte row per token;
+//   2. dequantises V into LDS as FP8, one 136-byte row per token, channels
+//      in the dequantiser's order (the output index undoes it);
 //   3. runs the softmax in base 2 in fp32, scales P by 2^8 and splits it into
 //      two FP8 terms, P_hi = FP8(256 p) and P_lo = FP8(16 (256 p - P_hi)), so
-//      P_hi + P_lo / 16 carries about 8 significant bits; the denominator sums
-//      the same two terms, so numerator and denominator agree;
+//      P_hi + P_lo / 16 carries about 8 significant bits;
 //   4. computes O += P_hi V + 2^-4 P_lo V with the same MFMA (the second with
 //      its E8M0 operand scale set to 2^-4): all operands are read
 //      transposed from LDS with ds_read_b64_tr_b8 (within each 16-lane group,
 //      lane i receives byte i%8 of the 8-byte segments addressed by lanes
 //      i/8, i/8 + 2, ..., i/8 + 14), so lane i ends with 8 consecutive tokens
-//      of one head (P) or one channel (V).
+//      of one head (P) or one channel (V). The softmax denominator is the
+//      same product against FP8 ones, so it sums exactly the terms the
+//      numerator uses.
 #include "msa_nvfp4.h"
 #include "nvfp4_tile.h"
 #include "topk_select.h"
