@@ -181,10 +181,47 @@ __global__ __launch_bounds__(512) void indexer_kernel(const IndexerArgs a) {
   };
 
   if constexpr (STAGES == 1) {
+    static_assert(QG == 1, "the one-stage loop reduces at most two query-token rows");
+    // The block reduction is spread over the waves: lane = qi * 32 + t%32,
+    // wave w sums the heads of tokens 32w + 32Hk + t%32 and leaves its
+    // maximum per query token in LDS; wave 0 combines the H maxima one
+    // barrier later.
+    __shared__ float wmax[2][2][MSA_MAX_HEADS];  // [buffer][query token][wave]
+    auto reduce_part = [&](int k, int buf) {
+      const int blk = first + k * G;
+      const int qi = lane >> 5;
+      const int pos = L - Q + qi;
+      float m = 0.0f;
+      if (qi < Q) {
+        const float* pq = part + buf * part_stride + qi * 2 * kBlockTokens;
+        for (int t = 32 * wave + (lane & 31); t < kBlockTokens; t += 32 * H) {
+          float sum = 0.0f;
+          for (int h = 0; h < H; ++h)
+            sum += pq[h * QR * 2 * kBlockTokens + t] + pq[h * QR * 2 * kBlockTokens + kBlockTokens + t];
+          if (blk * kBlockTokens + t <= pos) m = fmaxf(m, sum);
+        }
+      }
+      // m >= 0: maxima of the bit patterns, per 32-lane half
+      uint32_t v = row16_max_u32(__float_as_uint(m));
+      const uint32_t r0 = __builtin_amdgcn_readlane(int(v), 15), r1 = __builtin_amdgcn_readlane(int(v), 31);
+      const uint32_t r2 = __builtin_amdgcn_readlane(int(v), 47), r3 = __builtin_amdgcn_readlane(int(v), 63);
+      if (lane == 0) {
+        wmax[buf][0][wave] = __uint_as_float(max(r0, r1));
+        wmax[buf][1][wave] = __uint_as_float(max(r2, r3));
+      }
+    };
+    auto finish = [&](int k, int buf) {
+      const int blk = first + k * G;
+      if (wave == 0 && lane < Q && blk * kBlockTokens <= L - Q + lane) {
+        float m = 0.0f;
+        for (int w = 0; w < H; ++w) m = fmaxf(m, wmax[buf][lane][w]);
+        a.bscore[(qrow0 + lane) * a.max_blocks + blk] = pages[k] >= 0 ? m : 0.0f;
+      }
+    };
     // one register buffer: the next block's loads are issued as soon as the
     // current block's codes are consumed, so their latency overlaps the
-    // barrier and the block reduction (the scheduling barriers keep the
-    // compiler from hoisting them into a second buffer)
+    // barrier and the reduction (the scheduling barriers keep the compiler
+    // from hoisting them into a second buffer)
     TileLoads t;
     if (count > 0) issue_loads(t, codes_h, scales_h, pages[0], page_codes, page_scales);
     for (int k = 0; k < count; ++k) {
@@ -193,7 +230,12 @@ __global__ __launch_bounds__(512) void indexer_kernel(const IndexerArgs a) {
       if (k + 1 < count) issue_loads(t, codes_h, scales_h, pages[k + 1], page_codes, page_scales);
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
-      reduce(k, k & 1);
+      if (k > 0) finish(k - 1, (k - 1) & 1);
+      reduce_part(k, k & 1);
+    }
+    if (count > 0) {
+      __syncthreads();
+      finish(count - 1, (count - 1) & 1);
     }
     return;
   }

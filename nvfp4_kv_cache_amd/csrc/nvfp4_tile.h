@@ -183,11 +183,16 @@ __device__ __forceinline__ uint4 load_stream16(const void* p) {
 // read 0, the identity), then the four row results through lane reads. No
 // LDS round trips, unlike a shuffle butterfly. Non-negative floats can use it
 // on their bit patterns.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+// Prefix maximum inside each row of 16 lanes (lane 15 of a row ends with
+// the row's maximum).
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
   v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x111, 0xF, 0xF, true)));  // row_shr:1
   v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x112, 0xF, 0xF, true)));  // row_shr:2
   v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x114, 0xF, 0xF, true)));  // row_shr:4
-  v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x118, 0xF, 0xF, true)));  // row_shr:8
+  return max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x118, 0xF, 0xF, true)));  // row_shr:8
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = row16_max_u32(v);
   const uint32_t r0 = __builtin_amdgcn_readlane(int(v), 15), r1 = __builtin_amdgcn_readlane(int(v), 31);
   const uint32_t r2 = __builtin_amdgcn_readlane(int(v), 47), r3 = __builtin_amdgcn_readlane(int(v), 63);
   return max(max(r0, r1), max(r2, r3));

@@ -135,6 +135,26 @@ def test_tiny_parity(nb, lens, q, fused):
     assert not fails, "\n".join(fails[:20])
 
 
+@pytest.mark.parametrize("heads", [1, 2, 8])
+def test_head_counts(nb, heads):
+    # every kernel takes the number of index-key / KV heads at run time (1..8,
+    # 8 query heads each); the scan uses one wavefront per head
+    say(f"{heads} index / KV heads, {8 * heads} query heads")
+    wl = tiny_config([2400, 700, 17 * 128 + 1], 2, seed=50 + heads)
+    wl.num_kv_heads = wl.num_idx_heads = heads
+    wl.num_q_heads = 8 * heads
+    pools = S.fill_pools(wl, nb)
+    inp = S.device_inputs(wl)
+    ids, sc, o = _to_np(S.run_step(nb, wl, pools, inp))
+    ids2, sc2, o2 = _to_np(S.run_step(nb, wl, pools, inp, fused=False))
+    assert np.array_equal(ids, ids2) and np.array_equal(o, o2)
+    _structural(wl, ids)
+    fails = S.check_page_bytes(wl, pools, wl.pages_in_use()[:6])
+    for b in range(wl.num_seqs):
+        fails += S.check_sequence(wl, b, ids, sc, o)
+    assert not fails, "\n".join(fails[:20])
+
+
 def test_outlier_channels_parity(nb):
     say("tiny parity with 5% outlier channels")
     wl = tiny_config([3000, 4100], 1, seed=5, outliers=True)
