@@ -57,30 +57,46 @@ struct TileLoads {
   uint4 s;
 };
 
-__device__ __forceinline__ void issue_loads(TileLoads& t, const uint8_t* codes_h,
-                                            const uint8_t* scales_h, int page, int64_t page_codes,
-                                            int64_t page_scales) {
-  if (page >= 0) {
-    const uint8_t* cp = codes_h + int64_t(page) * page_codes;
-    const uint8_t* sp = scales_h + int64_t(page) * page_scales;
+// A buffer descriptor over `bytes` bytes at `base` (gfx9 layout: stride 0,
+// default format word). A buffer load past the record count returns zeros
+// and reads no memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, bytes, 0x00020000);
+}
+
+constexpr int kLoadNonTemporal = 2;  // buffer-load cache policy: streamed, not kept
+
+__device__ __forceinline__ uint4 load_tile16(__amdgpu_buffer_rsrc_t r, uint32_t lane_off, int uniform_off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, uniform_off, kLoadNonTemporal);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// This wave's loads of one block. `live` (uniform) false stands for an
+// absent block (past the workgroup's count, or an unmapped page): the
+// descriptors then hold no records, every lane receives zeros and nothing is
+// read. There is no branch, so the wait the compiler places before a block's
+// first use covers that block's loads only, not the next block's issued
+// after them.
+__device__ __forceinline__ void issue_loads(TileLoads& t, const uint8_t* codes_w,
+                                            const uint8_t* scales_w, int page, bool live,
+                                            int64_t page_codes, int64_t page_scales,
+                                            uint32_t code_lane, uint32_t scale_lane) {
+  const int64_t p = live ? page : 0;
+  const auto cr = tile_rsrc(codes_w + p * page_codes, live ? kCodePage : 0);
+  const auto sr = tile_rsrc(scales_w + p * page_scales, live ? kScalePage : 0);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) t.c[j] = load_stream16(cp + j * 16 * kCodeRow);
-    t.s = load_stream16(sp);
-  } else {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) t.c[j] = make_uint4(0, 0, 0, 0);
-    t.s = make_uint4(0, 0, 0, 0);
-  }
+  for (int j = 0; j < 8; ++j) t.c[j] = load_tile16(cr, code_lane, j * 16 * kCodeRow);
+  t.s = load_tile16(sr, scale_lane, 0);
 }
 
 // QG: 16-row MFMA groups per index head = ceil(8 * q_per_seq / 16).
-// STAGES: blocks in flight per wave. With QG = 1 the kernel is bound by HBM
-// and more resident waves hide the latency better than a second register
-// buffer (measured ~3% faster); with QG >= 2 the MFMA epilogue is long
-// enough that the next block's loads must overlap it.
-template <int QG, int STAGES>
+// One block in flight per wave: the next block's loads are issued as soon as
+// the current block's codes are consumed, and more resident waves hide the
+// latency better than a second register buffer would (measured with 1 and 8
+// query tokens).
+template <int QG>
 __global__ __launch_bounds__(512) void indexer_kernel(const IndexerArgs a) {
-  extern __shared__ float part[];  // [2][H][2*QG][2][128] partial token scores per head group half
+  extern __shared__ float part[];  // [2][H][2*QG][128] partial token scores per index head
   __shared__ uint2 lut[128];
   __shared__ int pages[kMaxBlocksPerWg];
 
@@ -134,125 +150,114 @@ __global__ __launch_bounds__(512) void indexer_kernel(const IndexerArgs a) {
 
   const int64_t page_codes = int64_t(H) * kCodePage;
   const int64_t page_scales = int64_t(H) * kScalePage;
-  const uint8_t* codes_h = a.codes + int64_t(wave) * kCodePage + (lane & 15) * kCodeRow + slice * 16;
-  const uint8_t* scales_h = a.scales + int64_t(wave) * kScalePage + scale_word_offset(slice, lane & 15);
-  const int part_stride = H * QR * 2 * kBlockTokens;
-  // lane l holds query token 2rg + l/32, heads 4*((l/16)&1) .. +3 of the
-  // group, token 16j + l%16: each lane writes its own partial
-  const int part_lane = ((lane >> 5) * 2 + ((lane >> 4) & 1)) * kBlockTokens + (lane & 15);
+  // this wave's head within a page (uniform), and the lane's offsets in a tile
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint8_t* codes_w = a.codes + int64_t(wave_u) * kCodePage;
+  const uint8_t* scales_w = a.scales + int64_t(wave_u) * kScalePage;
+  const uint32_t code_lane = (lane & 15) * kCodeRow + slice * 16;
+  const uint32_t scale_lane = scale_word_offset(slice, lane & 15);
+  const int count_u = __builtin_amdgcn_readfirstlane(count);
+  auto issue = [&](TileLoads& t, int k) {
+    const int page = __builtin_amdgcn_readfirstlane(pages[min(k, kMaxBlocksPerWg - 1)]);
+    issue_loads(t, codes_w, scales_w, page, k < count_u && page >= 0, page_codes, page_scales,
+                code_lane, scale_lane);
+  };
+  const int part_stride = H * QR * kBlockTokens;
+  // an MFMA result lane l holds query token 2rg + l/32, heads
+  // 4*((l/16)&1) .. +3 of the index head's 8, token 16j + l%16; lanes l and
+  // l^16 swap halves so that each writes the 8-head sum of one token,
+  // 32i + l%32, for the pair j = 2i, 2i+1
+  const int part_lane = (lane >> 5) * kBlockTokens + (lane & 31);
 
   // dequantise, multiply, apply ReLU and weights; per-head partials to LDS
   auto compute = [&](const TileLoads& t, int buf) {
-    float* pw = part + buf * part_stride + wave * QR * 2 * kBlockTokens + part_lane;
+    float* pw = part + buf * part_stride + wave * QR * kBlockTokens + part_lane;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t sj = tile_scales(t.s, j);
-      const v8i kop = dequant32(t.c[j], lut[sj & 0x7F], lut[(sj >> 8) & 0x7F]);
+    for (int i = 0; i < 4; ++i) {
+      float s2[2][QG];
 #pragma unroll
-      for (int rg = 0; rg < QG; ++rg) {
-        const v4f acc = mfma_fp8_16x16x128(qop[rg], kop, v4f{0.0f, 0.0f, 0.0f, 0.0f});
-        float s = wv[rg][0] * fmaxf(acc[0], 0.0f);
-        s += wv[rg][1] * fmaxf(acc[1], 0.0f);
-        s += wv[rg][2] * fmaxf(acc[2], 0.0f);
-        s += wv[rg][3] * fmaxf(acc[3], 0.0f);
-        pw[2 * rg * 2 * kBlockTokens + 16 * j] = s;
-      }
-    }
-  };
-  // sum the heads, maximise over the block's visible tokens, store B(blk)
-  auto reduce = [&](int k, int buf) {
-    const bool page_ok = pages[k] >= 0;
-    const int blk = first + k * G;
-    for (int qi = wave; qi < Q; qi += H) {
-      const int pos = L - Q + qi;
-      if (blk * kBlockTokens > pos) continue;  // block not visible to this query token
-      const float* pq = part + buf * part_stride + qi * 2 * kBlockTokens;
-      float m = 0.0f;
+      for (int e = 0; e < 2; ++e) {
+        const uint32_t sj = tile_scales(t.s, 2 * i + e);
+        const v8i kop = dequant32(t.c[2 * i + e], lut[sj & 0x7F], lut[(sj >> 8) & 0x7F]);
 #pragma unroll
-      for (int t = lane; t < kBlockTokens; t += 64) {
-        float s = 0.0f;
-        for (int h = 0; h < H; ++h)
-          s += pq[h * QR * 2 * kBlockTokens + t] + pq[h * QR * 2 * kBlockTokens + kBlockTokens + t];
-        if (blk * kBlockTokens + t <= pos) m = fmaxf(m, s);
-      }
-      m = __uint_as_float(wave_max_u32(__float_as_uint(m)));  // m >= 0
-      if (lane == 0) a.bscore[(qrow0 + qi) * a.max_blocks + blk] = page_ok ? m : 0.0f;
-    }
-  };
-
-  if constexpr (STAGES == 1) {
-    static_assert(QG == 1, "the one-stage loop reduces at most two query-token rows");
-    // The block reduction is spread over the waves: lane = qi * 32 + t%32,
-    // wave w sums the heads of tokens 32w + 32Hk + t%32 and leaves its
-    // maximum per query token in LDS; wave 0 combines the H maxima one
-    // barrier later.
-    __shared__ float wmax[2][2][MSA_MAX_HEADS];  // [buffer][query token][wave]
-    auto reduce_part = [&](int k, int buf) {
-      const int blk = first + k * G;
-      const int qi = lane >> 5;
-      const int pos = L - Q + qi;
-      float m = 0.0f;
-      if (qi < Q) {
-        const float* pq = part + buf * part_stride + qi * 2 * kBlockTokens;
-        for (int t = 32 * wave + (lane & 31); t < kBlockTokens; t += 32 * H) {
-          float sum = 0.0f;
-          for (int h = 0; h < H; ++h)
-            sum += pq[h * QR * 2 * kBlockTokens + t] + pq[h * QR * 2 * kBlockTokens + kBlockTokens + t];
-          if (blk * kBlockTokens + t <= pos) m = fmaxf(m, sum);
+        for (int rg = 0; rg < QG; ++rg) {
+          const v4f acc = mfma_fp8_16x16x128(qop[rg], kop, v4f{0.0f, 0.0f, 0.0f, 0.0f});
+          float s = wv[rg][0] * fmaxf(acc[0], 0.0f);
+          s += wv[rg][1] * fmaxf(acc[1], 0.0f);
+          s += wv[rg][2] * fmaxf(acc[2], 0.0f);
+          s += wv[rg][3] * fmaxf(acc[3], 0.0f);
+          s2[e][rg] = s;
         }
       }
+#pragma unroll
+      for (int rg = 0; rg < QG; ++rg) {
+        // v_permlane16_swap: the odd rows of the first operand trade places
+        // with the even rows of the second, so an even-row lane ends with
+        // its own j = 2i partial and its partner's, an odd-row lane with
+        // both j = 2i+1 partials (heads 0-3 first, as in the unpaired sum)
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(s2[0][rg]),
+                                                         __float_as_uint(s2[1][rg]), false, false);
+        pw[2 * rg * kBlockTokens + 32 * i] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // Sum the heads, maximise over the block's visible tokens, store the block
+  // score. The reduction is spread over the waves in units of (query-token
+  // pair p, 32-token chunk c), lane = (query token - 2p) * 32 + t % 32:
+  // wave w takes units w, w + H, ..., sums the heads of each token and
+  // leaves the unit's maximum per query token in LDS; wave 0 combines the
+  // four chunk maxima one barrier later.
+  __shared__ float wmax[2][MSA_MAX_Q_PER_SEQ][4];  // [buffer][query token][chunk]
+  const int units = 4 * ((Q + 1) >> 1);
+  auto reduce_part = [&](int k, int buf) {
+    const int blk = first + k * G;
+    for (int u = wave_u; u < units; u += H) {
+      const int qi = 2 * (u >> 2) + (lane >> 5);
+      const int t = 32 * (u & 3) + (lane & 31);
+      float m = 0.0f;
+      if (qi < Q && blk * kBlockTokens + t <= L - Q + qi) {
+        const float* pt = part + buf * part_stride + qi * kBlockTokens + t;
+        float sum = 0.0f;
+        for (int h = 0; h < H; ++h) sum += pt[h * QR * kBlockTokens];
+        m = fmaxf(m, sum);
+      }
       // m >= 0: maxima of the bit patterns, per 32-lane half
-      uint32_t v = row16_max_u32(__float_as_uint(m));
+      const uint32_t v = row16_max_u32(__float_as_uint(m));
       const uint32_t r0 = __builtin_amdgcn_readlane(int(v), 15), r1 = __builtin_amdgcn_readlane(int(v), 31);
       const uint32_t r2 = __builtin_amdgcn_readlane(int(v), 47), r3 = __builtin_amdgcn_readlane(int(v), 63);
       if (lane == 0) {
-        wmax[buf][0][wave] = __uint_as_float(max(r0, r1));
-        wmax[buf][1][wave] = __uint_as_float(max(r2, r3));
+        wmax[buf][2 * (u >> 2)][u & 3] = __uint_as_float(max(r0, r1));
+        wmax[buf][2 * (u >> 2) + 1][u & 3] = __uint_as_float(max(r2, r3));
       }
-    };
-    auto finish = [&](int k, int buf) {
-      const int blk = first + k * G;
-      if (wave == 0 && lane < Q && blk * kBlockTokens <= L - Q + lane) {
-        float m = 0.0f;
-        for (int w = 0; w < H; ++w) m = fmaxf(m, wmax[buf][lane][w]);
-        a.bscore[(qrow0 + lane) * a.max_blocks + blk] = pages[k] >= 0 ? m : 0.0f;
-      }
-    };
-    // one register buffer: the next block's loads are issued as soon as the
-    // current block's codes are consumed, so their latency overlaps the
-    // barrier and the reduction (the scheduling barriers keep the compiler
-    // from hoisting them into a second buffer)
-    TileLoads t;
-    if (count > 0) issue_loads(t, codes_h, scales_h, pages[0], page_codes, page_scales);
-    for (int k = 0; k < count; ++k) {
-      compute(t, k & 1);
-      __builtin_amdgcn_sched_barrier(0);
-      if (k + 1 < count) issue_loads(t, codes_h, scales_h, pages[k + 1], page_codes, page_scales);
-      __builtin_amdgcn_sched_barrier(0);
-      __syncthreads();
-      if (k > 0) finish(k - 1, (k - 1) & 1);
-      reduce_part(k, k & 1);
     }
-    if (count > 0) {
-      __syncthreads();
-      finish(count - 1, (count - 1) & 1);
+  };
+  auto finish = [&](int k, int buf) {
+    const int blk = first + k * G;
+    if (wave == 0 && lane < Q && blk * kBlockTokens <= L - Q + lane) {
+      const float* w4 = wmax[buf][lane];
+      const float m = fmaxf(fmaxf(w4[0], w4[1]), fmaxf(w4[2], w4[3]));
+      a.bscore[(qrow0 + lane) * a.max_blocks + blk] = pages[k] >= 0 ? m : 0.0f;
     }
-    return;
+  };
+  // one register buffer: the next block's loads are issued as soon as the
+  // current block's codes are consumed, so their latency overlaps the
+  // barrier and the reduction (the scheduling barriers keep the compiler
+  // from hoisting them into a second buffer)
+  TileLoads t;
+  issue(t, 0);
+  for (int k = 0; k < count_u; ++k) {
+    compute(t, k & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(t, k + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    if (k > 0) finish(k - 1, (k - 1) & 1);
+    reduce_part(k, k & 1);
   }
-  // two-stage pipeline: the next block's loads are in flight while the
-  // current block is computed
-  TileLoads ta, tb;
-  if (count > 0) issue_loads(ta, codes_h, scales_h, pages[0], page_codes, page_scales);
-  for (int k = 0; k < count; k += 2) {
-    if (k + 1 < count) issue_loads(tb, codes_h, scales_h, pages[k + 1], page_codes, page_scales);
-    compute(ta, 0);
+  if (count_u > 0) {
     __syncthreads();
-    reduce(k, 0);
-    if (k + 1 >= count) break;
-    if (k + 2 < count) issue_loads(ta, codes_h, scales_h, pages[k + 2], page_codes, page_scales);
-    compute(tb, 1);
-    __syncthreads();
-    reduce(k + 1, 1);
+    finish(count_u - 1, (count_u - 1) & 1);
   }
 }
 
@@ -336,13 +341,13 @@ static msa_status launch_scan(const msa_pool_desc* idx, const uint8_t* idx_codes
   const dim3 grid((max_blocks + bpw - 1) / bpw, num_seqs);
   const dim3 block(64 * idx->num_heads);
   const int qg_pow2 = qg == 1 ? 1 : (qg == 2 ? 2 : 4);
-  const size_t lds = size_t(2) * idx->num_heads * (2 * qg_pow2) * 2 * MSA_BLOCK_TOKENS * sizeof(float);
+  const size_t lds = size_t(2) * idx->num_heads * (2 * qg_pow2) * MSA_BLOCK_TOKENS * sizeof(float);
   if (qg_pow2 == 1)
-    hipLaunchKernelGGL((indexer_kernel<1, 1>), grid, block, lds, s, a);
+    hipLaunchKernelGGL((indexer_kernel<1>), grid, block, lds, s, a);
   else if (qg_pow2 == 2)
-    hipLaunchKernelGGL((indexer_kernel<2, 2>), grid, block, lds, s, a);
+    hipLaunchKernelGGL((indexer_kernel<2>), grid, block, lds, s, a);
   else
-    hipLaunchKernelGGL((indexer_kernel<4, 2>), grid, block, lds, s, a);
+    hipLaunchKernelGGL((indexer_kernel<4>), grid, block, lds, s, a);
   return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
 }
 

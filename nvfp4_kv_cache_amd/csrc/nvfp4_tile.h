@@ -191,12 +191,6 @@ __device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
   v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x114, 0xF, 0xF, true)));  // row_shr:4
   return max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x118, 0xF, 0xF, true)));  // row_shr:8
 }
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = row16_max_u32(v);
-  const uint32_t r0 = __builtin_amdgcn_readlane(int(v), 15), r1 = __builtin_amdgcn_readlane(int(v), 31);
-  const uint32_t r2 = __builtin_amdgcn_readlane(int(v), 47), r3 = __builtin_amdgcn_readlane(int(v), 63);
-  return max(max(r0, r1), max(r2, r3));
-}
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
