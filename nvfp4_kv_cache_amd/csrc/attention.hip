@@ -56,7 +56,7 @@ struct AttnArgs {
   const float* bscore;     // block scores [T_q][max_blocks] to select from
   int32_t* out_ids;        // selection output [T_q][17] (optional, selecting kernel)
   int num_sel;
-  int slots_per_wave;  // R
+  int slots_per_wg;    // selected slots per workgroup
   int num_splits;
   float scale_log2;    // softmax_scale * log2(e)
   float* part_o;       // [T_q * Hq][num_splits][128] unnormalised, when num_splits > 1
@@ -68,10 +68,16 @@ typedef float v2f __attribute__((ext_vector_type(2)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v2i lds_v2i;
 
+constexpr int kAttnWaves = 4;                         // wavefronts per workgroup
 constexpr int kVRow = 136;                            // LDS bytes per V row (128 + pad)
-constexpr int kVBytes = kBlockTokens * kVRow;         // 17,408
-constexpr int kPBytes = kBlockTokens * kHeadsPerKv;   // 1,024: P as [token][head] FP8
-constexpr int kWaveLds = kVBytes + 2 * kPBytes;       // per wavefront: V, P_hi, P_lo
+// LDS of one wavefront that takes TOK tokens of a block: V rows, then P_hi
+// and P_lo as [token][head] FP8
+template <int TOK>
+struct WaveLds {
+  static constexpr int kV = TOK * kVRow;
+  static constexpr int kP = TOK * kHeadsPerKv;
+  static constexpr int kBytes = kV + 2 * kP;
+};
 constexpr float kPScale = 256.0f;                     // P_hi = FP8(256 p)
 constexpr float kPLoScale = 16.0f;                    // P_lo = FP8(16 (256 p - P_hi))
 constexpr int kE8M0One = 0x7F7F7F7F;                  // MFMA operand scale 2^0
@@ -102,6 +108,33 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v + dpp_row<kRowRor8>(v);
 }
 
+// The scale bytes of a wavefront's NT tiles from the lane's 16-byte scale
+// word (tile-major: tile j's two bytes at bytes 2j, 2j+1): the whole word
+// for a whole block, one dword (tiles first, first + 1) for a quarter.
+template <int NT>
+struct TileScaleWords {
+  uint32_t d[NT / 2];
+};
+template <int NT>
+__device__ __forceinline__ TileScaleWords<NT> load_tile_scales(const uint8_t* word, int first) {
+  TileScaleWords<NT> r;
+  if constexpr (NT == 8) {
+    const uint4 w = load_stream16(word);
+    r.d[0] = w.x;
+    r.d[1] = w.y;
+    r.d[2] = w.z;
+    r.d[3] = w.w;
+  } else {
+    static_assert(NT == 2, "whole blocks or quarters");
+    r.d[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(word + 2 * first));
+  }
+  return r;
+}
+template <int NT>
+__device__ __forceinline__ uint32_t scale_pair(const TileScaleWords<NT>& w, int j) {
+  return (j & 1) ? (w.d[j >> 1] >> 16) : (w.d[j >> 1] & 0xFFFFu);
+}
+
 // 32 bytes of an MFMA operand from four transposed 8-byte LDS reads.
 __device__ __forceinline__ v8i tr_operand(const uint8_t* p0, const uint8_t* p1, const uint8_t* p2,
                                           const uint8_t* p3) {
@@ -112,26 +145,42 @@ __device__ __forceinline__ v8i tr_operand(const uint8_t* p0, const uint8_t* p1, 
   return v8i{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
+// TOK: tokens of a block per wavefront. TOK = 128: each wavefront takes
+// whole blocks (slots s, s + 4, ... of its workgroup's range) and runs the
+// selection itself (no barrier). TOK = 32: the four wavefronts share every
+// block of the workgroup's range, wave w taking tokens 32w .. 32w + 31, which
+// cuts the serial work per wavefront for launches with few (query token, KV
+// head) pairs; wave 0 selects and hands the slots over through LDS.
 // SELECT: the kernel selects the blocks itself from the indexer's block
-// scores (every wavefront runs the same selection, so no barrier is needed);
-// otherwise the caller's ids are used.
-template <int W, bool SELECT>
-__global__ __launch_bounds__(64 * W) void sparse_attn_kernel(const AttnArgs a) {
+// scores; otherwise the caller's ids are used.
+template <int TOK, bool SELECT>
+__global__ __launch_bounds__(64 * kAttnWaves)
+__attribute__((amdgpu_waves_per_eu(TOK < kBlockTokens ? 3 : 1))) void sparse_attn_kernel(const AttnArgs a) {
+  constexpr int W = kAttnWaves;
   static_assert(W == 4, "the workgroup merge maps 256 threads onto 8 heads x 32 channel quads");
+  constexpr bool kShared = TOK < kBlockTokens;  // the waves share each block
+  static_assert(TOK == kBlockTokens || TOK * W == kBlockTokens, "a block is one wave's or all four's");
+  constexpr int NT = TOK / 16;  // 16-token tiles per wavefront
+  using WL = WaveLds<TOK>;
+  static_assert(sizeof(SelectScratch) <= size_t(kShared ? W : 1) * WL::kBytes,
+                "the selection's scratch lives in the V rows");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // W x (V rows, P) + zeros
   __shared__ uint2 lut[128];
+  __shared__ int slot_blk[kShared ? 64 : 1], slot_page[kShared ? 64 : 1];
 
   const int sp = blockIdx.x, kh = blockIdx.y, qt = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int slice = lane >> 4;  // 32-channel slice (QK) / 32-token group (PV)
   const int li = lane & 15;     // row of A / column of B inside a 16-lane group
   const int Q = a.q_per_seq;
   const int b = qt / Q, qi = qt - b * Q;
   const int Hq = a.num_q_heads;
-  uint8_t* vrows = smem + wave * kWaveLds;
-  uint8_t* prows = vrows + kVBytes;        // P_hi [token][head]
-  uint8_t* plows = prows + kPBytes;        // P_lo [token][head]
-  const uint8_t* zeros = smem + W * kWaveLds;
+  const bool selector = !kShared || wave_u == 0;  // this wavefront runs the selection
+  uint8_t* vrows = smem + wave * WL::kBytes;
+  uint8_t* prows = vrows + WL::kV;         // P_hi [token][head]
+  uint8_t* plows = prows + WL::kP;         // P_lo [token][head]
+  const uint8_t* zeros = smem + W * WL::kBytes;
 
   // Loads in flight first, oldest first: the query operand (unconditional,
   // rows 8..15 masked afterwards), then this query token's block scores or
@@ -145,7 +194,7 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(const AttnArgs a) {
   float x0[kSelPerLane];
   int sel = -1;
   if constexpr (SELECT) {
-    load_score_chunk(a.bscore + int64_t(qt) * a.max_blocks, a.max_blocks, 0, lane, x0);
+    if (selector) load_score_chunk(a.bscore + int64_t(qt) * a.max_blocks, a.max_blocks, 0, lane, x0);
   } else {
     if (lane < a.num_sel) sel = a.sel_ids[int64_t(qt) * a.num_sel + lane];
   }
@@ -154,7 +203,7 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(const AttnArgs a) {
   const int pos = L - Q + qi;
 
   for (int i = tid; i < 128; i += 64 * W) lut[i] = make_uint2(kAttnLut.lo[i], kAttnLut.hi[i]);
-  if (tid < 16) reinterpret_cast<uint32_t*>(smem + W * kWaveLds)[tid] = 0u;
+  if (tid < 16) reinterpret_cast<uint32_t*>(smem + W * WL::kBytes)[tid] = 0u;
   // query operand: rows 0..7 = the 8 query heads of this KV head. Consuming
   // the loads here (before anything waits for the later ones) keeps the
   // compiler from sinking them past the selection.
@@ -167,16 +216,22 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(const AttnArgs a) {
   // wavefront runs the same selection (no barrier, scratch in its own LDS).
   int pg = -1;
   if constexpr (SELECT) {
-    if (seq_ok) {
-      float score;
-      int page;
-      sel = select_blocks(a.bscore + int64_t(qt) * a.max_blocks, a.max_blocks,
-                          pos / kBlockTokens + 1, x0, *reinterpret_cast<SelectScratch*>(vrows),
-                          lane, &score, a.block_table + int64_t(b) * a.max_blocks, &page);
-      pg = (sel >= 0 && page >= 0 && page < a.num_pages) ? page : -1;
+    if (selector) {
+      if (seq_ok) {
+        float score;
+        int page;
+        sel = select_blocks(a.bscore + int64_t(qt) * a.max_blocks, a.max_blocks,
+                            pos / kBlockTokens + 1, x0, *reinterpret_cast<SelectScratch*>(vrows),
+                            lane, &score, a.block_table + int64_t(b) * a.max_blocks, &page);
+        pg = (sel >= 0 && page >= 0 && page < a.num_pages) ? page : -1;
+      }
+      if (a.out_ids && sp == 0 && kh == 0 && wave_u == 0 && lane <= kTopK)
+        a.out_ids[int64_t(qt) * (kTopK + 1) + lane] = sel;
+      if (kShared) {
+        slot_blk[lane] = sel;
+        slot_page[lane] = pg;
+      }
     }
-    if (a.out_ids && sp == 0 && kh == 0 && wave == 0 && lane <= kTopK)
-      a.out_ids[int64_t(qt) * (kTopK + 1) + lane] = sel;
   } else {
     if (seq_ok && sel >= 0 && sel < a.max_blocks && sel * kBlockTokens <= pos) {
       const int p = a.block_table[int64_t(b) * a.max_blocks + sel];
@@ -191,6 +246,10 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(const AttnArgs a) {
 #pragma unroll
   for (int n = 0; n < 8; ++n) o[n] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   __syncthreads();
+  if (SELECT && kShared && !selector) {
+    sel = slot_blk[lane];
+    pg = slot_page[lane];
+  }
 
   const int64_t page_codes = int64_t(a.num_kv_heads) * kCodePage;
   const int64_t page_scales = int64_t(a.num_kv_heads) * kScalePage;
@@ -200,30 +259,34 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(const AttnArgs a) {
   // group, left or right 8 bytes (V) / real or zero segment (P)
   const int seg_row = li >> 1, seg_half = li & 1;
 
-  const int s_begin = sp * W * a.slots_per_wave;
-  const int s_end = min(a.num_sel, s_begin + W * a.slots_per_wave);
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int s_begin = sp * a.slots_per_wg;
+  const int s_end = min(a.num_sel, s_begin + a.slots_per_wg);
+  const int t_wave = kShared ? TOK * wave_u : 0;  // this wavefront's first token of a block
   bool fresh = true;  // no block accumulated yet: o is zero and needs no rescale
-  for (int si = s_begin + wave_u; si < s_end; si += W) {
+  for (int si = s_begin + (kShared ? 0 : wave_u); si < s_end; si += (kShared ? 1 : W)) {
     const int page = __builtin_amdgcn_readlane(pg, si);
     if (page < 0) continue;  // uniform over the wavefront
     const int blk = __builtin_amdgcn_readlane(sel, si);
-    const int ntok = min(kBlockTokens, pos + 1 - blk * kBlockTokens);
-    const int64_t hc = int64_t(page) * page_codes + int64_t(kh) * kCodePage + lane_code;
+    // visible tokens of this wavefront's part of the block
+    const int nvis = min(TOK, pos + 1 - blk * kBlockTokens - t_wave);
+    if (nvis <= 0) continue;  // uniform
+    const int64_t hc = int64_t(page) * page_codes + int64_t(kh) * kCodePage + lane_code +
+                       int64_t(t_wave) * kCodeRow;
     const int64_t hs = int64_t(page) * page_scales + int64_t(kh) * kScalePage + lane_scale;
-    uint4 kc[8], vc[8];
+    uint4 kc[NT], vc[NT];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) kc[j] = load_stream16(a.k_codes + hc + j * 16 * kCodeRow);
-    const uint4 ksw = load_stream16(a.k_scales + hs);
+    for (int j = 0; j < NT; ++j) kc[j] = load_stream16(a.k_codes + hc + j * 16 * kCodeRow);
+    const TileScaleWords<NT> ksw = load_tile_scales<NT>(a.k_scales + hs, t_wave / 16);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) vc[j] = load_stream16(a.v_codes + hc + j * 16 * kCodeRow);
-    const uint4 vsw = load_stream16(a.v_scales + hs);
-    // 1. logits of 16 tokens per tile: lane holds heads 4*slice+v, token 16j+li
-    const bool part = ntok < kBlockTokens;  // the block is only partly visible
-    float z[8][4];
+    for (int j = 0; j < NT; ++j) vc[j] = load_stream16(a.v_codes + hc + j * 16 * kCodeRow);
+    const TileScaleWords<NT> vsw = load_tile_scales<NT>(a.v_scales + hs, t_wave / 16);
+    // 1. logits of 16 tokens per tile: lane holds heads 4*slice+v, token
+    //    t_wave + 16j + li
+    const bool part = nvis < TOK;  // this part of the block is only partly visible
+    float z[NT][4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t ks = tile_scales(ksw, j);
+    for (int j = 0; j < NT; ++j) {
+      const uint32_t ks = scale_pair(ksw, j);
       const v8i kop = dequant32(kc[j], lut[ks & 0x7F], lut[(ks >> 8) & 0x7F]);
       const v4f c = mfma_fp8_16x16x128(qop, kop, v4f{0.0f, 0.0f, 0.0f, 0.0f});
 #pragma unroll
@@ -231,17 +294,17 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(const AttnArgs a) {
     }
     if (part) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int j = 0; j < NT; ++j)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) z[j][v] = 16 * j + li < ntok ? z[j][v] : ninf;
+        for (int v = 0; v < 4; ++v) z[j][v] = 16 * j + li < nvis ? z[j][v] : ninf;
     }
     // 2. V rows into LDS in the dequantiser's channel order (0,2,4,6,1,3,5,7
     //    in every run of 8; the output index undoes it); invisible tokens -> 0
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t vsc = tile_scales(vsw, j);
+    for (int j = 0; j < NT; ++j) {
+      const uint32_t vsc = scale_pair(vsw, j);
       v8i vop = dequant32(vc[j], lut[vsc & 0x7F], lut[(vsc >> 8) & 0x7F]);
-      if (part && 16 * j + li >= ntok) vop = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+      if (part && 16 * j + li >= nvis) vop = v8i{0, 0, 0, 0, 0, 0, 0, 0};
       uint8_t* dst = vrows + (16 * j + li) * kVRow + slice * 32;
       *reinterpret_cast<uint2*>(dst) = make_uint2(uint32_t(vop[0]), uint32_t(vop[1]));
       *reinterpret_cast<uint2*>(dst + 8) = make_uint2(uint32_t(vop[2]), uint32_t(vop[3]));
@@ -255,13 +318,13 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(const AttnArgs a) {
     for (int v = 0; v < 4; ++v) {
       float mb = z[0][v];
 #pragma unroll
-      for (int j = 1; j < 8; ++j) mb = fmaxf(mb, z[j][v]);
+      for (int j = 1; j < NT; ++j) mb = fmaxf(mb, z[j][v]);
       const float m_new = fmaxf(m_run[v], row16_max(mb));
       alpha[v] = __builtin_amdgcn_exp2f(m_run[v] - m_new);
       m_run[v] = m_new;
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < NT; ++j) {
       float p[4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) p[v] = __builtin_amdgcn_exp2f(z[j][v] - m_run[v]) * kPScale;
@@ -290,7 +353,39 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(const AttnArgs a) {
     //    32*slice + 8r .. +7; lanes 8..15 read the zero segment (rows 8..15
     //    of A are zero). The softmax denominator is the same product with a
     //    column of FP8 ones, so it sums exactly the rounded terms of P.
-    {
+    const v8i ones = v8i{kFp8Ones, kFp8Ones, kFp8Ones, kFp8Ones,
+                         kFp8Ones, kFp8Ones, kFp8Ones, kFp8Ones};
+    if constexpr (kShared) {
+      // 32 tokens, one MFMA per 16 channels for both terms. The 16x16x128
+      // product takes bytes 0-15 of lane group g as K elements 16g .. 16g+15
+      // and bytes 16-31 as 64 + 16g .. 64 + 16g + 15, and the E8M0 scale of
+      // lane group c applies to K elements 32c .. 32c + 31 (both measured).
+      // Lane groups 0 and 1 carry tokens 16g .. 16g + 15: P_hi in their low
+      // halves (K block 0, scale 1), P_lo in their high halves (K block 2,
+      // scale 2^-4 from lane group 2); V repeats the same tokens in both
+      // halves; lane groups 2 and 3 are zero.
+      const bool live = slice < 2;
+      const int tok = 16 * slice + seg_row;  // token of this lane's segment (reads 0 and 2)
+      const uint8_t* ph = (live && !seg_half) ? prows + tok * kHeadsPerKv : zeros;
+      const uint8_t* pl = (live && !seg_half) ? plows + tok * kHeadsPerKv : zeros;
+      const int pstep = (live && !seg_half) ? 8 * kHeadsPerKv : 0;
+      const v8i pop = tr_operand(ph, ph + pstep, pl, pl + pstep);
+      const int pscale = slice == 2 ? kE8M0Sixteenth : kE8M0One;
+      const v4f lb = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          pop, ones, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, pscale, 0, kE8M0One);
+      const uint8_t* vb = live ? vrows + tok * kVRow + 8 * seg_half : zeros;
+      const int vstep = live ? 8 * kVRow : 0;
+      const int nstep = live ? 16 : 0;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const uint8_t* vp = vb + nstep * n;
+        const v8i vop = tr_operand(vp, vp + vstep, vp, vp + vstep);
+        o[n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pop, vop, o[n], 0, 0, 0, pscale, 0,
+                                                                 kE8M0One);
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) l_run[v] = l_run[v] * alpha[v] + lb[v];
+    } else {
       const int t0 = 32 * slice;
       const int poff = (t0 + seg_row) * kHeadsPerKv;
       const uint8_t* ph = seg_half ? zeros : prows + poff;
@@ -298,8 +393,6 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(const AttnArgs a) {
       const int pstep = seg_half ? 0 : 8 * kHeadsPerKv;
       const v8i pop_hi = tr_operand(ph, ph + pstep, ph + 2 * pstep, ph + 3 * pstep);
       const v8i pop_lo = tr_operand(pl, pl + pstep, pl + 2 * pstep, pl + 3 * pstep);
-      const v8i ones = v8i{kFp8Ones, kFp8Ones, kFp8Ones, kFp8Ones,
-                           kFp8Ones, kFp8Ones, kFp8Ones, kFp8Ones};
       v4f lb = mfma_fp8_16x16x128(pop_hi, ones, v4f{0.0f, 0.0f, 0.0f, 0.0f});
       lb = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pop_lo, ones, lb, 0, 0, 0,
                                                            kE8M0Sixteenth, 0, kE8M0One);
@@ -374,7 +467,7 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(const AttnArgs a) {
 // Merge kernel: one workgroup per (query token, KV head); thread (h, 4 ch)
 // combines the splits' (m, l, o) by log-sum-exp. Up to kMergeChunk splits
 // are fetched per round of independent loads.
-constexpr int kMergeChunk = 16;
+constexpr int kMergeChunk = 20;
 
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part_o,
                                                     const float* __restrict__ part_ml,
@@ -419,23 +512,33 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
       make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
 }
 
-constexpr int kAttnWaves = 4;
-
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 inline bool misaligned(const void* p, uintptr_t m) { return (reinterpret_cast<uintptr_t>(p) & m) != 0; }
 
-// Slots per wave R and split count: one block per wave while that keeps the
-// workgroup count under ~1024; otherwise more blocks per wave.
-inline void attn_plan(int64_t pairs, int num_sel, int* r, int* nsplit) {
+// Launch plan for `pairs` (query token, KV head) pairs and num_sel slots.
+// Few pairs (pairs * num_sel <= kSharedMaxWgs): one workgroup per selected
+// block, its four wavefronts sharing the block (32 tokens each), so the
+// serial work per wavefront is a quarter block. Measured against whole
+// blocks per wavefront at 17 slots: 2.3 us faster per step at 4 pairs, 1.5 us
+// at 16, 0.4 us slower at 32 (more workgroups than the chip runs evenly).
+// Otherwise whole blocks per wavefront: one block per wave while that keeps
+// the workgroup count under ~1024, else R blocks per wave.
+constexpr int64_t kSharedMaxWgs = 384;
+struct AttnPlan {
+  int tok;           // tokens of a block per wavefront: 32 or 128
+  int slots_per_wg;  // selected slots per workgroup
+  int splits;        // workgroups per pair
+};
+inline AttnPlan attn_plan(int64_t pairs, int num_sel) {
+  if (pairs * num_sel <= kSharedMaxWgs) return AttnPlan{kBlockTokens / kAttnWaves, 1, num_sel};
   int R = 1;
   while (R < num_sel && pairs * ((num_sel + kAttnWaves * R - 1) / (kAttnWaves * R)) > 1024) ++R;
-  *r = R;
-  *nsplit = (num_sel + kAttnWaves * R - 1) / (kAttnWaves * R);
+  return AttnPlan{kBlockTokens, kAttnWaves * R, (num_sel + kAttnWaves * R - 1) / (kAttnWaves * R)};
 }
 
-template <int W>
+template <int TOK>
 constexpr size_t attn_lds_bytes() {
-  return size_t(W) * kWaveLds + 64;
+  return size_t(kAttnWaves) * WaveLds<TOK>::kBytes + 64;
 }
 
 }  // namespace msa
@@ -443,9 +546,12 @@ constexpr size_t attn_lds_bytes() {
 extern "C" size_t msa_attn_workspace_bytes(int32_t num_seqs, int32_t q_per_seq,
                                            int32_t num_q_heads, int32_t num_sel) {
   if (num_seqs <= 0 || q_per_seq <= 0 || num_q_heads <= 0 || num_sel <= 0) return 0;
-  // enough for the largest split count the launch can choose (one block per wave)
+  // the split partials of the launch plan for these shapes
+  const int64_t kv_heads = (num_q_heads + MSA_HEADS_PER_KV - 1) / MSA_HEADS_PER_KV;
+  const msa::AttnPlan plan = msa::attn_plan(int64_t(num_seqs) * q_per_seq * kv_heads, num_sel);
+  if (plan.splits <= 1) return 0;
   const size_t rows = size_t(num_seqs) * q_per_seq * num_q_heads;
-  const size_t splits = size_t(num_sel + msa::kAttnWaves - 1) / msa::kAttnWaves;
+  const size_t splits = size_t(plan.splits);
   return msa::align256(rows * splits * MSA_HEAD_DIM * 4) + msa::align256(rows * splits * 2 * 4);
 }
 
@@ -484,7 +590,9 @@ static msa_status run_attn(AttnArgs a, const msa_pool_desc* kv, int32_t num_seqs
                            int32_t q_per_seq, int32_t num_q_heads, void* workspace,
                            size_t workspace_bytes, hipStream_t s) {
   const int64_t tq = int64_t(num_seqs) * q_per_seq;
-  attn_plan(tq * kv->num_heads, a.num_sel, &a.slots_per_wave, &a.num_splits);
+  const AttnPlan plan = attn_plan(tq * kv->num_heads, a.num_sel);
+  a.slots_per_wg = plan.slots_per_wg;
+  a.num_splits = plan.splits;
   if (a.num_splits > 1) {
     const size_t need = msa_attn_workspace_bytes(num_seqs, q_per_seq, num_q_heads, a.num_sel);
     if (!workspace || workspace_bytes < need || misaligned(workspace, 255)) return MSA_ERR_WORKSPACE;
@@ -497,8 +605,12 @@ static msa_status run_attn(AttnArgs a, const msa_pool_desc* kv, int32_t num_seqs
     a.part_ml = nullptr;
   }
   const dim3 grid(a.num_splits, kv->num_heads, unsigned(tq));
-  hipLaunchKernelGGL((sparse_attn_kernel<kAttnWaves, SELECT>), grid, dim3(64 * kAttnWaves),
-                     attn_lds_bytes<kAttnWaves>(), s, a);
+  if (plan.tok == kBlockTokens)
+    hipLaunchKernelGGL((sparse_attn_kernel<kBlockTokens, SELECT>), grid, dim3(64 * kAttnWaves),
+                       attn_lds_bytes<kBlockTokens>(), s, a);
+  else
+    hipLaunchKernelGGL((sparse_attn_kernel<kBlockTokens / kAttnWaves, SELECT>), grid,
+                       dim3(64 * kAttnWaves), attn_lds_bytes<kBlockTokens / kAttnWaves>(), s, a);
   if (hipGetLastError() != hipSuccess) return MSA_ERR_HIP;
   if (a.num_splits > 1) {
     hipLaunchKernelGGL(merge_kernel, dim3(unsigned(tq * kv->num_heads)), dim3(256), 0, s,

@@ -159,9 +159,10 @@ __device__ __forceinline__ v8i q_operand(uint4 a, uint4 b) {
 }
 
 // D(16x16, fp32) = A(16x128, FP8 E4M3) x B(128x16, FP8 E4M3) + C. Lane l
-// supplies row l%16 of A and column l%16 of B (32 bytes each, the same
-// 32-element slice of the reduction dimension); it receives D rows
-// 4*(l/16) .. 4*(l/16)+3 of column l%16.
+// supplies row l%16 of A and column l%16 of B, 32 bytes each and the same 32
+// elements of the reduction dimension: bytes 0-15 are elements 16(l/16) ..
+// 16(l/16)+15, bytes 16-31 are 64 + 16(l/16) .. 64 + 16(l/16)+15 (measured
+// on gfx950). It receives D rows 4*(l/16) .. 4*(l/16)+3 of column l%16.
 __device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b, v4f c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
@@ -178,19 +179,17 @@ __device__ __forceinline__ uint4 load_stream16(const void* p) {
 }
 
 // ---------------------------------------------------------------- waves
-// Maximum of an unsigned value over the wavefront, uniform result: prefix
-// maxima inside each row of 16 lanes with DPP row shifts (out-of-row lanes
-// read 0, the identity), then the four row results through lane reads. No
-// LDS round trips, unlike a shuffle butterfly. Non-negative floats can use it
-// on their bit patterns.
-// Prefix maximum inside each row of 16 lanes (lane 15 of a row ends with
-// the row's maximum).
+// Prefix maximum of an unsigned value inside each row of 16 lanes, with DPP
+// row shifts (out-of-row lanes read 0, the identity): lane 15 of a row ends
+// with the row's maximum. No LDS round trips, unlike a shuffle butterfly.
+// Non-negative floats can use it on their bit patterns.
 __device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
   v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x111, 0xF, 0xF, true)));  // row_shr:1
   v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x112, 0xF, 0xF, true)));  // row_shr:2
   v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x114, 0xF, 0xF, true)));  // row_shr:4
   return max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x118, 0xF, 0xF, true)));  // row_shr:8
 }
+// Maximum of a 64-bit key over the wavefront (xor butterfly), uniform result.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {

@@ -50,13 +50,21 @@ __device__ __forceinline__ int key_block_id(uint64_t k) { return int(0xFFFFFFFFu
 __device__ __forceinline__ float key_score_value(uint64_t k) { return __uint_as_float(uint32_t(k >> 32)); }
 
 // One chunk of a query token's block scores: lane l gets entries
-// c0 + l + 64 k. Loads are clamped to the row (row_len > 0 entries) instead
-// of predicated, so all of them are in flight at once; entries past the
-// candidates are masked by index later.
+// c0 + l + 64 k. The loads go through a buffer descriptor over the row
+// (row_len entries; a buffer load past the record count returns 0), with one
+// 32-bit lane offset and the stride of k in the constant offsets: nothing is
+// predicated, so all 32 loads are in flight at once, and no per-element
+// 64-bit address is formed. Entries past the candidates are masked by index
+// later.
 __device__ __forceinline__ void load_score_chunk(const float* row, int row_len, int c0, int lane,
                                                  float (&x)[kSelPerLane]) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(row), 0, row_len * int(sizeof(float)), 0x00020000);
+  const uint32_t off = uint32_t(c0 + lane) * uint32_t(sizeof(float));
 #pragma unroll
-  for (int k = 0; k < kSelPerLane; ++k) x[k] = row[min(c0 + lane + 64 * k, row_len - 1)];
+  for (int k = 0; k < kSelPerLane; ++k)
+    x[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                         r, off, 64 * k * int(sizeof(float)), 0));
 }
 
 // Inclusive prefix sum over the wavefront: DPP row shifts inside rows of 16
@@ -98,10 +106,12 @@ __device__ __forceinline__ int select_blocks(const float* row, int row_len, int 
   const int n = nb - 1;  // candidates; the recent block is always kept
   const int nchunks = (n + kSelChunk - 1) / kSelChunk;
   uint32_t v[kSelPerLane];
-  auto chunk_bits = [&](int c) {
+  // chunk c's score bits into v: chunk 0 from x0 on the first pass only, so
+  // x0 is dead afterwards (later passes over several chunks reload them)
+  auto chunk_bits = [&](int c, bool from_x0) {
     const int c0 = c * kSelChunk;
     float x[kSelPerLane];
-    if (c == 0) {
+    if (from_x0) {
 #pragma unroll
       for (int k = 0; k < kSelPerLane; ++k) x[k] = x0[k];
     } else {
@@ -116,8 +126,9 @@ __device__ __forceinline__ int select_blocks(const float* row, int row_len, int 
   };
   // 1. lane maxima
   uint32_t m = 0;
+  chunk_bits(0, true);
   for (int c = 0; c < nchunks; ++c) {
-    chunk_bits(c);
+    if (c > 0) chunk_bits(c, false);
 #pragma unroll
     for (int k = 0; k < kSelPerLane; ++k) m = max(m, v[k]);
   }
@@ -142,7 +153,7 @@ __device__ __forceinline__ int select_blocks(const float* row, int row_len, int 
   for (int c = 0; c < nchunks; ++c) {
     const int c0 = c * kSelChunk;
     if (nchunks > 1) {
-      chunk_bits(c);
+      chunk_bits(c, false);
       stage_chunk();
     } else if (c == 0) {
       stage_chunk();
@@ -192,7 +203,7 @@ __device__ __forceinline__ int select_blocks(const float* row, int row_len, int 
     for (int r = 0; r < kTopK; ++r) {
       uint64_t best = 0;
       for (int c = 0; c < nchunks; ++c) {
-        if (nchunks > 1) chunk_bits(c);
+        if (nchunks > 1) chunk_bits(c, false);
         const int c0 = c * kSelChunk;
 #pragma unroll
         for (int k = 0; k < kSelPerLane; ++k) {

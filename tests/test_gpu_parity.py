@@ -135,6 +135,27 @@ def test_tiny_parity(nb, lens, q, fused):
     assert not fails, "\n".join(fails[:20])
 
 
+# The attention launch plan switches on pairs * slots (pairs = query tokens
+# x KV heads, 17 slots): up to 384 workgroups the four wavefronts of a
+# workgroup share each block (32 tokens each), above that every wavefront
+# takes whole blocks. Five sequences (20 pairs) run the shared form, six
+# (24 pairs) the whole-block form, on the same lengths.
+@pytest.mark.parametrize("nseq", [5, 6], ids=["shared-block-waves", "whole-block-waves"])
+def test_attention_launch_forms(nb, nseq):
+    lens = [1, 130, 200, 2177, 4099, 3000][:nseq]
+    say(f"attention launch forms lens={lens}")
+    wl = tiny_config(lens, 1, seed=60 + nseq)
+    pools = S.fill_pools(wl, nb)
+    inp = S.device_inputs(wl)
+    for fused in (True, False):
+        ids, sc, o = _to_np(S.run_step(nb, wl, pools, inp, fused=fused))
+        _structural(wl, ids)
+        fails = []
+        for b in range(wl.num_seqs):
+            fails += S.check_sequence(wl, b, ids, sc, o)
+        assert not fails, "\n".join(fails[:20])
+
+
 @pytest.mark.parametrize("heads", [1, 2, 8])
 def test_head_counts(nb, heads):
     # every kernel takes the number of index-key / KV heads at run time (1..8,

@@ -40,13 +40,27 @@ def test_status_strings(L):
     assert "unknown" in nb.msa_status_string(99)
 
 
-def test_workspace_sizes(L):
+def _attn_splits(pairs, num_sel):
+    # the launch plan: few (query token, KV head) pairs -> one workgroup per
+    # selected block; otherwise one block per wavefront (4 per workgroup),
+    # R blocks per wavefront while the workgroup count exceeds 1024
+    if pairs * num_sel <= 384:
+        return num_sel
+    r = 1
+    while r < num_sel and pairs * -(-num_sel // (4 * r)) > 1024:
+        r += 1
+    return -(-num_sel // (4 * r))
+
+
+@pytest.mark.parametrize("seqs,q,heads,sel", [(16, 8, 32, 17), (8, 1, 32, 17), (32, 1, 32, 17),
+                                              (1, 1, 32, 17), (2, 1, 8, 64), (45, 1, 32, 17)])
+def test_workspace_sizes(L, seqs, q, heads, sel):
     assert nb.msa_indexer_workspace_bytes(8, 1, 2048) == 8 * 2048 * 4
     assert nb.msa_indexer_workspace_bytes(0, 1, 10) == 0
-    rows = 16 * 8 * 32
-    splits = (17 + 3) // 4
-    want = rows * splits * 128 * 4 + rows * splits * 2 * 4
-    got = nb.msa_attn_workspace_bytes(16, 8, 32, 17)
+    rows = seqs * q * heads
+    splits = _attn_splits(seqs * q * heads // 8, sel)
+    want = rows * splits * 128 * 4 + rows * splits * 2 * 4 if splits > 1 else 0
+    got = nb.msa_attn_workspace_bytes(seqs, q, heads, sel)
     assert want <= got <= want + 2 * 255
 
 
