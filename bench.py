@@ -54,12 +54,24 @@ def parse():
     return p.parse_args()
 
 
-def algorithmic_bytes(wl, ids):
+def algorithmic_bytes(wl, ids, dedup=False):
     """Bytes the method must move per step (never the dense K/V it skips).
+    With dedup (the shared-prefix scan) a physical page shared by several
+    sequences counts once, with the most tokens any of them sees.
     Returns (scan, rest of the step, selected-block union)."""
     tq, hq = wl.num_q_tokens, wl.num_q_heads
     nblocks = sum(wl.blocks_of(b) for b in range(wl.num_seqs))
-    scan = (sum(int(L) for L in wl.seq_lens) * wl.num_idx_heads * IDX_BYTES_PER_TOKEN_HEAD
+    if dedup:
+        seen = {}
+        for b in range(wl.num_seqs):
+            L = int(wl.seq_lens[b])
+            for j in range(wl.blocks_of(b)):
+                page = int(wl.block_table[b, j])
+                seen[page] = max(seen.get(page, 0), min(128, L - 128 * j))
+        index_tokens = sum(seen.values())
+    else:
+        index_tokens = sum(int(L) for L in wl.seq_lens)
+    scan = (index_tokens * wl.num_idx_heads * IDX_BYTES_PER_TOKEN_HEAD
             + tq * hq * 128          # FP8 index queries
             + tq * hq * 4            # head weights
             + nblocks * 4)           # block-table entries
@@ -186,7 +198,7 @@ def main():
     import torch
     import nvfp4_kv_cache_amd as nb
     from msa_workloads import get_config, synth
-    from msa_workloads.device import device_inputs, fill_pools
+    from msa_workloads.device import device_inputs, fill_pools, shared_groups
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     nb.lib()
@@ -208,9 +220,19 @@ def main():
     bscores = ws_i[: tq * wl.max_blocks * 4].view(torch.float32).view(tq, wl.max_blocks)
 
     # each library call validated and marshalled once (binding.Prepared):
-    # re-issuing it is one ctypes call, so the host stays far ahead of the GPU
-    scan = nb.msa_indexer_scan(ic, isc, inp["q_idx"], inp["w"], inp["block_table"],
-                               inp["seq_lens"], wl.q_per_seq, bscores, prepare=True)
+    # re-issuing it is one ctypes call, so the host stays far ahead of the GPU.
+    # A batch whose sequences share leading pages (a cached common prefix)
+    # is scanned with msa_indexer_scan_shared: each shared block is read and
+    # dequantised once for all the sequences that share it.
+    groups = shared_groups(wl)
+    dedup = groups[3] > 0
+    if dedup:
+        scan = nb.msa_indexer_scan_shared(ic, isc, inp["q_idx"], inp["w"], inp["block_table"],
+                                          inp["seq_lens"], wl.q_per_seq, *groups, bscores,
+                                          prepare=True)
+    else:
+        scan = nb.msa_indexer_scan(ic, isc, inp["q_idx"], inp["w"], inp["block_table"],
+                                   inp["seq_lens"], wl.q_per_seq, bscores, prepare=True)
     select_attend = nb.msa_sparse_attn_select_decode(
         kc, ks, vc, vs, inp["q_attn"], inp["block_table"], inp["seq_lens"], wl.q_per_seq,
         bscores, scale, out, ws_a, out_ids=ids, prepare=True)
@@ -250,8 +272,13 @@ def main():
         cap = torch.cuda.Stream()
         cap.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(cap):
-            g_scan = nb.msa_indexer_scan(ic, isc, inp["q_idx"], inp["w"], inp["block_table"],
-                                         inp["seq_lens"], wl.q_per_seq, bscores, prepare=True)
+            if dedup:
+                g_scan = nb.msa_indexer_scan_shared(ic, isc, inp["q_idx"], inp["w"],
+                                                    inp["block_table"], inp["seq_lens"],
+                                                    wl.q_per_seq, *groups, bscores, prepare=True)
+            else:
+                g_scan = nb.msa_indexer_scan(ic, isc, inp["q_idx"], inp["w"], inp["block_table"],
+                                             inp["seq_lens"], wl.q_per_seq, bscores, prepare=True)
             g_attn = nb.msa_sparse_attn_select_decode(
                 kc, ks, vc, vs, inp["q_attn"], inp["block_table"], inp["seq_lens"],
                 wl.q_per_seq, bscores, scale, out, ws_a, out_ids=ids, prepare=True)
@@ -323,7 +350,7 @@ def main():
     del flush
 
     ids_np = ids.cpu().numpy()
-    idx_bytes, attn_bytes, union = algorithmic_bytes(wl, ids_np)
+    idx_bytes, attn_bytes, union = algorithmic_bytes(wl, ids_np, dedup=dedup)
     ms = wall / args.steps * 1e3
     step_bytes = idx_bytes + attn_bytes
     idx_gbs = idx_bytes / t_idx / 1e9
@@ -348,7 +375,9 @@ def main():
                    "context_tokens": int(max(wl.seq_lens)), "q_per_seq": wl.q_per_seq,
                    "kv_heads": wl.num_kv_heads, "index_heads": wl.num_idx_heads,
                    "q_heads": wl.num_q_heads, "head_dim": 128, "block_tokens": 128,
-                   "topk": wl.topk},
+                   "topk": wl.topk,
+                   "shared_prefix_groups": int(len(groups[2])),
+                   "shared_prefix_blocks": [int(x) for x in groups[2].cpu().tolist()]},
         "achieved_hbm_gbs": round(step_bytes / (ms * 1e-3) / 1e9, 1),
         "hbm_frac_of_peak": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": int(step_bytes),

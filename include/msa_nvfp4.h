@@ -163,6 +163,43 @@ msa_status msa_indexer_scan(const msa_pool_desc* idx, const uint8_t* idx_codes,
                             float* block_scores, void* stream);
 
 /*
+ * msa_indexer_scan for a batch in which groups of sequences share leading
+ * blocks: the same physical pages at the same logical block indices, as a
+ * cached common prefix gives. Each shared block is read and dequantised once
+ * per call and scored against the query tokens of every member of its group;
+ * the other blocks are scanned as by msa_indexer_scan. The block scores are
+ * the values msa_indexer_scan writes for the same inputs. (MiniMax-M3.1-Flash
+ * serving summary, section "AMD uses different conversion and communication
+ * mechanisms": shared prefixes reduce repeated dequantisation across
+ * requests.)
+ *   num_groups         groups of sequences, 0 .. 65535 (0: msa_indexer_scan)
+ *   group_start        int32 [num_groups + 1], device: the members of group g
+ *                      are group_seqs[group_start[g] .. group_start[g + 1])
+ *   group_seqs         int32 sequence ids, device; a sequence is in at most
+ *                      one group
+ *   group_blocks       int32 [num_groups], device: leading blocks group g
+ *                      shares; for every member b and j < group_blocks[g],
+ *                      block_table[b][j] == block_table[first member][j]
+ *   max_group_blocks   host: >= every group_blocks[g], in [1, max_blocks]
+ *                      (ignored when num_groups == 0)
+ *   seq_shared_blocks  int32 [num_seqs], device: group_blocks of the group
+ *                      of sequence b, 0 for a sequence in no group
+ * Other arguments as msa_indexer_scan. group_start must be non-decreasing
+ * and index group_seqs; other breaches of these rules give wrong scores but
+ * no out-of-bounds access (member ids outside the batch are skipped, block
+ * counts are clamped to max_blocks).
+ */
+msa_status msa_indexer_scan_shared(const msa_pool_desc* idx, const uint8_t* idx_codes,
+                                   const uint8_t* idx_scales, const uint8_t* q_fp8,
+                                   const float* head_w, int32_t num_q_heads,
+                                   const int32_t* block_table, int32_t max_blocks,
+                                   const int32_t* seq_lens, int32_t num_seqs, int32_t q_per_seq,
+                                   int32_t num_groups, const int32_t* group_start,
+                                   const int32_t* group_seqs, const int32_t* group_blocks,
+                                   int32_t max_group_blocks, const int32_t* seq_shared_blocks,
+                                   float* block_scores, void* stream);
+
+/*
  * msa_indexer_select reads block_scores (as written by msa_indexer_scan) and
  * writes out_ids / out_scores exactly as msa_indexer_decode does; scores
  * must be finite (negative values and -0 rank as 0).

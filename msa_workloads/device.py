@@ -62,6 +62,15 @@ def fill_pools(wl, nb, device="cuda", garbage=True, chunk_pages=256, overrides=N
     return pools
 
 
+def shared_groups(wl, device="cuda"):
+    """The workload's shared-prefix groups as device int32 tensors plus the
+    largest group block count: (group_start, group_seqs, group_blocks,
+    max_group_blocks, seq_shared_blocks)."""
+    start, seqs, blocks, shared = wl.shared_prefix_groups()
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)  # noqa: E731
+    return (to(start), to(seqs), to(blocks), int(blocks.max()) if len(blocks) else 0, to(shared))
+
+
 def device_inputs(wl, device="cuda"):
     return dict(
         q_idx=wl.q_idx().to(device),

@@ -48,6 +48,8 @@ SIGNATURES = {
                                           _I32, _P, _P, _P, _SZ, _P]),
     "msa_indexer_scan": (ctypes.c_int, [_DESC, _P, _P, _P, _P, _I32, _P, _I32, _P, _I32, _I32,
                                         _P, _P]),
+    "msa_indexer_scan_shared": (ctypes.c_int, [_DESC, _P, _P, _P, _P, _I32, _P, _I32, _P, _I32,
+                                               _I32, _I32, _P, _P, _P, _I32, _P, _P, _P]),
     "msa_indexer_select": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _I32, _P, _P, _P]),
     "msa_attn_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
     "msa_sparse_attn_decode": (ctypes.c_int, [_DESC, _P, _P, _P, _P, _P, _I32, _P, _I32, _P,
@@ -257,6 +259,35 @@ def msa_indexer_scan(idx_codes, idx_scales, q_fp8, head_w, block_table, seq_lens
         ctypes.byref(desc), _ptr(idx_codes), _ptr(idx_scales), _ptr(q_fp8), _ptr(head_w), hq,
         _ptr(block_table), max_blocks, _ptr(seq_lens), num_seqs, q_per_seq, _ptr(block_scores),
         _stream()), prepare, keep=(desc,))
+
+
+def msa_indexer_scan_shared(idx_codes, idx_scales, q_fp8, head_w, block_table, seq_lens, q_per_seq,
+                            group_start, group_seqs, group_blocks, max_group_blocks,
+                            seq_shared_blocks, block_scores, prepare=False):
+    """msa_indexer_scan with shared leading blocks read and dequantised once per
+    group: group_start int32 [G+1], group_seqs int32, group_blocks int32 [G],
+    seq_shared_blocks int32 [B] (device), max_group_blocks >= every
+    group_blocks entry (host int)."""
+    _check_pool(idx_codes, idx_scales, "idx")
+    num_seqs, max_blocks, tq, hq = _check_indexer_inputs(q_fp8, head_w, block_table, seq_lens,
+                                                         q_per_seq)
+    _need(block_scores, "block_scores", torch.float32, 2)
+    if block_scores.shape != (tq, max_blocks):
+        raise ValueError("block_scores must be [T_q, max_blocks]")
+    for t, name in ((group_start, "group_start"), (group_seqs, "group_seqs"),
+                    (group_blocks, "group_blocks"), (seq_shared_blocks, "seq_shared_blocks")):
+        _need(t, name, torch.int32, 1)
+    num_groups = group_start.shape[0] - 1
+    if num_groups < 0 or group_blocks.shape[0] != num_groups:
+        raise ValueError("group_start must be [G+1] and group_blocks [G]")
+    if seq_shared_blocks.shape[0] != num_seqs:
+        raise ValueError("seq_shared_blocks must be [num_seqs]")
+    desc = pool_desc(idx_codes)
+    return _issue("msa_indexer_scan_shared", (
+        ctypes.byref(desc), _ptr(idx_codes), _ptr(idx_scales), _ptr(q_fp8), _ptr(head_w), hq,
+        _ptr(block_table), max_blocks, _ptr(seq_lens), num_seqs, q_per_seq, num_groups,
+        _ptr(group_start), _ptr(group_seqs), _ptr(group_blocks), int(max_group_blocks),
+        _ptr(seq_shared_blocks), _ptr(block_scores), _stream()), prepare, keep=(desc,))
 
 
 def msa_indexer_select(block_scores, seq_lens, q_per_seq, out_ids, out_scores=None, topk=TOPK,

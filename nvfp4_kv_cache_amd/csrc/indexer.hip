@@ -46,6 +46,7 @@ struct IndexerArgs {
   int q_per_seq;
   int blocks_per_wg;
   float* bscore;       // [num_seqs * q_per_seq][max_blocks]
+  const int32_t* seq_skip;  // [num_seqs] leading blocks scored by the shared pass, or null
 };
 
 constexpr int kMaxBlocksPerWg = 8;  // blocks per scan workgroup (page list size)
@@ -114,10 +115,15 @@ __global__ __launch_bounds__(512) void indexer_kernel(const IndexerArgs a) {
   const bool seq_ok = L >= Q && L <= a.max_blocks * kBlockTokens;
   const int nb_last = seq_ok ? (L - 1) / kBlockTokens + 1 : 0;
   // workgroup x of a sequence takes blocks x, x + G, x + 2G, ... (G = grid
-  // width), so the workgroups running at any moment read neighbouring pages
+  // width), so the workgroups running at any moment read neighbouring pages;
+  // blocks below the sequence's shared prefix are left to the shared pass
   const int G = gridDim.x;
-  const int first = blockIdx.x;
-  const int count = nb_last > first ? min(a.blocks_per_wg, (nb_last - first + G - 1) / G) : 0;
+  const int x = blockIdx.x;
+  const int total = nb_last > x ? min(a.blocks_per_wg, (nb_last - x + G - 1) / G) : 0;
+  const int skip = a.seq_skip ? a.seq_skip[b] : 0;
+  const int k0 = x < skip ? min(total, (skip - x + G - 1) / G) : 0;
+  const int first = x + k0 * G;
+  const int count = total - k0;
   const int64_t qrow0 = int64_t(b) * Q;
   const int Hq = a.num_q_heads;
   if (int(threadIdx.x) < count) {
@@ -261,6 +267,158 @@ __global__ __launch_bounds__(512) void indexer_kernel(const IndexerArgs a) {
   }
 }
 
+// Shared pass for sequences that share leading blocks (the same physical
+// pages at the same logical blocks): workgroup (j, g, c) reads block j of
+// group g, one wavefront per index head, dequantises its 8 tiles into
+// registers and scores them against query tokens 8c .. 8c + 7 of the group's
+// members (64 MFMA rows: token 8c + R/8, head R%8); the chunks of a block run
+// side by side and share its read through L2, so a block is dequantised once
+// per 8 member tokens instead of once per member. The
+// arithmetic per token is the regular scan's, in the same order (the same
+// MFMA operands, the ReLU-weighted sum of a lane's 4 heads, the head-pair
+// exchange, the sum over index heads in head order, the maxima), so the
+// block scores are the same values the regular scan writes.
+struct SharedScanArgs {
+  IndexerArgs a;
+  const int32_t* group_start;   // [num_groups + 1]
+  const int32_t* group_seqs;    // member sequence ids
+  const int32_t* group_blocks;  // [num_groups] shared leading blocks
+  int num_seqs;
+};
+
+__global__ __launch_bounds__(512) void shared_scan_kernel(const SharedScanArgs sa) {
+  constexpr int QG = 4;      // 16-row groups per chunk
+  constexpr int kChunk = 8;  // query tokens per chunk
+  __shared__ float part[MSA_MAX_HEADS][kChunk][kBlockTokens];  // partial token scores
+  __shared__ float wmax[kChunk][4];                             // [token][32-token chunk]
+  __shared__ uint2 lut[128];
+  __shared__ int tok_row[kChunk], tok_pos[kChunk];  // query row b*Q + qi, position (-1: none)
+  const IndexerArgs& a = sa.a;
+  const int H = a.num_heads;
+  const int Q = a.q_per_seq;
+  const int Hq = a.num_q_heads;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int slice = lane >> 4;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int j = blockIdx.x, g = blockIdx.y;
+  const int c0 = kChunk * int(blockIdx.z);
+  // uniform over the workgroup: nothing to do past the group's shared blocks
+  // or past its member tokens
+  if (j >= min(sa.group_blocks[g], a.max_blocks)) return;
+  const int m0 = sa.group_start[g], m1 = sa.group_start[g + 1];
+  if (m1 <= m0 || c0 >= (m1 - m0) * Q) return;
+  const int lead = sa.group_seqs[m0];
+  if (lead < 0 || lead >= sa.num_seqs) return;
+
+  for (int i = threadIdx.x; i < 128; i += blockDim.x) lut[i] = make_uint2(kIdxLut.lo[i], kIdxLut.hi[i]);
+  const int p = a.block_table[int64_t(lead) * a.max_blocks + j];
+  const bool page_ok = p >= 0 && p < a.num_pages;
+  TileLoads t;
+  issue_loads(t, a.codes + int64_t(wave_u) * kCodePage, a.scales + int64_t(wave_u) * kScalePage,
+              p, page_ok, int64_t(H) * kCodePage, int64_t(H) * kScalePage,
+              (lane & 15) * kCodeRow + slice * 16, scale_word_offset(slice, lane & 15));
+  // this chunk's member tokens (token k of the group: sequence
+  // group_seqs[m0 + k / Q], query token k % Q), looked up once while the
+  // block's loads are in flight
+  const int T = (m1 - m0) * Q;
+  if (threadIdx.x < kChunk) {
+    const int k = c0 + int(threadIdx.x);
+    int row = 0, pos = -1;
+    if (k < T) {
+      const int m = k / Q, qi = k - m * Q;
+      const int bb = sa.group_seqs[m0 + m];
+      if (bb >= 0 && bb < sa.num_seqs) {
+        const int L = a.seq_lens[bb];
+        row = bb * Q + qi;
+        if (L >= Q && L <= a.max_blocks * kBlockTokens) pos = L - Q + qi;
+      }
+    }
+    tok_row[threadIdx.x] = row;
+    tok_pos[threadIdx.x] = pos;
+  }
+  __syncthreads();  // the lookup table and the token list
+  v8i kop[8];
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    const uint32_t sj = tile_scales(t.s, jj);
+    kop[jj] = dequant32(t.c[jj], lut[sj & 0x7F], lut[(sj >> 8) & 0x7F]);
+  }
+
+  const int part_lane = (lane >> 5) * kBlockTokens + (lane & 31);
+  // query operands and weights of tokens c0 .. c0 + 7
+  v8i qop[QG];
+  float wv[QG][4];
+#pragma unroll
+  for (int rg = 0; rg < QG; ++rg) {
+    const int R = 16 * rg + (lane & 15);
+    qop[rg] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    if (tok_pos[R >> 3] >= 0) {
+      const uint4* qp = reinterpret_cast<const uint4*>(
+          a.q + (int64_t(tok_row[R >> 3]) * Hq + wave * kHeadsPerKv + (R & 7)) * kHeadDim +
+          slice * 32);
+      qop[rg] = q_operand(qp[0], qp[1]);
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int R2 = 16 * rg + 4 * slice + v;
+      wv[rg][v] = tok_pos[R2 >> 3] >= 0
+                      ? a.w[int64_t(tok_row[R2 >> 3]) * Hq + wave * kHeadsPerKv + (R2 & 7)]
+                      : 0.0f;
+    }
+  }
+  // ReLU-weighted head sums per token, head pairs combined, to LDS
+  float* pw = &part[wave][0][0] + part_lane;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float s2[2][QG];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+#pragma unroll
+      for (int rg = 0; rg < QG; ++rg) {
+        const v4f acc = mfma_fp8_16x16x128(qop[rg], kop[2 * i + e], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+        float s = wv[rg][0] * fmaxf(acc[0], 0.0f);
+        s += wv[rg][1] * fmaxf(acc[1], 0.0f);
+        s += wv[rg][2] * fmaxf(acc[2], 0.0f);
+        s += wv[rg][3] * fmaxf(acc[3], 0.0f);
+        s2[e][rg] = s;
+      }
+    }
+#pragma unroll
+    for (int rg = 0; rg < QG; ++rg) {
+      const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(s2[0][rg]),
+                                                       __float_as_uint(s2[1][rg]), false, false);
+      pw[2 * rg * kBlockTokens + 32 * i] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+  }
+  __syncthreads();
+  // sum over index heads and maximum over the visible tokens, in units of
+  // (token pair, 32-token chunk) spread over the waves
+  for (int u = wave_u; u < 16; u += H) {
+    const int tq = 2 * (u >> 2) + (lane >> 5);
+    const int tt = 32 * (u & 3) + (lane & 31);
+    float m = 0.0f;
+    if (j * kBlockTokens + tt <= tok_pos[tq]) {  // visible (tok_pos -1: no token)
+      float sum = 0.0f;
+      for (int h = 0; h < H; ++h) sum += part[h][tq][tt];
+      m = fmaxf(m, sum);
+    }
+    const uint32_t v = row16_max_u32(__float_as_uint(m));
+    const uint32_t r0 = __builtin_amdgcn_readlane(int(v), 15), r1 = __builtin_amdgcn_readlane(int(v), 31);
+    const uint32_t r2 = __builtin_amdgcn_readlane(int(v), 47), r3 = __builtin_amdgcn_readlane(int(v), 63);
+    if (lane == 0) {
+      wmax[2 * (u >> 2)][u & 3] = __uint_as_float(max(r0, r1));
+      wmax[2 * (u >> 2) + 1][u & 3] = __uint_as_float(max(r2, r3));
+    }
+  }
+  __syncthreads();
+  if (wave == 0 && lane < kChunk && j * kBlockTokens <= tok_pos[lane]) {
+    const float* w4 = wmax[lane];
+    const float mx = fmaxf(fmaxf(w4[0], w4[1]), fmaxf(w4[2], w4[3]));
+    a.bscore[int64_t(tok_row[lane]) * a.max_blocks + j] = page_ok ? mx : 0.0f;
+  }
+}
+
 // Selection kernel: one wavefront per query token (topk_select.h).
 __global__ __launch_bounds__(64) void select_kernel(const float* __restrict__ bscore,
                                                     const int32_t* __restrict__ seq_lens,
@@ -315,8 +473,10 @@ static msa_status launch_scan(const msa_pool_desc* idx, const uint8_t* idx_codes
                               const uint8_t* idx_scales, const uint8_t* q_fp8, const float* head_w,
                               int32_t num_q_heads, const int32_t* block_table, int32_t max_blocks,
                               const int32_t* seq_lens, int32_t num_seqs, int32_t q_per_seq,
-                              float* block_scores, hipStream_t s) {
+                              float* block_scores, hipStream_t s,
+                              const int32_t* seq_skip = nullptr, IndexerArgs* args_out = nullptr) {
   IndexerArgs a;
+  a.seq_skip = seq_skip;
   a.codes = idx_codes;
   a.scales = idx_scales;
   a.num_pages = idx->num_pages;
@@ -340,6 +500,7 @@ static msa_status launch_scan(const msa_pool_desc* idx, const uint8_t* idx_codes
   a.blocks_per_wg = bpw;
   const dim3 grid((max_blocks + bpw - 1) / bpw, num_seqs);
   const dim3 block(64 * idx->num_heads);
+  if (args_out) *args_out = a;
   const int qg_pow2 = qg == 1 ? 1 : (qg == 2 ? 2 : 4);
   const size_t lds = size_t(2) * idx->num_heads * (2 * qg_pow2) * MSA_BLOCK_TOKENS * sizeof(float);
   if (qg_pow2 == 1)
@@ -386,6 +547,53 @@ extern "C" msa_status msa_indexer_scan(const msa_pool_desc* idx, const uint8_t* 
   return launch_scan(idx, idx_codes, idx_scales, q_fp8, head_w, num_q_heads, block_table,
                      max_blocks, seq_lens, num_seqs, q_per_seq, block_scores,
                      static_cast<hipStream_t>(stream));
+}
+
+extern "C" msa_status msa_indexer_scan_shared(
+    const msa_pool_desc* idx, const uint8_t* idx_codes, const uint8_t* idx_scales,
+    const uint8_t* q_fp8, const float* head_w, int32_t num_q_heads, const int32_t* block_table,
+    int32_t max_blocks, const int32_t* seq_lens, int32_t num_seqs, int32_t q_per_seq,
+    int32_t num_groups, const int32_t* group_start, const int32_t* group_seqs,
+    const int32_t* group_blocks, int32_t max_group_blocks, const int32_t* seq_shared_blocks,
+    float* block_scores, void* stream) {
+  using namespace msa;
+  if (!idx) return MSA_ERR_INVALID_ARG;
+  msa_status st = check_indexer_shape(num_seqs, q_per_seq, max_blocks);
+  if (st != MSA_OK) return st;
+  if (idx->head_dim != MSA_HEAD_DIM || idx->block_tokens != MSA_BLOCK_TOKENS)
+    return MSA_ERR_UNSUPPORTED;
+  if (idx->num_heads < 1 || idx->num_heads > MSA_MAX_HEADS) return MSA_ERR_UNSUPPORTED;
+  if (num_q_heads != MSA_HEADS_PER_KV * idx->num_heads) return MSA_ERR_UNSUPPORTED;
+  if (idx->num_pages <= 0 || idx->num_pages > 0x7FFFFFFF) return MSA_ERR_INVALID_ARG;
+  if (num_groups < 0 || num_groups > 65535) return MSA_ERR_INVALID_ARG;
+  if (num_groups > 0 && (max_group_blocks < 1 || max_group_blocks > max_blocks))
+    return MSA_ERR_INVALID_ARG;
+  if (num_seqs == 0) return MSA_OK;
+  if (!idx_codes || !idx_scales || !q_fp8 || !head_w || !block_table || !seq_lens || !block_scores)
+    return MSA_ERR_INVALID_ARG;
+  if (num_groups > 0 && (!group_start || !group_seqs || !group_blocks || !seq_shared_blocks))
+    return MSA_ERR_INVALID_ARG;
+  if (misaligned(idx_codes, 15) || misaligned(idx_scales, 15) || misaligned(q_fp8, 15) ||
+      misaligned(head_w, 3) || misaligned(block_table, 3) || misaligned(seq_lens, 3) ||
+      misaligned(block_scores, 3) || misaligned(group_start, 3) || misaligned(group_seqs, 3) ||
+      misaligned(group_blocks, 3) || misaligned(seq_shared_blocks, 3))
+    return MSA_ERR_INVALID_ARG;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  SharedScanArgs sa;
+  st = launch_scan(idx, idx_codes, idx_scales, q_fp8, head_w, num_q_heads, block_table, max_blocks,
+                   seq_lens, num_seqs, q_per_seq, block_scores, s,
+                   num_groups > 0 ? seq_shared_blocks : nullptr, &sa.a);
+  if (st != MSA_OK || num_groups == 0) return st;
+  sa.group_start = group_start;
+  sa.group_seqs = group_seqs;
+  sa.group_blocks = group_blocks;
+  sa.num_seqs = num_seqs;
+  // z: chunks of 8 member tokens (a group has at most num_seqs members)
+  const int64_t chunks = (int64_t(num_seqs) * q_per_seq + 7) / 8;
+  hipLaunchKernelGGL(shared_scan_kernel,
+                     dim3(unsigned(max_group_blocks), unsigned(num_groups), unsigned(chunks)),
+                     dim3(64 * idx->num_heads), 0, s, sa);
+  return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
 }
 
 extern "C" msa_status msa_indexer_select(const float* block_scores, const int32_t* seq_lens,

@@ -500,3 +500,77 @@ def test_workload_parity(nb, ci):
         say(f"workload {ci}: oracle on sequence {b} (length {wl.seq_lens[b]})")
         fails += S.check_sequence(wl, b, ids, sc, o)
     assert not fails, "\n".join(fails[:20])
+
+
+# Shared-prefix scan: groups of sequences whose leading blocks map to the
+# same pages are scored with one read and dequantisation per shared block;
+# the block scores must be the plain scan's, bit for bit, and the decode on
+# them must pass the oracle. Cases: a member whose last shared block is only
+# partly visible (L = 130, Q = 2), two groups plus an ungrouped sequence,
+# nine members with Q = 1 (two 8-token chunks), three members with Q = 8.
+SHARED = [
+    ([1000, 700, 3000, 130, 2600, 900], 2, [([0, 1, 3], 6), ([2, 4], 20)]),
+    ([2300] * 9 + [500], 1, [(list(range(9)), 17)]),
+    ([4100, 4000, 3000], 8, [([0, 1, 2], 23)]),
+]
+
+
+@pytest.mark.parametrize("lens,q,shared", SHARED)
+def test_shared_prefix_scan(nb, lens, q, shared):
+    from msa_workloads.device import shared_groups
+    say(f"shared prefix scan lens={lens} q={q} shared={shared}")
+    wl = tiny_config(lens, q, seed=70 + q, shared=shared)
+    pools = S.fill_pools(wl, nb)
+    inp = S.device_inputs(wl)
+    groups = shared_groups(wl)
+    assert groups[3] > 0
+    ic, isc = pools[synth.STREAM_IDX]
+    tq = wl.num_q_tokens
+    ref = torch.full((tq, wl.max_blocks), -1.0, dtype=torch.float32, device="cuda")
+    got = torch.full((tq, wl.max_blocks), -2.0, dtype=torch.float32, device="cuda")
+    nb.msa_indexer_scan(ic, isc, inp["q_idx"], inp["w"], inp["block_table"], inp["seq_lens"], q, ref)
+    nb.msa_indexer_scan_shared(ic, isc, inp["q_idx"], inp["w"], inp["block_table"],
+                               inp["seq_lens"], q, *groups, got)
+    torch.cuda.synchronize()
+    ref_np, got_np = ref.cpu().numpy(), got.cpu().numpy()
+    for b in range(wl.num_seqs):
+        for i, pos in enumerate(wl.positions(b)):
+            r = b * q + i
+            nbk = pos // 128 + 1
+            assert np.array_equal(ref_np[r, :nbk].view(np.uint32), got_np[r, :nbk].view(np.uint32)), \
+                f"seq {b} token {i}: shared-prefix scores differ from the plain scan"
+    # the decode step on the shared-prefix scores, against the oracle
+    ids = torch.empty((tq, wl.topk + 1), dtype=torch.int32, device="cuda")
+    sc = torch.empty((tq, wl.topk + 1), dtype=torch.float32, device="cuda")
+    o = torch.empty((tq, wl.num_q_heads, 128), dtype=torch.float32, device="cuda")
+    kc, ks = pools[synth.STREAM_K]
+    vc, vs = pools[synth.STREAM_V]
+    ws = nb.attn_workspace(wl.num_seqs, q, wl.num_q_heads, wl.topk + 1)
+    nb.msa_sparse_attn_select_decode(kc, ks, vc, vs, inp["q_attn"], inp["block_table"],
+                                     inp["seq_lens"], q, got, 1.0 / math.sqrt(128), o, ws,
+                                     out_ids=ids)
+    nb.msa_indexer_select(got, inp["seq_lens"], q, torch.empty_like(ids), sc)
+    ids_np, sc_np, o_np = _to_np(dict(ids=ids, scores=sc, o=o))
+    _structural(wl, ids_np)
+    fails = []
+    for b in range(wl.num_seqs):
+        fails += S.check_sequence(wl, b, ids_np, sc_np, o_np)
+    assert not fails, "\n".join(fails[:20])
+
+
+def test_shared_prefix_scan_without_groups_is_plain_scan(nb):
+    say("shared prefix scan, no groups")
+    wl = tiny_config([2000, 900, 130], 2, seed=77)
+    pools = S.fill_pools(wl, nb)
+    inp = S.device_inputs(wl)
+    ic, isc = pools[synth.STREAM_IDX]
+    tq = wl.num_q_tokens
+    ref = torch.full((tq, wl.max_blocks), -1.0, dtype=torch.float32, device="cuda")
+    got = torch.full((tq, wl.max_blocks), -1.0, dtype=torch.float32, device="cuda")
+    nb.msa_indexer_scan(ic, isc, inp["q_idx"], inp["w"], inp["block_table"], inp["seq_lens"], 2, ref)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    nb.msa_indexer_scan_shared(ic, isc, inp["q_idx"], inp["w"], inp["block_table"],
+                               inp["seq_lens"], 2, torch.zeros(1, **i32), torch.zeros(0, **i32),
+                               torch.zeros(0, **i32), 0, torch.zeros(wl.num_seqs, **i32), got)
+    torch.cuda.synchronize()
+    assert torch.equal(ref.view(torch.int32), got.view(torch.int32))

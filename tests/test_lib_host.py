@@ -154,6 +154,32 @@ def test_two_stage_indexer_rejects_before_launch(L):
     assert sel(256, 256, 4, 1, 9, 16, 256, None, None) == 2
 
 
+def test_shared_prefix_scan_rejects_before_launch(L):
+    f = L.msa_indexer_scan_shared
+    d = ctypes.byref(_desc())
+
+    def call(desc=d, q=32, mb=4, ns=1, qps=1, ng=1, gs=256, gq=256, gb=256, mgb=2, ssb=256,
+             bs=256, ptr=256):
+        return f(desc, ptr, ptr, ptr, ptr, q, ptr, mb, ptr, ns, qps, ng, gs, gq, gb, mgb, ssb, bs,
+                 None)
+    assert call(desc=None) == 1
+    assert call(q=24) == 2
+    assert call(qps=9) == 2
+    assert call(ng=-1) == 1
+    assert call(ng=65536) == 1
+    assert call(mgb=0) == 1                      # groups need shared blocks
+    assert call(mgb=5) == 1                      # more than max_blocks
+    assert call(ns=0) == 0
+    assert call(gs=None) == 1
+    assert call(gq=None) == 1
+    assert call(gb=None) == 1
+    assert call(ssb=None) == 1
+    assert call(gs=4096 + 2) == 1                # misaligned group arrays
+    assert call(ssb=4096 + 1) == 1
+    assert call(bs=None) == 1
+    assert call(ptr=None) == 1
+
+
 def test_scale_layout_view_matches_header_formula():
     import torch
     from nvfp4_kv_cache_amd import scales_rows
