@@ -20,13 +20,15 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 from msa_workloads import synth  # noqa: E402
-from msa_workloads.device import STREAMS, device_inputs, fill_pools, page_rows  # noqa: E402,F401
+from msa_workloads.device import (  # noqa: E402,F401
+    STREAMS, device_inputs, fill_pools, page_rows, shared_groups)
 
 
 def run_step(nb, wl, pools, inp, ws_idx=None, ws_attn=None, out=None, fused=True):
     """One decode step on the GPU.
 
-    fused=True is the launch sequence bench.py times: msa_indexer_scan, then
+    fused=True is the launch sequence bench.py times: msa_indexer_scan (or
+    msa_indexer_scan_shared when sequences share leading pages), then
     msa_sparse_attn_select_decode (selection inside the attention launch);
     msa_indexer_select on the same block scores then supplies the selected
     blocks' scores and must reproduce the ids. fused=False runs
@@ -48,8 +50,13 @@ def run_step(nb, wl, pools, inp, ws_idx=None, ws_attn=None, out=None, fused=True
     scale = 1.0 / math.sqrt(128)
     if fused:
         bscores = ws_idx[: tq * wl.max_blocks * 4].view(torch.float32).view(tq, wl.max_blocks)
-        nb.msa_indexer_scan(ic, isc, inp["q_idx"], inp["w"], inp["block_table"], inp["seq_lens"],
-                            wl.q_per_seq, bscores)
+        groups = shared_groups(wl, device=dev)
+        if groups[3] > 0:
+            nb.msa_indexer_scan_shared(ic, isc, inp["q_idx"], inp["w"], inp["block_table"],
+                                       inp["seq_lens"], wl.q_per_seq, *groups, bscores)
+        else:
+            nb.msa_indexer_scan(ic, isc, inp["q_idx"], inp["w"], inp["block_table"],
+                                inp["seq_lens"], wl.q_per_seq, bscores)
         nb.msa_sparse_attn_select_decode(kc, ks, vc, vs, inp["q_attn"], inp["block_table"],
                                          inp["seq_lens"], wl.q_per_seq, bscores, scale, out["o"],
                                          ws_attn, out_ids=out["ids"])
