@@ -11,10 +11,10 @@
 //   1. lane l holds the scores of blocks l, l+64, ..., l+64*31 of a chunk of
 //      2,048 (one chunk in registers; longer contexts loop over chunks) and
 //      their maximum;
-//   2. theta = the 16th largest of the 64 lane maxima (ranked by counting
-//      against broadcast LDS reads): the 16 lanes holding the largest maxima
-//      each own a block scoring >= theta, so at least 16 candidates reach
-//      theta and the top-16 are among them;
+//   2. theta = the 16th largest of the 64 lane maxima (a radix select with
+//      wavefront votes): the 16 lanes holding the largest maxima each own a
+//      block scoring >= theta, so at least 16 candidates reach theta and the
+//      top-16 are among them;
 //   3. the candidates >= theta (typically 16..25) are compacted into LDS at
 //      offsets from a DPP prefix sum of per-lane hit counts and ranked exactly
 //      by counting against broadcast LDS reads; with more than 64 of them
@@ -33,13 +33,11 @@ constexpr int kSelChunk = 64 * kSelPerLane;   // 2,048 candidates per chunk
 
 struct __align__(16) SelectScratch {
   uint32_t stage[kSelChunk];  // the current chunk's score bits, [k][lane]
-  uint64_t lanemax[64];       // (lane maximum << 6 | 63 - lane)
   uint64_t cand[64];          // compacted candidates (keys)
   uint64_t win[kTopK];
   int32_t id[kTopK];
   float score[kTopK];
   int32_t page[kTopK];
-  uint32_t theta;
 };
 
 __device__ __forceinline__ uint32_t score_bits(float s) { return __float_as_uint(s > 0.0f ? s : 0.0f); }
@@ -132,20 +130,23 @@ __device__ __forceinline__ int select_blocks(const float* row, int row_len, int 
 #pragma unroll
     for (int k = 0; k < kSelPerLane; ++k) m = max(m, v[k]);
   }
-  // 2. theta: the lane maximum of rank 15 among the 64, ranked as distinct
-  //    keys (maximum, then lane) by counting against broadcast LDS reads
-  const uint64_t mkey = (uint64_t(m) << 6) | uint64_t(63 - lane);
-  sc.lanemax[lane] = mkey;
-  wave_lds_sync();
-  int mrank = 0;
+  // 2. theta: the 16th largest of the 64 lane maxima, counted with
+  //    multiplicity, truncated below bit 11, by a radix select on the bit
+  //    patterns: the largest x with at least 16 lanes holding a maximum >= x,
+  //    decided two bits at a time from the top with three independent
+  //    wavefront votes and population counts (no LDS). Score bits are
+  //    non-negative, so bit 31 is clear. The truncation only admits the
+  //    few candidates within ~2^-11 (relative) below the 16th largest; the
+  //    exact ranking below sorts them out.
+  uint32_t theta = 0;
 #pragma unroll
-  for (int i = 0; i < 64; i += 2) {
-    const ulonglong2 two = *reinterpret_cast<const ulonglong2*>(&sc.lanemax[i]);
-    mrank += (two.x > mkey ? 1 : 0) + (two.y > mkey ? 1 : 0);
+  for (int bit = 29; bit >= 11; bit -= 2) {
+    const uint32_t t1 = theta | (1u << bit), t2 = theta | (2u << bit), t3 = theta | (3u << bit);
+    const int c1 = __popcll(__ballot(m >= t1));
+    const int c2 = __popcll(__ballot(m >= t2));
+    const int c3 = __popcll(__ballot(m >= t3));
+    theta = c3 >= kTopK ? t3 : (c2 >= kTopK ? t2 : (c1 >= kTopK ? t1 : theta));
   }
-  if (mrank == kTopK - 1) sc.theta = m;
-  wave_lds_sync();
-  const uint32_t theta = sc.theta;
   // 3. compact the candidates reaching theta: a per-lane bit mask of hits,
   //    positions from a prefix sum of its population count, hit values read
   //    back from the LDS copy of the chunk (hits are rare: a lane has 0..2)
