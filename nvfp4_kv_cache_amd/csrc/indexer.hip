@@ -90,6 +90,36 @@ __device__ __forceinline__ void issue_loads(TileLoads& t, const uint8_t* codes_w
   t.s = load_tile16(sr, scale_lane, 0);
 }
 
+// Block maxima of two query rows r0, r0 + 1 of a partial-score buffer
+// part[h][row][t] (rows of 128 floats, head stride hs floats): per token the
+// sum over heads 0 .. H-1 in head order, then the maximum, starting from 0,
+// over the tokens t <= lim of each row. Lane (row - r0) * 32 + t / 4 sums
+// tokens t .. t + 3 with 16-byte LDS reads; lim is the lane's row's last
+// visible token in the block (< 0: none). Returns both maxima (uniform).
+__device__ __forceinline__ float2 row_pair_max(const float* part, int hs, int H, int r0, int lim,
+                                               int lane) {
+  const int t0 = 4 * (lane & 31);
+  float m = 0.0f;
+  if (t0 <= lim) {
+    const float* pt = part + (r0 + (lane >> 5)) * kBlockTokens + t0;
+    float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int h = 0; h < H; ++h) {
+      const float4 v = *reinterpret_cast<const float4*>(pt + h * hs);
+      s.x += v.x;
+      s.y += v.y;
+      s.z += v.z;
+      s.w += v.w;
+    }
+    m = fmaxf(fmaxf(m, s.x), t0 + 1 <= lim ? s.y : 0.0f);
+    m = fmaxf(m, fmaxf(t0 + 2 <= lim ? s.z : 0.0f, t0 + 3 <= lim ? s.w : 0.0f));
+  }
+  // m >= 0: maxima of the bit patterns, per 32-lane half
+  const uint32_t v = row16_max_u32(__float_as_uint(m));
+  const uint32_t a0 = __builtin_amdgcn_readlane(int(v), 15), a1 = __builtin_amdgcn_readlane(int(v), 31);
+  const uint32_t a2 = __builtin_amdgcn_readlane(int(v), 47), a3 = __builtin_amdgcn_readlane(int(v), 63);
+  return make_float2(__uint_as_float(max(a0, a1)), __uint_as_float(max(a2, a3)));
+}
+
 // QG: 16-row MFMA groups per index head = ceil(8 * q_per_seq / 16).
 // One block in flight per wave: the next block's loads are issued as soon as
 // the current block's codes are consumed, and more resident waves hide the
@@ -208,42 +238,20 @@ __global__ __launch_bounds__(512) void indexer_kernel(const IndexerArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // Sum the heads, maximise over the block's visible tokens, store the block
-  // score. The reduction is spread over the waves in units of (query-token
-  // pair p, 32-token chunk c), lane = (query token - 2p) * 32 + t % 32:
-  // wave w takes units w, w + H, ..., sums the heads of each token and
-  // leaves the unit's maximum per query token in LDS; wave 0 combines the
-  // four chunk maxima one barrier later.
-  __shared__ float wmax[2][MSA_MAX_Q_PER_SEQ][4];  // [buffer][query token][chunk]
-  const int units = 4 * ((Q + 1) >> 1);
+  // Sum the heads, maximise over the block's visible tokens and store the
+  // block score, one query-token pair per wavefront (waves take pairs w,
+  // w + H, ...).
+  const int pairs = (Q + 1) >> 1;
   auto reduce_part = [&](int k, int buf) {
     const int blk = first + k * G;
-    for (int u = wave_u; u < units; u += H) {
-      const int qi = 2 * (u >> 2) + (lane >> 5);
-      const int t = 32 * (u & 3) + (lane & 31);
-      float m = 0.0f;
-      if (qi < Q && blk * kBlockTokens + t <= L - Q + qi) {
-        const float* pt = part + buf * part_stride + qi * kBlockTokens + t;
-        float sum = 0.0f;
-        for (int h = 0; h < H; ++h) sum += pt[h * QR * kBlockTokens];
-        m = fmaxf(m, sum);
-      }
-      // m >= 0: maxima of the bit patterns, per 32-lane half
-      const uint32_t v = row16_max_u32(__float_as_uint(m));
-      const uint32_t r0 = __builtin_amdgcn_readlane(int(v), 15), r1 = __builtin_amdgcn_readlane(int(v), 31);
-      const uint32_t r2 = __builtin_amdgcn_readlane(int(v), 47), r3 = __builtin_amdgcn_readlane(int(v), 63);
-      if (lane == 0) {
-        wmax[buf][2 * (u >> 2)][u & 3] = __uint_as_float(max(r0, r1));
-        wmax[buf][2 * (u >> 2) + 1][u & 3] = __uint_as_float(max(r2, r3));
-      }
-    }
-  };
-  auto finish = [&](int k, int buf) {
-    const int blk = first + k * G;
-    if (wave == 0 && lane < Q && blk * kBlockTokens <= L - Q + lane) {
-      const float* w4 = wmax[buf][lane];
-      const float m = fmaxf(fmaxf(w4[0], w4[1]), fmaxf(w4[2], w4[3]));
-      a.bscore[(qrow0 + lane) * a.max_blocks + blk] = pages[k] >= 0 ? m : 0.0f;
+    const bool page_ok = pages[k] >= 0;
+    for (int u = wave_u; u < pairs; u += H) {
+      const int qi = 2 * u + (lane >> 5);
+      const int lim = qi < Q ? L - Q + qi - blk * kBlockTokens : -1;
+      const float2 mx = row_pair_max(part + buf * part_stride, QR * kBlockTokens, H, 2 * u, lim, lane);
+      const int q = 2 * u + lane;
+      if (lane < 2 && q < Q && blk * kBlockTokens <= L - Q + q)
+        a.bscore[(qrow0 + q) * a.max_blocks + blk] = page_ok ? (lane ? mx.y : mx.x) : 0.0f;
     }
   };
   // one register buffer: the next block's loads are issued as soon as the
@@ -258,12 +266,7 @@ __global__ __launch_bounds__(512) void indexer_kernel(const IndexerArgs a) {
     issue(t, k + 1);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
-    if (k > 0) finish(k - 1, (k - 1) & 1);
     reduce_part(k, k & 1);
-  }
-  if (count_u > 0) {
-    __syncthreads();
-    finish(count_u - 1, (count_u - 1) & 1);
   }
 }
 
@@ -290,7 +293,6 @@ __global__ __launch_bounds__(512) void shared_scan_kernel(const SharedScanArgs s
   constexpr int QG = 4;      // 16-row groups per chunk
   constexpr int kChunk = 8;  // query tokens per chunk
   __shared__ float part[MSA_MAX_HEADS][kChunk][kBlockTokens];  // partial token scores
-  __shared__ float wmax[kChunk][4];                             // [token][32-token chunk]
   __shared__ uint2 lut[128];
   __shared__ int tok_row[kChunk], tok_pos[kChunk];  // query row b*Q + qi, position (-1: none)
   const IndexerArgs& a = sa.a;
@@ -392,30 +394,15 @@ __global__ __launch_bounds__(512) void shared_scan_kernel(const SharedScanArgs s
     }
   }
   __syncthreads();
-  // sum over index heads and maximum over the visible tokens, in units of
-  // (token pair, 32-token chunk) spread over the waves
-  for (int u = wave_u; u < 16; u += H) {
-    const int tq = 2 * (u >> 2) + (lane >> 5);
-    const int tt = 32 * (u & 3) + (lane & 31);
-    float m = 0.0f;
-    if (j * kBlockTokens + tt <= tok_pos[tq]) {  // visible (tok_pos -1: no token)
-      float sum = 0.0f;
-      for (int h = 0; h < H; ++h) sum += part[h][tq][tt];
-      m = fmaxf(m, sum);
-    }
-    const uint32_t v = row16_max_u32(__float_as_uint(m));
-    const uint32_t r0 = __builtin_amdgcn_readlane(int(v), 15), r1 = __builtin_amdgcn_readlane(int(v), 31);
-    const uint32_t r2 = __builtin_amdgcn_readlane(int(v), 47), r3 = __builtin_amdgcn_readlane(int(v), 63);
-    if (lane == 0) {
-      wmax[2 * (u >> 2)][u & 3] = __uint_as_float(max(r0, r1));
-      wmax[2 * (u >> 2) + 1][u & 3] = __uint_as_float(max(r2, r3));
-    }
-  }
-  __syncthreads();
-  if (wave == 0 && lane < kChunk && j * kBlockTokens <= tok_pos[lane]) {
-    const float* w4 = wmax[lane];
-    const float mx = fmaxf(fmaxf(w4[0], w4[1]), fmaxf(w4[2], w4[3]));
-    a.bscore[int64_t(tok_row[lane]) * a.max_blocks + j] = page_ok ? mx : 0.0f;
+  // sum over index heads and maximum over the visible tokens, one token
+  // pair per wavefront
+  for (int u = wave_u; u < kChunk / 2; u += H) {
+    const int tq = 2 * u + (lane >> 5);
+    const float2 mx = row_pair_max(&part[0][0][0], kChunk * kBlockTokens, H, 2 * u,
+                                   tok_pos[tq] - j * kBlockTokens, lane);
+    const int q = 2 * u + lane;
+    if (lane < 2 && j * kBlockTokens <= tok_pos[q])
+      a.bscore[int64_t(tok_row[q]) * a.max_blocks + j] = page_ok ? (lane ? mx.y : mx.x) : 0.0f;
   }
 }
 
