@@ -14,6 +14,8 @@ Modules
              and exact attention over the selected blocks, plus dense attention
   acceptance the acceptance rules used to compare another implementation
              with this oracle
+  insert     the cache-insertion path after the QKV projection (optional
+             RMSNorm, RoPE, NVFP4 insert of K / V / index keys, FP8 queries)
 
 Parity status (see each function's docstring for its pin):
   formats, nvfp4       pinned (library casts, closed forms, page byte counts)
@@ -25,5 +27,9 @@ Parity status (see each function's docstring for its pin):
       build's reading. The implementation of that reading is pinned by
       planted-block and invariance tests, but the reading itself is
       parity unpinned by the pages.
+  insert               pinned (bf16 against torch, closed-form RMSNorm and RoPE
+      cases, RoPE as a complex rotation, segment placement); which heads are
+      normalised, the rotate-half pairing and the angle formula are this
+      build's reading of "normalization, RoPE" on the pages.
 """
-from . import formats, nvfp4, msa, acceptance  # noqa: F401
+from . import formats, nvfp4, msa, acceptance, insert  # noqa: F401
