@@ -209,6 +209,44 @@ msa_status msa_indexer_select(const float* block_scores, const int32_t* seq_lens
                               int32_t topk, int32_t* out_ids, float* out_scores, void* stream);
 
 /*
+ * Cache insertion after the QKV projection, in one launch: the pages'
+ * fused projection / normalisation / RoPE / cache-insertion path, which
+ * avoids writing the intermediate tensor to HBM and reading it back
+ * (MiniMax-M3.1-Flash serving summary, section "Reduce both data movement
+ * and resource waits"); the projection itself is the caller's. Per token t:
+ *   1. optional RMSNorm of every query head (q and q_idx, weight q_norm_w)
+ *      and key head (k and k_idx, weight k_norm_w):
+ *      y = x / sqrt(mean(x^2) + rms_eps) * w; V is not normalised;
+ *   2. RoPE, rotate-half form, on channels 0 .. rotary_dim-1 of the q, q_idx,
+ *      k and k_idx heads: for i < rotary_dim/2 the pair (i, i + rotary_dim/2)
+ *      is rotated by positions[t] * rope_theta^(-2i/rotary_dim) radians;
+ *   3. k, v and k_idx are encoded to NVFP4 exactly as msa_nvfp4_quantize
+ *      would encode the fp32 values, into slot slot_mapping[t] of their pools
+ *      (slots < 0 or past the pool: not stored);
+ *   4. q and q_idx are rounded to FP8 E4M3 (nearest even, clamped to +-448).
+ * Arithmetic is fp32 (the angles are evaluated in fp64).
+ *   qkv          bf16 bit patterns [num_tokens][(8 Hkv + 8 Hidx + 2 Hkv +
+ *                Hidx) * 128]: heads q (8 Hkv), q_idx (8 Hidx), k (Hkv),
+ *                v (Hkv), k_idx (Hidx), Hkv = kv->num_heads,
+ *                Hidx = idx->num_heads; 16-byte aligned
+ *   positions    int32 [num_tokens]; slot_mapping int64 [num_tokens]
+ *   kv, idx      shapes of the K / V pools and of the index-key pool
+ *   q_norm_w, k_norm_w  float [128] or NULL (no normalisation)
+ *   rotary_dim   0, 32, 64, 96 or 128 (else MSA_ERR_UNSUPPORTED); rope_theta
+ *                > 1 when rotary_dim > 0
+ *   q_fp8        uint8 [num_tokens][8 Hkv][128]; q_idx_fp8 uint8
+ *                [num_tokens][8 Hidx][128]
+ * One kernel on `stream`; no workspace.
+ */
+msa_status msa_qkv_rope_insert(const uint16_t* qkv, int64_t num_tokens, const int32_t* positions,
+                               const int64_t* slot_mapping, const msa_pool_desc* kv,
+                               uint8_t* k_codes, uint8_t* k_scales, uint8_t* v_codes,
+                               uint8_t* v_scales, const msa_pool_desc* idx, uint8_t* idx_codes,
+                               uint8_t* idx_scales, const float* q_norm_w, const float* k_norm_w,
+                               float rms_eps, int32_t rotary_dim, float rope_theta,
+                               uint8_t* q_fp8, uint8_t* q_idx_fp8, void* stream);
+
+/*
  * Workspace bytes msa_sparse_attn_decode needs for its split partial results
  * (running max, denominator and unnormalised output per split). No initial
  * contents are required.

@@ -31,6 +31,8 @@ STREAM_QIDX = 3
 STREAM_QATTN = 4
 STREAM_W = 5
 STREAM_FILL = 6      # garbage written into never-used page slots by tests
+STREAM_PROJ = 7      # QKV projection rows (cache-insertion path)
+STREAM_NORMW = 8     # RMSNorm weights (cache-insertion path)
 
 _TABLE_CACHE: dict = {}
 
@@ -133,3 +135,20 @@ def head_weights(seed: int, num_q_tokens: int, num_heads: int) -> torch.Tensor:
     n = num_q_tokens * num_heads
     return uniform01_f32(seed, STREAM_W, torch.arange(n, dtype=torch.int64)).reshape(
         num_q_tokens, num_heads)
+
+
+def projection_rows(seed: int, num_tokens: int, width: int, device="cpu") -> torch.Tensor:
+    """bf16 projection rows [T, width]: N(0,1) draws times a per-(token, head)
+    magnitude 2^e, e uniform in -3..3 (exact), rounded to bf16 by torch's
+    cast (nearest even). Heads are 128 channels wide."""
+    n = num_tokens * width
+    x = normal_f32(seed, STREAM_PROJ, torch.arange(n, dtype=torch.int64, device=device))
+    heads = torch.arange(n, dtype=torch.int64, device=device) // 128
+    e = (hash_u32(seed, STREAM_PROJ + 100, heads) % 7).to(torch.float32) - 3.0
+    return (x * torch.exp2(e)).reshape(num_tokens, width).to(torch.bfloat16)
+
+
+def norm_weights(seed: int, which: int, device="cpu") -> torch.Tensor:
+    """RMSNorm weights fp32 [128], U(0.5, 1.5) (which: 0 queries, 1 keys)."""
+    u = uniform01_f32(seed, STREAM_NORMW, torch.arange(128, dtype=torch.int64, device=device) + 128 * which)
+    return u + 0.5

@@ -9,6 +9,6 @@ from .binding import (  # noqa: F401
     msa_attn_workspace_bytes, msa_indexer_decode, msa_indexer_scan, msa_indexer_scan_shared,
     msa_indexer_select,
     msa_indexer_workspace_bytes,
-    msa_nvfp4_quantize, msa_sparse_attn_decode, msa_sparse_attn_select_decode, msa_status_string,
+    msa_nvfp4_quantize, msa_qkv_rope_insert, msa_sparse_attn_decode, msa_sparse_attn_select_decode, msa_status_string,
     pool_desc, scales_rows,
 )

@@ -57,6 +57,8 @@ SIGNATURES = {
     "msa_sparse_attn_select_decode": (ctypes.c_int, [_DESC, _P, _P, _P, _P, _P, _I32, _P, _I32,
                                                      _P, _I32, _I32, _P, _I32, _P, _F32, _P, _P,
                                                      _SZ, _P]),
+    "msa_qkv_rope_insert": (ctypes.c_int, [_P, _I64, _P, _P, _DESC, _P, _P, _P, _P, _DESC, _P, _P,
+                                           _P, _P, _F32, _I32, _F32, _P, _P, _P]),
 }
 
 
@@ -180,6 +182,46 @@ def msa_nvfp4_quantize(src, slot_mapping, codes, scales, prepare=False):
     return _issue("msa_nvfp4_quantize", (
         ctypes.byref(desc), _ptr(src), _ptr(slot_mapping), src.shape[0], _ptr(codes),
         _ptr(scales), _stream()), prepare, keep=(desc,))
+
+
+def msa_qkv_rope_insert(qkv, positions, slot_mapping, k_pool, v_pool, idx_pool, q_fp8, q_idx_fp8,
+                        q_norm_w=None, k_norm_w=None, rms_eps=1e-6, rotary_dim=128,
+                        rope_theta=10000.0, prepare=False):
+    """The cache-insertion path after the QKV projection, in one launch.
+
+    qkv bfloat16 [T, (8 Hkv + 8 Hidx + 2 Hkv + Hidx) * 128] (heads q, q_idx,
+    k, v, k_idx), positions int32 [T], slot_mapping int64 [T]; pools are
+    (codes, scales) pairs (K and V with Hkv heads, the index keys with Hidx);
+    q_fp8 uint8 [T, 8 Hkv, 128] and q_idx_fp8 uint8 [T, 8 Hidx, 128] receive
+    the FP8 queries. q_norm_w / k_norm_w float32 [128] or None (no RMSNorm)."""
+    for (c, sc), nm in ((k_pool, "k"), (v_pool, "v"), (idx_pool, "idx")):
+        _check_pool(c, sc, nm)
+    _need(qkv, "qkv", torch.bfloat16, 2)
+    _need(positions, "positions", torch.int32, 1)
+    _need(slot_mapping, "slot_mapping", torch.int64, 1)
+    _need(q_fp8, "q_fp8", torch.uint8, 3)
+    _need(q_idx_fp8, "q_idx_fp8", torch.uint8, 3)
+    kv, idx = pool_desc(k_pool[0]), pool_desc(idx_pool[0])
+    if tuple(v_pool[0].shape) != tuple(k_pool[0].shape):
+        raise ValueError("the K and V pools must have the same shape")
+    hkv, hidx, t = kv.num_heads, idx.num_heads, qkv.shape[0]
+    width = (8 * hkv + 8 * hidx + 2 * hkv + hidx) * HEAD_DIM
+    if qkv.shape[1] != width:
+        raise ValueError(f"qkv rows must hold {width} channels, got {qkv.shape[1]}")
+    if positions.shape[0] != t or slot_mapping.shape[0] != t:
+        raise ValueError("positions and slot_mapping need one entry per token")
+    if tuple(q_fp8.shape) != (t, 8 * hkv, HEAD_DIM) or tuple(q_idx_fp8.shape) != (t, 8 * hidx, HEAD_DIM):
+        raise ValueError("q_fp8 / q_idx_fp8 shapes do not match the pools' head counts")
+    for w, nm in ((q_norm_w, "q_norm_w"), (k_norm_w, "k_norm_w")):
+        if w is not None:
+            _need(w, nm, torch.float32, 1)
+            if w.shape[0] != HEAD_DIM:
+                raise ValueError(f"{nm} must have {HEAD_DIM} entries")
+    return _issue("msa_qkv_rope_insert", (
+        _ptr(qkv), t, _ptr(positions), _ptr(slot_mapping), ctypes.byref(kv), _ptr(k_pool[0]),
+        _ptr(k_pool[1]), _ptr(v_pool[0]), _ptr(v_pool[1]), ctypes.byref(idx), _ptr(idx_pool[0]),
+        _ptr(idx_pool[1]), _ptr(q_norm_w), _ptr(k_norm_w), float(rms_eps), int(rotary_dim),
+        float(rope_theta), _ptr(q_fp8), _ptr(q_idx_fp8), _stream()), prepare, keep=(kv, idx))
 
 
 def msa_indexer_workspace_bytes(num_seqs: int, q_per_seq: int, max_blocks: int) -> int:

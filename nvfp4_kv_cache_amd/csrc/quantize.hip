@@ -42,33 +42,8 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_kernel(
     x[4 * i + 2] = v.z;
     x[4 * i + 3] = v.w;
   }
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
-
-  // scale byte = number of thresholds strictly below amax, tie -> even
-  int sb = 0;
-#pragma unroll
-  for (int step = 64; step > 0; step >>= 1)
-    if (thr[sb + step - 1] < amax) sb += step;
-  if (sb < 126 && amax == thr[sb] && (sb & 1)) sb += 1;
-  const float s = e4m3_to_float(sb);
-
-  // E2M1 midpoints times s: exact
-  const float m0 = 0.25f * s, m1 = 0.75f * s, m2 = 1.25f * s, m3 = 1.75f * s;
-  const float m4 = 2.5f * s, m5 = 3.5f * s, m6 = 5.0f * s;
-  uint32_t packed[2] = {0u, 0u};
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float a = fabsf(x[i]);
-    int below = (a > m0) + (a > m1) + (a > m2) + (a > m3) + (a > m4) + (a > m5) + (a > m6);
-    const bool tie = (a == m0) | (a == m1) | (a == m2) | (a == m3) | (a == m4) | (a == m5) |
-                     (a == m6);
-    below += (tie & (below & 1)) ? 1 : 0;
-    if (sb == 0) below = 0;
-    const uint32_t nib = (uint32_t(__float_as_uint(x[i]) >> 31) << 3) | uint32_t(below);
-    packed[i >> 3] |= nib << (4 * (i & 7));
-  }
+  uint32_t packed[2];
+  const int sb = nvfp4_encode_group(x, thr, packed);
 
   const int64_t page = slot / kBlockTokens;
   const int row = int(slot % kBlockTokens);

@@ -190,3 +190,28 @@ def test_scale_layout_view_matches_header_formula():
         for g in range(8):
             off = ((g // 2) * 16 + r % 16) * 16 + (r // 16) * 2 + g % 2
             assert int(rows[1, 2, r, g]) == (1 * h_ + 2) * 1024 + off
+
+
+def test_qkv_rope_insert_rejects_before_launch(L):
+    f = L.msa_qkv_rope_insert
+    kv, idx = ctypes.byref(_desc(heads=4)), ctypes.byref(_desc(heads=4))
+    fake = ctypes.c_void_p(1 << 20)   # never dereferenced: every call below fails a host check
+
+    def call(n=1, kvd=kv, idxd=idx, qn=None, eps=1e-6, rot=128, theta=1e4, qkv=fake):
+        return f(qkv, n, fake, fake, kvd, fake, fake, fake, fake, idxd, fake, fake, qn, None,
+                 eps, rot, theta, fake, fake, None)
+
+    assert call(n=-1) == 1
+    assert call(kvd=None) == 1
+    assert call(kvd=ctypes.byref(_desc(d=64))) == 2
+    assert call(idxd=ctypes.byref(_desc(heads=9))) == 2
+    assert call(idxd=ctypes.byref(_desc(pages=0))) == 1
+    for bad_rot in (-32, 16, 48, 160):
+        assert call(rot=bad_rot) == 2
+    assert call(theta=0.5) == 1                 # rope needs theta > 1
+    assert call(theta=float("nan")) == 1
+    assert call(qn=fake, eps=-1.0) == 1         # negative eps with a norm
+    assert call(n=0, qkv=None) == 0             # nothing to do
+    assert call(qkv=None) == 1
+    assert call(qkv=ctypes.c_void_p((1 << 20) + 8)) == 1   # qkv must be 16-byte aligned
+    assert call(n=1 << 31) == 2

@@ -129,3 +129,50 @@ def test_insert_norm_and_rope_reach_the_outputs():
     assert np.allclose(np.sqrt(np.mean(k ** 2, axis=-1)), 1.0)     # rotation keeps RMS
     assert np.allclose(v.reshape(2, -1), x[:, (16 + 1) * 128:(16 + 2) * 128])
     assert np.allclose(q, I.rope(I.rms_norm(x[:, :1024].reshape(2, 8, 128), w, 0.0), [11, 12], 128, 1e4))
+
+
+# ---------------------------------------------------------------- acceptance rules
+from oracle import acceptance as A  # noqa: E402
+
+
+def test_e4m3_window_rule():
+    rng = np.random.default_rng(4)
+    x = rng.normal(size=2000) * 30
+    b = F.e4m3_encode(x)
+    assert A.check_e4m3_within(b, x, 0.0) == (None, 0)
+    wrong = b.copy()
+    wrong[7] ^= 1                                            # a neighbouring code
+    assert A.check_e4m3_within(wrong, x, 0.0)[0] is not None
+    # on a midpoint +- a hair, delta admits the other side, and only that
+    m = np.float64(F.E4M3_MID[60])
+    xs = np.array([m * (1 - 1e-9), m * (1 + 1e-9)])
+    other = F.e4m3_encode(xs[::-1])
+    assert A.check_e4m3_within(other, xs, 0.0)[0] is not None
+    msg, n = A.check_e4m3_within(other, xs, 1e-6 * m)
+    assert msg is None and n == 2
+    far = F.e4m3_encode(xs * 1.3)
+    assert A.check_e4m3_within(far, xs, 1e-6 * m)[0] is not None
+
+
+def test_nvfp4_window_rule():
+    rng = np.random.default_rng(5)
+    x = rng.normal(size=(40, 128))
+    c, s = N.quantize(x.astype(np.float32))
+    assert A.check_nvfp4_within(c, s, x.astype(np.float32).astype(np.float64), 0.0) == (None, 0)
+    bad = c.copy()
+    bad[3, 10] ^= 0x01                                       # one magnitude step
+    assert A.check_nvfp4_within(bad, s, x.astype(np.float32).astype(np.float64), 0.0)[0] is not None
+    bad_s = s.copy()
+    bad_s[2, 1] += 1
+    assert A.check_nvfp4_within(c, bad_s, x.astype(np.float32).astype(np.float64), 0.0)[0] is not None
+    # an element on an E2M1 midpoint: the window admits either neighbour
+    g = np.zeros((1, 16))
+    g[0, 0] = 6.0                                            # amax 6 -> scale 1.0
+    g[0, 1] = 1.25 * (1 + 1e-12)                             # just above the 1 | 1.5 midpoint
+    cg, sg = N.quantize(g.astype(np.float32))
+    assert sg[0, 0] == F.e4m3_encode(1.0)
+    alt = cg.copy()
+    alt[0, 0] = (alt[0, 0] & 0x0F) | (0x2 << 4)             # magnitude index 2 (1.0) instead of 3
+    assert A.check_nvfp4_within(alt, sg, g, 0.0)[0] is not None
+    msg, n = A.check_nvfp4_within(alt, sg, g, 1e-6)
+    assert msg is None and n == 1
