@@ -14,6 +14,12 @@ calls (arguments marshalled once); --graph times HIP-graph replays instead. Prin
 line: query tokens/s (value), achieved HBM GB/s of the step, the indexer
 kernel against the HBM roofline (HIP events on the launch stream, eager
 launches), and the CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py --insert
+
+benchmarks the cache-insertion path instead (msa_qkv_rope_insert on 16,384
+new tokens, against the same transform done as separate passes) and prints
+its own JSON line in the same form.
 """
 from __future__ import annotations
 
@@ -43,6 +49,9 @@ def parse():
     p.add_argument("--workload", type=int, default=2,
                    help="workload index (0..4); 2 = 8 x 262,144 tokens")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--insert", action="store_true",
+                   help="benchmark the cache-insertion path (msa_qkv_rope_insert) on 16,384 "
+                        "new tokens instead of the decode step; prints its own JSON line")
     p.add_argument("--graph", action="store_true",
                    help="time HIP-graph replays of the captured step instead of eager launches")
     p.add_argument("--copy-calibration", action="store_true",
@@ -89,26 +98,31 @@ def algorithmic_bytes(wl, ids, dedup=False):
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_indexer_scan_long_context_8x256k.json")
 
 
-def kernel_source_digest() -> str:
-    """sha256 of the scan kernel's sources (a stored traffic figure is only
+SCAN_SOURCES = ("indexer.hip", "nvfp4_tile.h")
+INSERT_SOURCES = ("insert.hip", "nvfp4_encode.h", "nvfp4_tile.h")
+INSERT_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qkv_rope_insert_prefill_16k.json")
+
+
+def kernel_source_digest(sources=SCAN_SOURCES) -> str:
+    """sha256 of a kernel's sources (a stored traffic figure is only
     reported while the kernel it was measured on is unchanged)."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("indexer.hip", "nvfp4_tile.h"):
+    for f in sources:
         with open(os.path.join(ROOT, "nvfp4_kv_cache_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def measured_traffic(workload_name: str):
-    """HBM bytes per scan launch from the committed rocprofv3 counter record,
-    or None when there is none for this workload or the kernel changed."""
+def measured_traffic(workload_name: str, path=None, sources=SCAN_SOURCES):
+    """HBM bytes per launch from a committed rocprofv3 counter record, or
+    None when there is none for this workload or the kernel changed."""
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(path or TRAFFIC_FILE) as fh:
             rec = json.load(fh)
     except (OSError, ValueError):
         return None
-    if rec.get("workload") != workload_name or rec.get("kernel_source_sha256") != kernel_source_digest():
+    if rec.get("workload") != workload_name or rec.get("kernel_source_sha256") != kernel_source_digest(sources):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -183,6 +197,157 @@ def cpu_baseline(wl, nblk):
     }
 
 
+# The cache-insertion benchmark: 16,384 new tokens (8 sequences x the last
+# 2,048 positions of a 256K context), 4 KV heads and 4 index-key heads, so a
+# projection row holds 32 + 32 query heads and 4 + 4 + 4 key/value heads.
+INSERT_TOKENS, INSERT_HKV, INSERT_HIDX = 16384, 4, 4
+
+
+def insert_algorithmic_bytes(t, hkv, hidx):
+    """Bytes the insertion must move: the bf16 projection rows, positions and
+    slots, the two norm weight vectors; the NVFP4 K / V / index rows and the
+    FP8 queries written."""
+    rows = 8 * hkv + 8 * hidx + 2 * hkv + hidx
+    read = t * rows * 128 * 2 + t * (4 + 8) + 2 * 128 * 4
+    write = t * (2 * hkv + hidx) * IDX_BYTES_PER_TOKEN_HEAD + t * 8 * (hkv + hidx) * 128
+    return read + write
+
+
+def insert_cpu_baseline(rows, pos, qn, kn, sample):
+    """The oracle (as is) on the first `sample` tokens, scaled to tokens/s."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import insert as oins
+    from oracle import nvfp4
+
+    cores = len(os.sched_getaffinity(0))
+    bits = rows[:sample].cpu().view(__import__("torch").int16).numpy().view(np.uint16)
+    pools = [nvfp4.empty_pool(sample // 128 + 1, h) for h in (INSERT_HKV, INSERT_HKV, INSERT_HIDX)]
+    with threadpool_limits(limits=cores):
+        t0 = time.perf_counter()
+        oins.insert(bits, pos[:sample], np.arange(sample), *pools, qn, kn, 1e-6, 128, 1e4)
+        dt = time.perf_counter() - t0
+    return {"value": round(sample / dt, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"the first {sample} of {INSERT_TOKENS} tokens through oracle.insert "
+                      f"(fp64 RMSNorm and RoPE, NVFP4 and E4M3 encoding); measured {dt:.1f} s"}
+
+
+def insert_bench(args):
+    """One launch of msa_qkv_rope_insert per step over INSERT_TOKENS tokens."""
+    import numpy as np
+    import torch
+    import nvfp4_kv_cache_amd as nb
+    from msa_workloads import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    nb.lib()
+    t, hkv, hidx = INSERT_TOKENS, INSERT_HKV, INSERT_HIDX
+    width = (8 * hkv + 8 * hidx + 2 * hkv + hidx) * 128
+    dev = "cuda"
+    rows = synth.projection_rows(11, t, width, device=dev)
+    pos_np = np.tile(np.arange(262144 - 2048, 262144), t // 2048)
+    pos = torch.as_tensor(pos_np, dtype=torch.int32, device=dev)
+    slots = torch.arange(t, dtype=torch.int64, device=dev)
+    pools = [nb.empty_pool(t // 128, h) for h in (hkv, hkv, hidx)]
+    q = torch.empty((t, 8 * hkv, 128), dtype=torch.uint8, device=dev)
+    qi = torch.empty((t, 8 * hidx, 128), dtype=torch.uint8, device=dev)
+    qn, kn = synth.norm_weights(5, 0).to(dev), synth.norm_weights(5, 1).to(dev)
+    fused = nb.msa_qkv_rope_insert(rows, pos, slots, *pools, q, qi, q_norm_w=qn, k_norm_w=kn,
+                                   rms_eps=1e-6, rotary_dim=128, rope_theta=1e4, prepare=True)
+
+    # the unfused comparison: the same transform as separate passes that write
+    # and re-read the fp32 intermediate (torch elementwise ops for RMSNorm,
+    # RoPE and the FP8 query cast; msa_nvfp4_quantize for the three caches).
+    # cos/sin are precomputed once (fp64 angles), as a rotary cache would be.
+    ang = (torch.as_tensor(pos_np, dtype=torch.float64)[:, None] *
+           1e4 ** (-2.0 * torch.arange(64, dtype=torch.float64) / 128))
+    cos = ang.cos().float().to(dev)[:, None, :]
+    sin = ang.sin().float().to(dev)[:, None, :]
+    heads = [8 * hkv, 8 * hidx, hkv, hkv, hidx]
+
+    def unfused():
+        x = rows.float().view(t, sum(heads), 128)
+        xq, xqi, xk, xv, xki = x.split(heads, dim=1)
+
+        def norm(a, w):
+            return a * torch.rsqrt(a.pow(2).mean(-1, keepdim=True) + 1e-6) * w
+
+        def rope(a):
+            lo, hi = a[..., :64], a[..., 64:]
+            return torch.cat([lo * cos - hi * sin, hi * cos + lo * sin], dim=-1)
+
+        outs = [rope(norm(xq, qn)), rope(norm(xqi, qn)), rope(norm(xk, kn)), xv.contiguous(),
+                rope(norm(xki, kn))]
+        for (c, sc), src in zip(pools, outs[2:]):
+            nb.msa_nvfp4_quantize(src.contiguous(), slots, c, sc)
+        q.copy_(outs[0].clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8))
+        qi.copy_(outs[1].clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8))
+
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3
+
+    print(f"[bench] insert: {t} tokens, warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        fused()
+    t_w = time.perf_counter()
+    warmup_run = args.warmup
+    while (time.perf_counter() - t_w) * 1e3 < args.settle_ms:
+        for _ in range(10):
+            fused()
+        warmup_run += 10
+        torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    us = timed(fused, args.steps)
+    wall = (time.perf_counter() - t0) / args.steps * 1e6
+    for _ in range(3):
+        unfused()
+    us_unfused = timed(unfused, max(3, args.steps // 5))
+    alg = insert_algorithmic_bytes(t, hkv, hidx)
+    achieved = alg / (us * 1e-6) / 1e9
+    res = {
+        "metric": "cache-insert tokens/s (bf16 QKV projection rows -> RMSNorm, RoPE, NVFP4 K/V/index pages, FP8 queries)",
+        "value": round(t / (us * 1e-6), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "warmup_steps_run": warmup_run,
+        "ms_per_step": round(us / 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) x 2^U{-3..3} per head, bf16; U(0.5,1.5) norm weights)",
+        "config": {"workload": "prefill_insert_16k", "tokens": t, "kv_heads": hkv,
+                   "index_heads": hidx, "q_heads": 8 * hkv, "index_q_heads": 8 * hidx,
+                   "rotary_dim": 128, "rope_theta": 1e4, "rms_norm": True,
+                   "positions": "8 x (262,144 - 2,048 .. 262,143)"},
+        "wall_us_per_step": round(wall, 2),
+        "unfused_us_per_step": round(us_unfused, 2),
+        "unfused": "torch elementwise RMSNorm / RoPE / FP8 cast on the fp32 intermediate + 3 x msa_nvfp4_quantize",
+        "roofline": {"bound": "hbm", "kernel": "qkv_rope_insert_kernel (msa_qkv_rope_insert)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "algorithmic_bytes": alg,
+                     "traffic": measured_traffic("prefill_insert_16k", INSERT_TRAFFIC_FILE,
+                                                 INSERT_SOURCES)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] insert: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = insert_cpu_baseline(rows, pos_np, qn.cpu().numpy(), kn.cpu().numpy(), 256)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -192,6 +357,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.insert:
+        insert_bench(args)
         return
 
     import numpy as np

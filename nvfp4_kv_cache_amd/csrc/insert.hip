@@ -8,22 +8,29 @@
 // registers, and what leaves the kernel is the NVFP4 K / V / index-key rows
 // in their pages and the FP8 attention and index queries.
 //
-// One workgroup per token, 256 threads: eight lanes per 128-channel head row
-// (lane g of a row holds channels 16g .. 16g+15), 32 rows per pass. The
-// token's RoPE cos/sin (at most 64 angles) are evaluated once in fp64 and
-// staged in LDS as fp32; everything else is fp32:
-//   - RMSNorm: the row's sum of squares over its eight lanes (xor shuffles),
-//     x * (1 / sqrt(mean + eps)) * w;
-//   - RoPE (rotate-half): channel i < r/2 pairs with i + r/2, i.e. lane g
-//     with lane g +- r/32 of the same row (a shuffle per element);
+// One workgroup per two tokens, 256 threads: eight lanes per 128-channel
+// head row (lane g of a row holds channels 16g .. 16g+15), 32 rows per pass
+// over the two tokens' rows (152 rows: 5 passes at 95% occupancy). Per
+// token, LDS tables fold RMSNorm's weights into RoPE: for each channel c of
+// the query heads and of the key heads, A = w_c cos and B = -+ w_p sin
+// (partner p = c +- r/2), so an element costs y = inv * (x A + x_p B), with
+// inv = 1/sqrt(mean(x^2) + eps) of its row and x_p its partner's raw value.
+// The angles pos * theta^(-2i/r) are formed and reduced modulo 2 pi in fp64
+// (the frequencies come from the host's pow), their cosine and sine taken
+// in fp32; everything else is fp32:
+//   - the row's sum of squares over its eight lanes (xor shuffles);
+//   - the partner values by a lane shuffle (lane g with g +- r/32);
 //   - K, V, index keys: NVFP4 group encoding (nvfp4_encode_group), 8 code
-//     bytes and one scale byte into the token's page row;
+//     bytes and one scale byte into the token's page row; V is neither
+//     normalised nor rotated;
 //   - queries: E4M3 (nearest even, clamped to +-448) with the hardware
 //     conversion, 16 bytes per lane.
-#include <math.h>
+// Without RoPE the B term is not formed, and without normalisation either,
+// the inputs reach the encoders unchanged.
+#include <cmath>
 
 #include "msa_nvfp4.h"
-#include "nvfp4_tile.h"
+#include "nvfp4_encode.h"
 
 namespace msa {
 
@@ -31,6 +38,7 @@ __constant__ ScaleThresholds kInsertThr = make_scale_thresholds();
 
 struct InsertArgs {
   const uint16_t* qkv;  // bf16 [T][rows * 128]
+  int64_t num_tokens;
   int rows;             // heads per token row: 8 hkv + 8 hidx + 2 hkv + hidx
   int hkv, hidx;
   const int32_t* positions;
@@ -47,7 +55,7 @@ struct InsertArgs {
   const float* k_norm_w;  // [128] or null
   float eps;
   int rotary_dim;  // 0, 32, 64, 96 or 128
-  float theta;
+  double inv_freq[64];  // theta^(-2i/rotary_dim), i < rotary_dim / 2 (host libm pow)
   uint8_t* q_fp8;   // [T][8 hkv][128]
   uint8_t* qi_fp8;  // [T][8 hidx][128]
 };
@@ -61,77 +69,139 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float 
   return uint32_t(r);
 }
 
-__global__ __launch_bounds__(256) void qkv_rope_insert_kernel(const InsertArgs a) {
+constexpr int kInsertThreads = 256;                      // 4 wavefronts
+constexpr int kInsertRowsPerPass = kInsertThreads / 8;   // 32 head rows
+constexpr int kInsertTokens = 2;                         // tokens per workgroup
+
+__global__ __launch_bounds__(kInsertThreads) void qkv_rope_insert_kernel(const InsertArgs a) {
   __shared__ float thr[128];
-  __shared__ float cs[64], sn[64];
+  __shared__ float2 csn[kInsertTokens][64];  // cos, sin per angle
+  // [token][query, key class][A, B][channel]
+  __shared__ __attribute__((aligned(16))) float tab[kInsertTokens][2][2][128];
   const int tid = threadIdx.x;
-  const int64_t t = blockIdx.x;
-  if (tid < 128) thr[tid] = kInsertThr.t[tid];
+  const int64_t t0 = int64_t(blockIdx.x) * kInsertTokens;
+  const int ntok = int(min(int64_t(kInsertTokens), a.num_tokens - t0));
+  const int nrows = ntok * a.rows;  // the workgroup's head rows, token-major
   const int half = a.rotary_dim >> 1;
-  if (tid < half) {
-    // angle = pos * theta^(-2i/r), in fp64 so that long positions keep
-    // their accuracy; the rotation itself is fp32
-    const double inv = pow(double(a.theta), -2.0 * double(tid) / double(a.rotary_dim));
-    const double ang = double(a.positions[t]) * inv;
-    cs[tid] = float(cos(ang));
-    sn[tid] = float(sin(ang));
+  const int hq = kHeadsPerKv * a.hkv, hqi = kHeadsPerKv * a.hidx;
+  const int g = tid & 7;
+  // the tokens' rows are contiguous, so the workgroup's rows are one range;
+  // the first pass's loads go out before anything else, so their latency
+  // overlaps the table set-up, and each later pass is loaded while the
+  // previous one is computed
+  const uint16_t* src = a.qkv + t0 * int64_t(a.rows) * kHeadDim;
+  auto load_rows = [&](int r0, uint4& u0, uint4& u1) {
+    const int r = r0 + (tid >> 3);
+    if (r < nrows) {
+      const uint4* p = reinterpret_cast<const uint4*>(src + int64_t(r) * kHeadDim + 16 * g);
+      u0 = p[0];
+      u1 = p[1];
+    } else {
+      u0 = u1 = make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  uint4 c0, c1;
+  load_rows(0, c0, c1);
+  if (tid < 128) thr[tid] = kInsertThr.t[tid];
+  if (tid < kInsertTokens * 64) {
+    const int tt = tid >> 6, i = tid & 63;
+    if (i < half && tt < ntok) {
+      // angle = pos * theta^(-2i/r): the product and its reduction modulo
+      // 2 pi (two-term Cody-Waite split, fma) in fp64, so long positions
+      // keep their accuracy; the cosine and sine of the reduced angle in fp32
+      const double ang = double(a.positions[t0 + tt]) * a.inv_freq[i];
+      constexpr double kTwoPiHi = 6.283185307179586232e+00;   // 2 pi rounded to double
+      constexpr double kTwoPiLo = 2.449293598294706414e-16;   // 2 pi - kTwoPiHi
+      const double k = rint(ang * (1.0 / kTwoPiHi));
+      const float red = float(fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, ang)));
+      float sv, cv;
+      sincosf(red, &sv, &cv);
+      csn[tt][i] = make_float2(cv, sv);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int tt = 0; tt < kInsertTokens; ++tt) {
+    // Per channel of the token's query (class 0) and key (class 1) heads:
+    // with weight w (1 without normalisation), y = inv * (x A + x_p B) is
+    // RMSNorm then RoPE, A = w_c cos, B = -+ w_p sin for the partner channel
+    // p = c +- r/2 of the lower / upper half; A = w_c, B = 0 past r
+    const int cls = tid >> 7, c = tid & 127;
+    const float* w = cls ? a.k_norm_w : a.q_norm_w;
+    float A = w ? w[c] : 1.0f, B = 0.0f;
+    if (c < a.rotary_dim) {
+      const bool lower = c < half;
+      const int ai = lower ? c : c - half, pc = lower ? c + half : c - half;
+      const float2 v = csn[tt][ai];
+      A *= v.x;
+      B = (lower ? -1.0f : 1.0f) * (w ? w[pc] : 1.0f) * v.y;
+    }
+    tab[tt][cls][0][c] = A;
+    tab[tt][cls][1][c] = B;
   }
   __syncthreads();
 
-  const int hq = kHeadsPerKv * a.hkv, hqi = kHeadsPerKv * a.hidx;
-  const int g = tid & 7;
-  const int row_lane0 = (tid & 63) & ~7;
-  const int64_t slot = a.slot_mapping[t];
-  const int rg = a.rotary_dim >> 4;  // rotary groups of 16 channels (r / 16)
-  const int hg = rg >> 1;            // groups in each half (r / 32)
-  const bool rot = g < rg;
-  const int partner = row_lane0 + (g < hg ? g + hg : g - hg);
-  const uint16_t* src_t = a.qkv + t * int64_t(a.rows) * kHeadDim;
+  const int hg = a.rotary_dim >> 5;  // 16-channel groups in each half (r / 32)
+  const int partner = ((tid & 63) & ~7) + (g < hg ? g + hg : g >= 2 * hg ? g : g - hg);
+  const int b1 = hq, b2 = hq + hqi, b3 = b2 + a.hkv, b4 = b3 + a.hkv;
 
-  for (int r0 = 0; r0 < a.rows; r0 += 32) {
-    const int r = r0 + (tid >> 3);
-    // kind: 0 q, 1 q_idx, 2 k, 3 v, 4 k_idx (rows past the end: none)
-    const bool in = r < a.rows;
-    const int kind = r < hq ? 0 : r < hq + hqi ? 1 : r < hq + hqi + a.hkv ? 2
-                   : r < hq + hqi + 2 * a.hkv ? 3 : 4;
-    const int head = kind == 0 ? r : kind == 1 ? r - hq : kind == 2 ? r - hq - hqi
-                   : kind == 3 ? r - hq - hqi - a.hkv : r - hq - hqi - 2 * a.hkv;
+  for (int r0 = 0; r0 < nrows; r0 += kInsertRowsPerPass) {
+    const int rr = r0 + (tid >> 3);
+    const bool in = rr < nrows;
+    const int tt = rr >= a.rows ? 1 : 0;  // kInsertTokens == 2
+    const int r = rr - tt * a.rows;
+    const int64_t t = t0 + tt;
+    // kind: 0 q, 1 q_idx, 2 k, 3 v, 4 k_idx
+    const int kind = (r >= b1) + (r >= b2) + (r >= b3) + (r >= b4);
+    const int head = r - (kind == 0 ? 0 : kind == 1 ? b1 : kind == 2 ? b2 : kind == 3 ? b3 : b4);
     float x[16];
-    if (in) {
-      const uint4* p = reinterpret_cast<const uint4*>(src_t + int64_t(r) * kHeadDim + 16 * g);
-      const uint4 u0 = p[0], u1 = p[1];
-      const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+    {
+      const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         x[2 * i] = __uint_as_float(w[i] << 16);
         x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) x[i] = 0.0f;
     }
-    // RMSNorm (the eight lanes of a row share the sum; every lane shuffles)
-    const float* nw = kind == 0 || kind == 1 ? a.q_norm_w : kind == 3 ? nullptr : a.k_norm_w;
-    float ss = 0.0f;
+    if (r0 + kInsertRowsPerPass < nrows) load_rows(r0 + kInsertRowsPerPass, c0, c1);
+    const int cls = kind <= 1 ? 0 : 1;
+    const bool qk = kind != 3;
+    const bool norm = cls == 0 ? a.q_norm_w != nullptr : a.k_norm_w != nullptr;
+    // RMSNorm's scale (the eight lanes of a row share the sum of squares)
+    float inv = 1.0f;
+    if (a.q_norm_w || a.k_norm_w) {
+      float ss = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) ss += x[i] * x[i];
-    ss += __shfl_xor(ss, 1, 64);
-    ss += __shfl_xor(ss, 2, 64);
-    ss += __shfl_xor(ss, 4, 64);
-    if (nw) {
-      const float inv = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + a.eps);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) x[i] = x[i] * inv * nw[16 * g + i];
+      for (int i = 0; i < 16; ++i) ss = fmaf(x[i], x[i], ss);
+      ss += __shfl_xor(ss, 1, 64);
+      ss += __shfl_xor(ss, 2, 64);
+      ss += __shfl_xor(ss, 4, 64);
+      if (norm) inv = __builtin_amdgcn_rsqf(ss * (1.0f / kHeadDim) + a.eps);
     }
-    // RoPE (every lane shuffles; only rotary lanes of rotated kinds use it)
-    const bool rotate = rot && kind != 3;
+    const float4* A4 = reinterpret_cast<const float4*>(&tab[tt][cls][0][16 * g]);
+    if (a.rotary_dim > 0) {
+      // every lane shuffles; V lanes keep their values
+      float xp[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float xp = __shfl(x[i], partner, 64);
-      if (rotate) {
-        const int c = 16 * g + i;
-        if (g < hg) x[i] = x[i] * cs[c] - xp * sn[c];
-        else x[i] = x[i] * cs[c - half] + xp * sn[c - half];
+      for (int i = 0; i < 16; ++i) xp[i] = __shfl(x[i], partner, 64);
+      const float4* B4 = reinterpret_cast<const float4*>(&tab[tt][cls][1][16 * g]);
+      if (qk) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float4 av = A4[j], bv = B4[j];
+          const float aa[4] = {av.x, av.y, av.z, av.w}, bb[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            x[4 * j + e] = inv * fmaf(x[4 * j + e], aa[e], xp[4 * j + e] * bb[e]);
+        }
+      }
+    } else if (qk && norm) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 av = A4[j];
+        const float aa[4] = {av.x, av.y, av.z, av.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * j + e] = inv * (x[4 * j + e] * aa[e]);
       }
     }
     if (!in) continue;
@@ -142,6 +212,7 @@ __global__ __launch_bounds__(256) void qkv_rope_insert_kernel(const InsertArgs a
           make_uint4(e4m3_pack4(x[0], x[1], x[2], x[3]), e4m3_pack4(x[4], x[5], x[6], x[7]),
                      e4m3_pack4(x[8], x[9], x[10], x[11]), e4m3_pack4(x[12], x[13], x[14], x[15]));
     } else {
+      const int64_t slot = a.slot_mapping[t];
       const int64_t nslots = kind == 4 ? a.idx_slots : a.kv_slots;
       if (slot < 0 || slot >= nslots) continue;
       uint8_t* codes = kind == 2 ? a.k_codes : kind == 3 ? a.v_codes : a.i_codes;
@@ -196,6 +267,7 @@ extern "C" msa_status msa_qkv_rope_insert(
     return MSA_ERR_INVALID_ARG;
   InsertArgs a{};
   a.qkv = qkv;
+  a.num_tokens = num_tokens;
   a.hkv = kv->num_heads;
   a.hidx = idx->num_heads;
   a.rows = kHeadsPerKv * (a.hkv + a.hidx) + 2 * a.hkv + a.hidx;
@@ -213,10 +285,13 @@ extern "C" msa_status msa_qkv_rope_insert(
   a.k_norm_w = k_norm_w;
   a.eps = rms_eps;
   a.rotary_dim = rotary_dim;
-  a.theta = rope_theta;
+  for (int i = 0; i < rotary_dim / 2; ++i)
+    a.inv_freq[i] = std::pow(double(rope_theta), -2.0 * i / double(rotary_dim));
   a.q_fp8 = q_fp8;
   a.qi_fp8 = q_idx_fp8;
-  hipLaunchKernelGGL(qkv_rope_insert_kernel, dim3(unsigned(num_tokens)), dim3(256), 0,
+  hipLaunchKernelGGL(qkv_rope_insert_kernel,
+                     dim3(unsigned((num_tokens + kInsertTokens - 1) / kInsertTokens)),
+                     dim3(kInsertThreads), 0,
                      static_cast<hipStream_t>(stream), a);
   return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
 }

@@ -10,7 +10,7 @@
 // Format: NVFP4 as reproduced by the pages' 34,560 bytes per token
 // (MiniMax-M3.1-Flash lands in vLLM on day one, first paragraph).
 #include "msa_nvfp4.h"
-#include "nvfp4_tile.h"
+#include "nvfp4_encode.h"
 
 namespace msa {
 
