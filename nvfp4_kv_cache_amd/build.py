@@ -29,9 +29,11 @@ FLAGS = [
 ]
 
 
-# per-source extra flags: the scan's ReLU and maxima need no IEEE NaN
-# quieting (the inputs are finite by contract), which saves one VALU op each
-EXTRA = {"indexer.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
+# per-source extra flags: the scan's ReLU and maxima and the insertion's
+# clamps and maxima need no IEEE NaN quieting (the inputs are finite by
+# contract), which saves one VALU op each
+_NO_NAN = ["-mno-amdgpu-ieee", "-fno-honor-nans"]
+EXTRA = {"indexer.hip": _NO_NAN, "insert.hip": _NO_NAN}
 
 
 def sources():

@@ -15,9 +15,9 @@
 // the query heads and of the key heads, A = w_c cos and B = -+ w_p sin
 // (partner p = c +- r/2), so an element costs y = inv * (x A + x_p B), with
 // inv = 1/sqrt(mean(x^2) + eps) of its row and x_p its partner's raw value.
-// The angles pos * theta^(-2i/r) are formed and reduced modulo 2 pi in fp64
-// (the frequencies come from the host's pow), their cosine and sine taken
-// in fp32; everything else is fp32:
+// The angles pos * theta^(-2i/r) are formed (theta^(-2i/r) as
+// exp2(-2i/r * log2 theta)) and reduced modulo 2 pi in fp64, their cosine and
+// sine taken in fp32; everything else is fp32:
 //   - the row's sum of squares over its eight lanes (xor shuffles);
 //   - the partner values by a lane shuffle (lane g with g +- r/32);
 //   - K, V, index keys: NVFP4 group encoding (nvfp4_encode_group), 8 code
@@ -55,7 +55,7 @@ struct InsertArgs {
   const float* k_norm_w;  // [128] or null
   float eps;
   int rotary_dim;  // 0, 32, 64, 96 or 128
-  double inv_freq[64];  // theta^(-2i/rotary_dim), i < rotary_dim / 2 (host libm pow)
+  double log2_theta;  // log2(theta), from the host's libm in fp64
   uint8_t* q_fp8;   // [T][8 hkv][128]
   uint8_t* qi_fp8;  // [T][8 hidx][128]
 };
@@ -72,12 +72,14 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float 
 constexpr int kInsertThreads = 256;                      // 4 wavefronts
 constexpr int kInsertRowsPerPass = kInsertThreads / 8;   // 32 head rows
 constexpr int kInsertTokens = 2;                         // tokens per workgroup
+constexpr int kMaxRowsPerToken = 2 * kHeadsPerKv * MSA_MAX_HEADS + 3 * MSA_MAX_HEADS;
 
 __global__ __launch_bounds__(kInsertThreads) void qkv_rope_insert_kernel(const InsertArgs a) {
   __shared__ float thr[128];
   __shared__ float2 csn[kInsertTokens][64];  // cos, sin per angle
   // [token][query, key class][A, B][channel]
   __shared__ __attribute__((aligned(16))) float tab[kInsertTokens][2][2][128];
+  __shared__ uint16_t rowinfo[kMaxRowsPerToken];  // kind << 8 | head, per row of a token
   const int tid = threadIdx.x;
   const int64_t t0 = int64_t(blockIdx.x) * kInsertTokens;
   const int ntok = int(min(int64_t(kInsertTokens), a.num_tokens - t0));
@@ -103,20 +105,26 @@ __global__ __launch_bounds__(kInsertThreads) void qkv_rope_insert_kernel(const I
   uint4 c0, c1;
   load_rows(0, c0, c1);
   if (tid < 128) thr[tid] = kInsertThr.t[tid];
+  const int b1 = hq, b2 = hq + hqi, b3 = b2 + a.hkv, b4 = b3 + a.hkv;
+  for (int r = tid; r < a.rows; r += kInsertThreads) {
+    // kind: 0 q, 1 q_idx, 2 k, 3 v, 4 k_idx
+    const int kind = (r >= b1) + (r >= b2) + (r >= b3) + (r >= b4);
+    const int head = r - (kind == 0 ? 0 : kind == 1 ? b1 : kind == 2 ? b2 : kind == 3 ? b3 : b4);
+    rowinfo[r] = uint16_t(kind << 8 | head);
+  }
   if (tid < kInsertTokens * 64) {
     const int tt = tid >> 6, i = tid & 63;
     if (i < half && tt < ntok) {
-      // angle = pos * theta^(-2i/r): the product and its reduction modulo
+      // angle = pos * theta^(-2i/r): the frequency, the product and its reduction modulo
       // 2 pi (two-term Cody-Waite split, fma) in fp64, so long positions
       // keep their accuracy; the cosine and sine of the reduced angle in fp32
-      const double ang = double(a.positions[t0 + tt]) * a.inv_freq[i];
+      const double inv_freq = exp2(-2.0 * double(i) / double(a.rotary_dim) * a.log2_theta);
+      const double ang = double(a.positions[t0 + tt]) * inv_freq;
       constexpr double kTwoPiHi = 6.283185307179586232e+00;   // 2 pi rounded to double
       constexpr double kTwoPiLo = 2.449293598294706414e-16;   // 2 pi - kTwoPiHi
       const double k = rint(ang * (1.0 / kTwoPiHi));
       const float red = float(fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, ang)));
-      float sv, cv;
-      sincosf(red, &sv, &cv);
-      csn[tt][i] = make_float2(cv, sv);
+      csn[tt][i] = make_float2(cosf(red), sinf(red));
     }
   }
   __syncthreads();
@@ -143,17 +151,15 @@ __global__ __launch_bounds__(kInsertThreads) void qkv_rope_insert_kernel(const I
 
   const int hg = a.rotary_dim >> 5;  // 16-channel groups in each half (r / 32)
   const int partner = ((tid & 63) & ~7) + (g < hg ? g + hg : g >= 2 * hg ? g : g - hg);
-  const int b1 = hq, b2 = hq + hqi, b3 = b2 + a.hkv, b4 = b3 + a.hkv;
 
   for (int r0 = 0; r0 < nrows; r0 += kInsertRowsPerPass) {
     const int rr = r0 + (tid >> 3);
     const bool in = rr < nrows;
     const int tt = rr >= a.rows ? 1 : 0;  // kInsertTokens == 2
-    const int r = rr - tt * a.rows;
+    const int r = min(rr - tt * a.rows, a.rows - 1);
     const int64_t t = t0 + tt;
-    // kind: 0 q, 1 q_idx, 2 k, 3 v, 4 k_idx
-    const int kind = (r >= b1) + (r >= b2) + (r >= b3) + (r >= b4);
-    const int head = r - (kind == 0 ? 0 : kind == 1 ? b1 : kind == 2 ? b2 : kind == 3 ? b3 : b4);
+    const uint32_t info = rowinfo[r];
+    const int kind = int(info >> 8), head = int(info & 0xFFu);
     float x[16];
     {
       const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
@@ -285,8 +291,7 @@ extern "C" msa_status msa_qkv_rope_insert(
   a.k_norm_w = k_norm_w;
   a.eps = rms_eps;
   a.rotary_dim = rotary_dim;
-  for (int i = 0; i < rotary_dim / 2; ++i)
-    a.inv_freq[i] = std::pow(double(rope_theta), -2.0 * i / double(rotary_dim));
+  a.log2_theta = std::log2(double(rope_theta));
   a.q_fp8 = q_fp8;
   a.qi_fp8 = q_idx_fp8;
   hipLaunchKernelGGL(qkv_rope_insert_kernel,

@@ -13,7 +13,7 @@ namespace msa {
 // E4M3 value nearest to amax / 6 (ties to even, satfinite), found as the
 // number of thresholds strictly below amax; each code is the E2M1 magnitude
 // nearest to |x| / s (ties to even) with the sign bit of x, found by
-// comparing |x| with s x the E2M1 midpoints. Every threshold and product is
+// comparing |x| with s x the E2M1 midpoints (a binary search over the seven). Every threshold and product is
 // exact in fp32, so no division or rounding enters a decision. Element i's
 // nibble goes to bits 4 (i % 8) of packed[i / 8] (channel 2j in the low
 // nibble of byte j). Returns the scale byte.
@@ -34,12 +34,19 @@ __device__ __forceinline__ int nvfp4_encode_group(const float (&x)[16], const fl
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const float a = fabsf(x[i]);
-    int below = (a > m0) + (a > m1) + (a > m2) + (a > m3) + (a > m4) + (a > m5) + (a > m6);
-    const bool tie = (a == m0) | (a == m1) | (a == m2) | (a == m3) | (a == m4) | (a == m5) |
-                     (a == m6);
-    below += (tie & (below & 1)) ? 1 : 0;
-    if (sb == 0) below = 0;
-    const uint32_t nib = (uint32_t(__float_as_uint(x[i]) >> 31) << 3) | uint32_t(below);
+    // the number of midpoints strictly below a, by a three-level binary
+    // search; `upper` is the smallest midpoint >= a (the last one a did not
+    // exceed), which decides a tie
+    const bool g3 = a > m3;
+    const float t1 = g3 ? m5 : m1;
+    const bool g1 = a > t1;
+    const float t0 = g3 ? (g1 ? m6 : m4) : (g1 ? m2 : m0);
+    const bool g0 = a > t0;
+    int mag = (g3 ? 4 : 0) + (g1 ? 2 : 0) + (g0 ? 1 : 0);
+    const float upper = !g0 ? t0 : !g1 ? t1 : !g3 ? m3 : __builtin_huge_valf();
+    mag += (a == upper && (mag & 1)) ? 1 : 0;  // a tie goes to the even code
+    if (sb == 0) mag = 0;
+    const uint32_t nib = (uint32_t(__float_as_uint(x[i]) >> 31) << 3) | uint32_t(mag);
     packed[i >> 3] |= nib << (4 * (i & 7));
   }
   return sb;
