@@ -20,6 +20,13 @@ launches), and the CPU oracle timed on a bounded sample of the same workload.
 benchmarks the cache-insertion path instead (msa_qkv_rope_insert on 16,384
 new tokens, against the same transform done as separate passes) and prints
 its own JSON line in the same form.
+
+    python bench.py --mono
+
+benchmarks the one-launch decode step for low concurrency (msa_decode_mono:
+scan, selection and attention in one kernel) on the 1 x 4,096-token
+workload against the three-kernel step, with a sweep of small batches, and
+prints its own JSON line in the same form.
 """
 from __future__ import annotations
 
@@ -46,7 +53,12 @@ def parse():
     p.add_argument("--settle-ms", type=float, default=60.0,
                    help="after the warmup steps, keep running untimed steps until this much "
                         "warm-up time has passed (the GPU's clocks settle under sustained load)")
-    p.add_argument("--workload", type=int, default=2,
+    p.add_argument("--mono", action="store_true",
+                   help="benchmark the one-launch decode step (msa_decode_mono) on the "
+                        "1 x 4,096-token workload (or --workload), against the "
+                        "three-kernel step, plus a sweep of small batches; prints its own "
+                        "JSON line")
+    p.add_argument("--workload", type=int, default=None,
                    help="workload index (0..4); 2 = 8 x 262,144 tokens")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--insert", action="store_true",
@@ -98,7 +110,7 @@ def algorithmic_bytes(wl, ids, dedup=False):
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_indexer_scan_long_context_8x256k.json")
 
 
-SCAN_SOURCES = ("indexer.hip", "nvfp4_tile.h")
+SCAN_SOURCES = ("indexer.hip", "scan_body.h", "nvfp4_tile.h")
 INSERT_SOURCES = ("insert.hip", "nvfp4_encode.h", "nvfp4_tile.h")
 INSERT_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qkv_rope_insert_prefill_16k.json")
 
@@ -348,6 +360,161 @@ def insert_bench(args):
     print(json.dumps(res), flush=True)
 
 
+def mono_bench(args):
+    """msa_decode_mono (one launch) against msa_indexer_scan +
+    msa_sparse_attn_select_decode (the three-kernel step) on one workload
+    (default: 1 x 4,096 tokens, 1 query token), plus a sweep of small
+    batches; same JSON contract as the decode benchmark."""
+    import numpy as np
+    import torch
+    import nvfp4_kv_cache_amd as nb
+    from msa_workloads import get_config, synth, tiny_config
+    from msa_workloads.device import device_inputs, fill_pools
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    nb.lib()
+    scale = 1.0 / math.sqrt(128)
+    stream = torch.cuda.current_stream()
+
+    def setup(wl):
+        pools = fill_pools(wl, nb, garbage=False)
+        inp = device_inputs(wl)
+        tq = wl.num_q_tokens
+        ic, isc = pools[synth.STREAM_IDX]
+        kc, ks = pools[synth.STREAM_K]
+        vc, vs = pools[synth.STREAM_V]
+        r = dict(wl=wl, pools=pools, inp=inp)
+        r["ws_m"] = nb.mono_workspace(wl.num_seqs, wl.q_per_seq, wl.num_q_heads, wl.max_blocks)
+        r["ws_i"] = nb.indexer_workspace(wl.num_seqs, wl.q_per_seq, wl.max_blocks)
+        r["ws_a"] = nb.attn_workspace(wl.num_seqs, wl.q_per_seq, wl.num_q_heads, wl.topk + 1)
+        for k in ("m", "3"):
+            r["ids" + k] = torch.empty((tq, wl.topk + 1), dtype=torch.int32, device="cuda")
+            r["out" + k] = torch.empty((tq, wl.num_q_heads, 128), dtype=torch.float32,
+                                       device="cuda")
+        bsc = r["ws_i"][: tq * wl.max_blocks * 4].view(torch.float32).view(tq, wl.max_blocks)
+        r["mono"] = nb.msa_decode_mono(ic, isc, inp["q_idx"], inp["w"], kc, ks, vc, vs,
+                                       inp["q_attn"], inp["block_table"], inp["seq_lens"],
+                                       wl.q_per_seq, scale, r["outm"], r["ws_m"],
+                                       out_ids=r["idsm"], prepare=True)
+        scan = nb.msa_indexer_scan(ic, isc, inp["q_idx"], inp["w"], inp["block_table"],
+                                   inp["seq_lens"], wl.q_per_seq, bsc, prepare=True)
+        attn = nb.msa_sparse_attn_select_decode(kc, ks, vc, vs, inp["q_attn"],
+                                                inp["block_table"], inp["seq_lens"],
+                                                wl.q_per_seq, bsc, scale, r["out3"], r["ws_a"],
+                                                out_ids=r["ids3"], prepare=True)
+
+        def three():
+            scan()
+            attn()
+        r["three"] = three
+        return r
+
+    def settle(fn, n0):
+        t_w = time.perf_counter()
+        for _ in range(n0):
+            fn()
+        torch.cuda.synchronize()
+        n = n0
+        while (time.perf_counter() - t_w) * 1e3 < args.settle_ms:
+            for _ in range(20):
+                fn()
+            n += 20
+            torch.cuda.synchronize()
+        return n
+
+    def wall_us(fn, k):
+        t0 = time.perf_counter()
+        for _ in range(k):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / k * 1e6
+
+    def event_us(fn, k):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(k)]
+        for e0, e1 in ev:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e3
+
+    wl = get_config(0 if args.workload is None else args.workload)
+    print(f"[bench] mono: workload {wl.name}: filling pools", file=sys.stderr, flush=True)
+    r = setup(wl)
+    warm = settle(lambda: (r["mono"](), r["three"]()), args.warmup)
+    same = (torch.equal(r["idsm"], r["ids3"]) and
+            torch.equal(r["outm"].view(torch.int32), r["out3"].view(torch.int32)))
+    tq = wl.num_q_tokens
+    us_mono = wall_us(r["mono"], args.steps)
+    us_three = wall_us(r["three"], args.steps)
+    ev_mono = event_us(r["mono"], args.steps)
+    ev_three = event_us(r["three"], args.steps)
+    ids_np = r["idsm"].cpu().numpy()
+    idx_bytes, rest_bytes, union = algorithmic_bytes(wl, ids_np)
+    step_bytes = idx_bytes + rest_bytes
+    # every block's K/V is read once more than the selection needs (the
+    # partials of unselected blocks are computed and dropped)
+    kv_read = sum(wl.blocks_of(b) for b in range(wl.num_seqs)) * 2 * wl.num_kv_heads * \
+        KV_BYTES_PER_BLOCK_HEAD * wl.q_per_seq
+
+    sweep = []
+    for lens, q in [([4096] * 2, 1), ([4096] * 4, 1), ([8192], 1), ([16384], 1),
+                    ([4096] * 2, 2), ([4096], 4)]:
+        w2 = tiny_config(lens, q, seed=len(lens) * 10 + q, spare_pages=0, permute=False,
+                         name=f"{len(lens)}x{lens[0]}_q{q}")
+        r2 = setup(w2)
+        settle(lambda: (r2["mono"](), r2["three"]()), 5)
+        sweep.append({"workload": w2.name, "num_seqs": len(lens), "context_tokens": lens[0],
+                      "q_per_seq": q,
+                      "mono_us": round(wall_us(r2["mono"], args.steps), 2),
+                      "three_kernel_us": round(wall_us(r2["three"], args.steps), 2)})
+        del r2
+    res = {
+        "metric": "decode query-tokens/s + achieved HBM GB/s (indexer+sparse-attn, 1 layer)",
+        "value": round(tq / (us_mono * 1e-6), 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "warmup_steps_run": warm,
+        "settle_ms": args.settle_ms,
+        "ms_per_step": round(us_mono * 1e-3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "launch": "eager (prepared calls), one kernel per step (msa_decode_mono)",
+        "data": "synthetic (seeded N(0,1) fp32 sources quantised to NVFP4 on the GPU; "
+                "FP8 queries; U(0,1) head weights)",
+        "config": {"workload": wl.name, "num_seqs": wl.num_seqs,
+                   "context_tokens": int(max(wl.seq_lens)), "q_per_seq": wl.q_per_seq,
+                   "kv_heads": wl.num_kv_heads, "index_heads": wl.num_idx_heads,
+                   "q_heads": wl.num_q_heads, "head_dim": 128, "block_tokens": 128,
+                   "topk": wl.topk},
+        "achieved_hbm_gbs": round(step_bytes / (us_mono * 1e-6) / 1e9, 1),
+        "hbm_frac_of_peak": round(step_bytes / (us_mono * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes_per_step": int(step_bytes),
+        "kv_bytes_read_per_step": int(kv_read),
+        "three_kernel_us_per_step": round(us_three, 2),
+        "speedup_vs_three_kernel": round(us_three / us_mono, 3),
+        "bit_identical_to_three_kernel": bool(same),
+        "kernels_us": {"msa_decode_mono": round(ev_mono, 2),
+                       "three_kernel_step_events": round(ev_three, 2)},
+        "sweep": sweep,
+        "roofline": {"bound": "hbm", "kernel": "mono_kernel (msa_decode_mono)",
+                     "achieved": round(step_bytes / (ev_mono * 1e-6) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(step_bytes / (ev_mono * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes": int(step_bytes), "traffic": None},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_blocks)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -361,6 +528,11 @@ def main():
     if args.insert:
         insert_bench(args)
         return
+    if args.mono:
+        mono_bench(args)
+        return
+    if args.workload is None:
+        args.workload = 2
 
     import numpy as np
     import torch

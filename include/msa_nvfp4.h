@@ -309,6 +309,61 @@ msa_status msa_sparse_attn_select_decode(const msa_pool_desc* kv, const uint8_t*
                                          int32_t* out_ids, float softmax_scale, float* out,
                                          void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Workspace bytes msa_decode_mono needs: the fp32 block scores
+ * [num_seqs * q_per_seq][max_blocks] (at offset 0), the attention partials of
+ * every block, and the launch's arrival counters. Zero-fill it before its
+ * first use: the counters must start at zero, and every call leaves them zero.
+ */
+size_t msa_decode_mono_workspace_bytes(int32_t num_seqs, int32_t q_per_seq, int32_t num_q_heads,
+                                       int32_t max_blocks);
+
+/*
+ * The whole decode step in one kernel launch, for low concurrency: the index
+ * scan of msa_indexer_scan, the selection and the attention of
+ * msa_sparse_attn_select_decode, with the same ids and the same output bits
+ * as those two calls make when the attention runs one workgroup per selected
+ * block (num_seqs * q_per_seq * 4 KV heads * 17 <= 384). The pages keep a
+ * separate mono-kernel strategy for low concurrency to reduce launches, and
+ * note that one kernel arrangement need not suit every regime
+ * (MiniMax-M3.1-Flash serving summary, sections "AMD uses different
+ * conversion and communication mechanisms" and "Keep capacity, layer, and
+ * system results separate").
+ * How: the attention partial (m, l, o) of EVERY block of every query token
+ * and KV head is computed while the scan runs, and per (query token, KV head)
+ * a last workgroup waits for both, selects the 16 + 1 blocks from the scores
+ * and merges only their partials. That costs max_blocks x 73,728 bytes of K/V
+ * reads per sequence instead of 17 x 73,728, so the launch is bounded:
+ * num_seqs * q_per_seq * 4 * max_blocks <= 8192 (else MSA_ERR_UNSUPPORTED).
+ *   idx, idx_codes, idx_scales, q_idx_fp8, head_w   as msa_indexer_scan; the
+ *                index pool must have 4 heads
+ *   kv, k_*, v_*, q_fp8, num_q_heads, block_table, max_blocks, seq_lens,
+ *   num_seqs, q_per_seq, softmax_scale, out   as msa_sparse_attn_decode; the
+ *                KV pools must have 4 heads (num_q_heads = 32); the index and
+ *                KV pools share the block table
+ *   topk         must be 16
+ *   out_ids      int32 [num_seqs * q_per_seq][17] or NULL: the selected ids,
+ *                as msa_indexer_select writes them
+ *   workspace    msa_decode_mono_workspace_bytes(...) bytes, 256-byte aligned,
+ *                zero-filled before its first use (see above); it must not be
+ *                shared by calls that may overlap
+ * Device-side checks as msa_sparse_attn_select_decode. The launch's
+ * workgroups wait only for workgroups dispatched before them; each wait is
+ * still bounded (20 ms), and one that times out gives that query token zero
+ * output and ids -1 and sets the error word, the last 32-bit word of the
+ * msa_decode_mono_workspace_bytes(...) bytes, to 1; it stays set until the
+ * caller zeroes it.
+ */
+msa_status msa_decode_mono(const msa_pool_desc* idx, const uint8_t* idx_codes,
+                           const uint8_t* idx_scales, const uint8_t* q_idx_fp8,
+                           const float* head_w, const msa_pool_desc* kv, const uint8_t* k_codes,
+                           const uint8_t* k_scales, const uint8_t* v_codes,
+                           const uint8_t* v_scales, const uint8_t* q_fp8, int32_t num_q_heads,
+                           const int32_t* block_table, int32_t max_blocks,
+                           const int32_t* seq_lens, int32_t num_seqs, int32_t q_per_seq,
+                           int32_t topk, int32_t* out_ids, float softmax_scale, float* out,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -57,6 +57,9 @@ SIGNATURES = {
     "msa_sparse_attn_select_decode": (ctypes.c_int, [_DESC, _P, _P, _P, _P, _P, _I32, _P, _I32,
                                                      _P, _I32, _I32, _P, _I32, _P, _F32, _P, _P,
                                                      _SZ, _P]),
+    "msa_decode_mono_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
+    "msa_decode_mono": (ctypes.c_int, [_DESC, _P, _P, _P, _P, _DESC, _P, _P, _P, _P, _P, _I32, _P,
+                                       _I32, _P, _I32, _I32, _I32, _P, _F32, _P, _P, _SZ, _P]),
     "msa_qkv_rope_insert": (ctypes.c_int, [_P, _I64, _P, _P, _DESC, _P, _P, _P, _P, _DESC, _P, _P,
                                            _P, _P, _F32, _I32, _F32, _P, _P, _P]),
 }
@@ -410,3 +413,49 @@ def msa_sparse_attn_select_decode(k_codes, k_scales, v_codes, v_scales, q_fp8, b
         _ptr(q_fp8), hq, _ptr(block_table), max_blocks, _ptr(seq_lens), num_seqs, q_per_seq,
         _ptr(block_scores), topk, _ptr(out_ids), float(softmax_scale), _ptr(out),
         _ptr(workspace), workspace.numel(), _stream()), prepare, keep=(desc,))
+
+
+def msa_decode_mono_workspace_bytes(num_seqs: int, q_per_seq: int, num_q_heads: int,
+                                    max_blocks: int) -> int:
+    return int(lib().msa_decode_mono_workspace_bytes(num_seqs, q_per_seq, num_q_heads, max_blocks))
+
+
+def mono_workspace(num_seqs, q_per_seq, num_q_heads, max_blocks, device="cuda"):
+    """Workspace for msa_decode_mono, zero-filled (its counters must start at
+    zero; every call leaves them zero)."""
+    n = msa_decode_mono_workspace_bytes(num_seqs, q_per_seq, num_q_heads, max_blocks)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def mono_block_scores(workspace, num_seqs, q_per_seq, max_blocks):
+    """The block scores [T_q, max_blocks] a msa_decode_mono call left at the
+    start of its workspace (a view)."""
+    tq = num_seqs * q_per_seq
+    return workspace[: tq * max_blocks * 4].view(torch.float32).view(tq, max_blocks)
+
+
+def msa_decode_mono(idx_codes, idx_scales, q_idx_fp8, head_w, k_codes, k_scales, v_codes,
+                    v_scales, q_fp8, block_table, seq_lens, q_per_seq, softmax_scale, out,
+                    workspace, out_ids=None, topk=TOPK, prepare=False):
+    """The whole decode step (index scan, selection, sparse attention) in one
+    launch: out float32 [B*Q, Hq, 128], ids into out_ids int32 [B*Q, 17] when
+    given; workspace from mono_workspace()."""
+    _check_pool(idx_codes, idx_scales, "idx")
+    num_seqs, max_blocks, tq, hq = _check_attn_inputs(k_codes, k_scales, v_codes, v_scales, q_fp8,
+                                                      block_table, seq_lens, q_per_seq, out,
+                                                      workspace)
+    _need(q_idx_fp8, "q_idx_fp8", torch.uint8, 3)
+    _need(head_w, "head_w", torch.float32, 2)
+    if q_idx_fp8.shape != q_fp8.shape or head_w.shape != (tq, hq):
+        raise ValueError("q_idx_fp8 must match q_fp8 and head_w be [T_q, Hq]")
+    if out_ids is not None:
+        _need(out_ids, "out_ids", torch.int32, 2)
+        if out_ids.shape != (tq, topk + 1):
+            raise ValueError("out_ids must be [T_q, topk + 1]")
+    idesc, kdesc = pool_desc(idx_codes), pool_desc(k_codes)
+    return _issue("msa_decode_mono", (
+        ctypes.byref(idesc), _ptr(idx_codes), _ptr(idx_scales), _ptr(q_idx_fp8), _ptr(head_w),
+        ctypes.byref(kdesc), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales),
+        _ptr(q_fp8), hq, _ptr(block_table), max_blocks, _ptr(seq_lens), num_seqs, q_per_seq, topk,
+        _ptr(out_ids), float(softmax_scale), _ptr(out), _ptr(workspace), workspace.numel(),
+        _stream()), prepare, keep=(idesc, kdesc))

@@ -25,100 +25,13 @@
 #include "msa_nvfp4.h"
 #include "nvfp4_tile.h"
 #include "topk_select.h"
+#include "scan_body.h"
 
 namespace msa {
 
 static_assert(kTopK == MSA_TOPK, "selection size");
 
 __constant__ Fp8Lut kIdxLut = make_fp8_lut();
-
-struct IndexerArgs {
-  const uint8_t* codes;
-  const uint8_t* scales;
-  int64_t num_pages;
-  int num_heads;  // index-key heads = wavefronts per workgroup
-  const uint8_t* q;
-  const float* w;
-  int num_q_heads;
-  const int32_t* block_table;
-  int max_blocks;
-  const int32_t* seq_lens;
-  int q_per_seq;
-  int blocks_per_wg;
-  float* bscore;       // [num_seqs * q_per_seq][max_blocks]
-  const int32_t* seq_skip;  // [num_seqs] leading blocks scored by the shared pass, or null
-};
-
-constexpr int kMaxBlocksPerWg = 8;  // blocks per scan workgroup (page list size)
-
-// One block's worth of this wave's loads: 8 tiles x 16 code bytes and the
-// 16-byte scale word (2 scale bytes per tile) per lane.
-struct TileLoads {
-  uint4 c[8];
-  uint4 s;
-};
-
-// A buffer descriptor over `bytes` bytes at `base` (gfx9 layout: stride 0,
-// default format word). A buffer load past the record count returns zeros
-// and reads no memory.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, bytes, 0x00020000);
-}
-
-constexpr int kLoadNonTemporal = 2;  // buffer-load cache policy: streamed, not kept
-
-__device__ __forceinline__ uint4 load_tile16(__amdgpu_buffer_rsrc_t r, uint32_t lane_off, int uniform_off) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, uniform_off, kLoadNonTemporal);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
-// This wave's loads of one block. `live` (uniform) false stands for an
-// absent block (past the workgroup's count, or an unmapped page): the
-// descriptors then hold no records, every lane receives zeros and nothing is
-// read. There is no branch, so the wait the compiler places before a block's
-// first use covers that block's loads only, not the next block's issued
-// after them.
-__device__ __forceinline__ void issue_loads(TileLoads& t, const uint8_t* codes_w,
-                                            const uint8_t* scales_w, int page, bool live,
-                                            int64_t page_codes, int64_t page_scales,
-                                            uint32_t code_lane, uint32_t scale_lane) {
-  const int64_t p = live ? page : 0;
-  const auto cr = tile_rsrc(codes_w + p * page_codes, live ? kCodePage : 0);
-  const auto sr = tile_rsrc(scales_w + p * page_scales, live ? kScalePage : 0);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) t.c[j] = load_tile16(cr, code_lane, j * 16 * kCodeRow);
-  t.s = load_tile16(sr, scale_lane, 0);
-}
-
-// Block maxima of two query rows r0, r0 + 1 of a partial-score buffer
-// part[h][row][t] (rows of 128 floats, head stride hs floats): per token the
-// sum over heads 0 .. H-1 in head order, then the maximum, starting from 0,
-// over the tokens t <= lim of each row. Lane (row - r0) * 32 + t / 4 sums
-// tokens t .. t + 3 with 16-byte LDS reads; lim is the lane's row's last
-// visible token in the block (< 0: none). Returns both maxima (uniform).
-__device__ __forceinline__ float2 row_pair_max(const float* part, int hs, int H, int r0, int lim,
-                                               int lane) {
-  const int t0 = 4 * (lane & 31);
-  float m = 0.0f;
-  if (t0 <= lim) {
-    const float* pt = part + (r0 + (lane >> 5)) * kBlockTokens + t0;
-    float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    for (int h = 0; h < H; ++h) {
-      const float4 v = *reinterpret_cast<const float4*>(pt + h * hs);
-      s.x += v.x;
-      s.y += v.y;
-      s.z += v.z;
-      s.w += v.w;
-    }
-    m = fmaxf(fmaxf(m, s.x), t0 + 1 <= lim ? s.y : 0.0f);
-    m = fmaxf(m, fmaxf(t0 + 2 <= lim ? s.z : 0.0f, t0 + 3 <= lim ? s.w : 0.0f));
-  }
-  // m >= 0: maxima of the bit patterns, per 32-lane half
-  const uint32_t v = row16_max_u32(__float_as_uint(m));
-  const uint32_t a0 = __builtin_amdgcn_readlane(int(v), 15), a1 = __builtin_amdgcn_readlane(int(v), 31);
-  const uint32_t a2 = __builtin_amdgcn_readlane(int(v), 47), a3 = __builtin_amdgcn_readlane(int(v), 63);
-  return make_float2(__uint_as_float(max(a0, a1)), __uint_as_float(max(a2, a3)));
-}
 
 // QG: 16-row MFMA groups per index head = ceil(8 * q_per_seq / 16).
 // One block in flight per wave: the next block's loads are issued as soon as
@@ -130,144 +43,7 @@ __global__ __launch_bounds__(512) void indexer_kernel(const IndexerArgs a) {
   extern __shared__ float part[];  // [2][H][2*QG][128] partial token scores per index head
   __shared__ uint2 lut[128];
   __shared__ int pages[kMaxBlocksPerWg];
-
-  const int H = a.num_heads;
-  const int Q = a.q_per_seq;
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int slice = lane >> 4;  // 32-channel slice of the reduction dimension
-  const int b = blockIdx.y;
-  constexpr int QR = 2 * QG;    // query-token rows of the partial buffer
-
-  for (int i = threadIdx.x; i < 128; i += blockDim.x) lut[i] = make_uint2(kIdxLut.lo[i], kIdxLut.hi[i]);
-
-  const int L = a.seq_lens[b];
-  const bool seq_ok = L >= Q && L <= a.max_blocks * kBlockTokens;
-  const int nb_last = seq_ok ? (L - 1) / kBlockTokens + 1 : 0;
-  // workgroup x of a sequence takes blocks x, x + G, x + 2G, ... (G = grid
-  // width), so the workgroups running at any moment read neighbouring pages;
-  // blocks below the sequence's shared prefix are left to the shared pass
-  const int G = gridDim.x;
-  const int x = blockIdx.x;
-  const int total = nb_last > x ? min(a.blocks_per_wg, (nb_last - x + G - 1) / G) : 0;
-  const int skip = a.seq_skip ? a.seq_skip[b] : 0;
-  const int k0 = x < skip ? min(total, (skip - x + G - 1) / G) : 0;
-  const int first = x + k0 * G;
-  const int count = total - k0;
-  const int64_t qrow0 = int64_t(b) * Q;
-  const int Hq = a.num_q_heads;
-  if (int(threadIdx.x) < count) {
-    const int p = a.block_table[int64_t(b) * a.max_blocks + first + threadIdx.x * G];
-    pages[threadIdx.x] = (p >= 0 && p < a.num_pages) ? p : -1;
-  }
-
-  // Query operands (rows: query token R/8, head wave*8 + R%8) and weights.
-  v8i qop[QG];
-  float wv[QG][4];
-#pragma unroll
-  for (int rg = 0; rg < QG; ++rg) {
-    const int R = 16 * rg + (lane & 15);
-    const int qi = R >> 3;
-    if (qi < Q) {
-      const uint4* qp = reinterpret_cast<const uint4*>(
-          a.q + ((qrow0 + qi) * Hq + wave * kHeadsPerKv + (R & 7)) * kHeadDim + slice * 32);
-      qop[rg] = q_operand(qp[0], qp[1]);
-    } else {
-      qop[rg] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int R2 = 16 * rg + 4 * slice + v;
-      const int qi2 = R2 >> 3;
-      wv[rg][v] = qi2 < Q ? a.w[(qrow0 + qi2) * Hq + wave * kHeadsPerKv + (R2 & 7)] : 0.0f;
-    }
-  }
-  __syncthreads();
-
-  const int64_t page_codes = int64_t(H) * kCodePage;
-  const int64_t page_scales = int64_t(H) * kScalePage;
-  // this wave's head within a page (uniform), and the lane's offsets in a tile
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const uint8_t* codes_w = a.codes + int64_t(wave_u) * kCodePage;
-  const uint8_t* scales_w = a.scales + int64_t(wave_u) * kScalePage;
-  const uint32_t code_lane = (lane & 15) * kCodeRow + slice * 16;
-  const uint32_t scale_lane = scale_word_offset(slice, lane & 15);
-  const int count_u = __builtin_amdgcn_readfirstlane(count);
-  auto issue = [&](TileLoads& t, int k) {
-    const int page = __builtin_amdgcn_readfirstlane(pages[min(k, kMaxBlocksPerWg - 1)]);
-    issue_loads(t, codes_w, scales_w, page, k < count_u && page >= 0, page_codes, page_scales,
-                code_lane, scale_lane);
-  };
-  const int part_stride = H * QR * kBlockTokens;
-  // an MFMA result lane l holds query token 2rg + l/32, heads
-  // 4*((l/16)&1) .. +3 of the index head's 8, token 16j + l%16; lanes l and
-  // l^16 swap halves so that each writes the 8-head sum of one token,
-  // 32i + l%32, for the pair j = 2i, 2i+1
-  const int part_lane = (lane >> 5) * kBlockTokens + (lane & 31);
-
-  // dequantise, multiply, apply ReLU and weights; per-head partials to LDS
-  auto compute = [&](const TileLoads& t, int buf) {
-    float* pw = part + buf * part_stride + wave * QR * kBlockTokens + part_lane;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float s2[2][QG];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const uint32_t sj = tile_scales(t.s, 2 * i + e);
-        const v8i kop = dequant32(t.c[2 * i + e], lut[sj & 0x7F], lut[(sj >> 8) & 0x7F]);
-#pragma unroll
-        for (int rg = 0; rg < QG; ++rg) {
-          const v4f acc = mfma_fp8_16x16x128(qop[rg], kop, v4f{0.0f, 0.0f, 0.0f, 0.0f});
-          float s = wv[rg][0] * fmaxf(acc[0], 0.0f);
-          s += wv[rg][1] * fmaxf(acc[1], 0.0f);
-          s += wv[rg][2] * fmaxf(acc[2], 0.0f);
-          s += wv[rg][3] * fmaxf(acc[3], 0.0f);
-          s2[e][rg] = s;
-        }
-      }
-#pragma unroll
-      for (int rg = 0; rg < QG; ++rg) {
-        // v_permlane16_swap: the odd rows of the first operand trade places
-        // with the even rows of the second, so an even-row lane ends with
-        // its own j = 2i partial and its partner's, an odd-row lane with
-        // both j = 2i+1 partials (heads 0-3 first, as in the unpaired sum)
-        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(s2[0][rg]),
-                                                         __float_as_uint(s2[1][rg]), false, false);
-        pw[2 * rg * kBlockTokens + 32 * i] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  // Sum the heads, maximise over the block's visible tokens and store the
-  // block score, one query-token pair per wavefront (waves take pairs w,
-  // w + H, ...).
-  const int pairs = (Q + 1) >> 1;
-  auto reduce_part = [&](int k, int buf) {
-    const int blk = first + k * G;
-    const bool page_ok = pages[k] >= 0;
-    for (int u = wave_u; u < pairs; u += H) {
-      const int qi = 2 * u + (lane >> 5);
-      const int lim = qi < Q ? L - Q + qi - blk * kBlockTokens : -1;
-      const float2 mx = row_pair_max(part + buf * part_stride, QR * kBlockTokens, H, 2 * u, lim, lane);
-      const int q = 2 * u + lane;
-      if (lane < 2 && q < Q && blk * kBlockTokens <= L - Q + q)
-        a.bscore[(qrow0 + q) * a.max_blocks + blk] = page_ok ? (lane ? mx.y : mx.x) : 0.0f;
-    }
-  };
-  // one register buffer: the next block's loads are issued as soon as the
-  // current block's codes are consumed, so their latency overlaps the
-  // barrier and the reduction (the scheduling barriers keep the compiler
-  // from hoisting them into a second buffer)
-  TileLoads t;
-  issue(t, 0);
-  for (int k = 0; k < count_u; ++k) {
-    compute(t, k & 1);
-    __builtin_amdgcn_sched_barrier(0);
-    issue(t, k + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
-    reduce_part(k, k & 1);
-  }
+  scan_workgroup<QG, false>(a, blockIdx.x, gridDim.x, blockIdx.y, kIdxLut, part, lut, pages);
 }
 
 // Shared pass for sequences that share leading blocks (the same physical

@@ -47,13 +47,27 @@ __device__ __forceinline__ uint64_t make_key(uint32_t bits, int j) {
 __device__ __forceinline__ int key_block_id(uint64_t k) { return int(0xFFFFFFFFu - uint32_t(k)); }
 __device__ __forceinline__ float key_score_value(uint64_t k) { return __uint_as_float(uint32_t(k >> 32)); }
 
+// Buffer-load cache policy for scores written earlier in the same launch:
+// device scope (sc1), so the load is coherent across the XCDs' L2 caches.
+constexpr int kDeviceScopeLoad = 16;
+
+// One score entry; COHERENT: a device-scope load (see kDeviceScopeLoad).
+template <bool COHERENT>
+__device__ __forceinline__ float load_score(const float* p) {
+  if constexpr (COHERENT)
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    return *p;
+}
+
 // One chunk of a query token's block scores: lane l gets entries
 // c0 + l + 64 k. The loads go through a buffer descriptor over the row
 // (row_len entries; a buffer load past the record count returns 0), with one
 // 32-bit lane offset and the stride of k in the constant offsets: nothing is
 // predicated, so all 32 loads are in flight at once, and no per-element
 // 64-bit address is formed. Entries past the candidates are masked by index
-// later.
+// later. COHERENT: device-scope loads.
+template <bool COHERENT = false>
 __device__ __forceinline__ void load_score_chunk(const float* row, int row_len, int c0, int lane,
                                                  float (&x)[kSelPerLane]) {
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
@@ -62,7 +76,8 @@ __device__ __forceinline__ void load_score_chunk(const float* row, int row_len, 
 #pragma unroll
   for (int k = 0; k < kSelPerLane; ++k)
     x[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                         r, off, 64 * k * int(sizeof(float)), 0));
+                                         r, off, 64 * k * int(sizeof(float)),
+                                         COHERENT ? kDeviceScopeLoad : 0));
 }
 
 // Inclusive prefix sum over the wavefront: DPP row shifts inside rows of 16
@@ -87,7 +102,9 @@ __device__ __forceinline__ int wave_inclusive_sum(int v, int lane) {
 // With a block-table row (table_row[j] = page of block j, j < nb), *page_out
 // receives the selected block's table entry, unchecked (-1 where no block):
 // the lookups are issued as soon as the candidates are known, so their
-// latency overlaps the exact ranking.
+// latency overlaps the exact ranking. COHERENT: the scores are read with
+// device-scope loads (written earlier in the same launch).
+template <bool COHERENT = false>
 __device__ __forceinline__ int select_blocks(const float* row, int row_len, int nb,
                                              const float (&x0)[kSelPerLane], SelectScratch& sc,
                                              int lane, float* score_out,
@@ -95,7 +112,8 @@ __device__ __forceinline__ int select_blocks(const float* row, int row_len, int 
                                              int* page_out = nullptr) {
   if (nb <= kTopK + 1) {
     const bool in = lane < nb;
-    *score_out = in ? __uint_as_float(score_bits(row[min(lane, row_len - 1)])) : 0.0f;
+    *score_out = in ? __uint_as_float(score_bits(load_score<COHERENT>(&row[min(lane, row_len - 1)])))
+                    : 0.0f;
     if (table_row) *page_out = in ? table_row[min(lane, nb - 1)] : -1;
     return in ? lane : -1;
   }
@@ -113,7 +131,7 @@ __device__ __forceinline__ int select_blocks(const float* row, int row_len, int 
 #pragma unroll
       for (int k = 0; k < kSelPerLane; ++k) x[k] = x0[k];
     } else {
-      load_score_chunk(row, row_len, c0, lane, x);
+      load_score_chunk<COHERENT>(row, row_len, c0, lane, x);
     }
 #pragma unroll
     for (int k = 0; k < kSelPerLane; ++k) v[k] = c0 + lane + 64 * k < n ? score_bits(x[k]) : 0u;
@@ -237,7 +255,7 @@ __device__ __forceinline__ int select_blocks(const float* row, int row_len, int 
   }
   if (table_row) *page_out = lane == kTopK ? recent_page : -1;
   if (lane == kTopK) {
-    *score_out = __uint_as_float(score_bits(row[nb - 1]));
+    *score_out = __uint_as_float(score_bits(load_score<COHERENT>(&row[nb - 1])));
     return nb - 1;
   }
   *score_out = 0.0f;

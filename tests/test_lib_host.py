@@ -215,3 +215,46 @@ def test_qkv_rope_insert_rejects_before_launch(L):
     assert call(qkv=None) == 1
     assert call(qkv=ctypes.c_void_p((1 << 20) + 8)) == 1   # qkv must be 16-byte aligned
     assert call(n=1 << 31) == 2
+
+
+def test_mono_workspace_layout(L):
+    # scores, partial o, partial (m, l), then the counters: every part
+    # 256-byte aligned; the error word is the last 32-bit word
+    def a256(x):
+        return -(-x // 256) * 256
+    for ns, q, mb in [(1, 1, 32), (4, 1, 33), (2, 8, 40), (3, 2, 1)]:
+        tq, rows = ns * q, ns * q * 32
+        want = (a256(tq * mb * 4) + a256(rows * mb * 128 * 4) + a256(rows * mb * 2 * 4)
+                + a256(((ns + tq * 4) * 128 + ns * 16 + 1) * 4))
+        assert nb.msa_decode_mono_workspace_bytes(ns, q, 32, mb) == want
+    assert nb.msa_decode_mono_workspace_bytes(0, 1, 32, 4) == 0
+
+
+def test_mono_rejects_before_launch(L):
+    f = L.msa_decode_mono
+    d4 = ctypes.byref(_desc())
+
+    def call(idx=d4, kv=d4, q=32, mb=4, ns=1, qps=1, topk=16, ids=None, scale=0.088, ptr=256,
+             ws=4096, wsb=None):
+        if wsb is None:
+            wsb = nb.msa_decode_mono_workspace_bytes(max(ns, 1), qps, 32, mb)
+        return f(idx, ptr, ptr, ptr, ptr, kv, ptr, ptr, ptr, ptr, ptr, q, ptr, mb, ptr, ns, qps,
+                 topk, ids, scale, ptr, ws, wsb, None)
+    assert call(idx=None) == 1 and call(kv=None) == 1
+    assert call(idx=ctypes.byref(_desc(heads=2))) == 2   # the scan's wavefronts: 4 index heads
+    assert call(kv=ctypes.byref(_desc(heads=8))) == 2
+    assert call(q=64) == 2
+    assert call(topk=8) == 2
+    assert call(qps=9) == 2
+    assert call(idx=ctypes.byref(_desc(bt=64))) == 2
+    assert call(mb=2049) == 2                            # 4 x 2049 block workgroups > 8192
+    assert call(ns=2, qps=8, mb=129) == 2                # 16 x 4 x 129 > 8192
+    assert call(ns=2, qps=8, mb=128, ptr=None) == 1      # at the bound: reaches the null check
+    assert call(scale=0.0) == 1
+    assert call(ns=0) == 0
+    assert call(ptr=None) == 1
+    assert call(ptr=4096 + 8) == 1                       # misaligned
+    assert call(ids=4096 + 2) == 1
+    assert call(ws=None) == 3
+    assert call(ws=4096 + 16) == 3                       # workspace not 256-byte aligned
+    assert call(wsb=64) == 3
