@@ -60,9 +60,14 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
   const int tid = threadIdx.x;
   const int64_t row = int64_t(blockIdx.x) * kHeadsPerKv + (tid >> 5);  // query head row
   const int pd = (tid & 31) * 4;
+  const float* po = part_o + row * num_splits * kHeadDim + pd;
+  const float* pm = part_ml + row * num_splits * 2;
   *reinterpret_cast<float4*>(out + row * kHeadDim + pd) =
-      merge_row<false>(part_o + row * num_splits * kHeadDim + pd, part_ml + row * num_splits * 2,
-                       num_splits, [](int k) { return k; });
+      merge_row(num_splits, [&](int s, float4& v, float2& ml) {
+        v = *reinterpret_cast<const float4*>(po + s * kHeadDim);
+        ml = *reinterpret_cast<const float2*>(pm + s * 2);
+        return true;
+      });
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }

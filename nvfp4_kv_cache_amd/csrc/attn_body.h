@@ -145,22 +145,39 @@ constexpr int kAttnEvery = 2;   // block sp itself, selected or not (the one-lau
 // SELECT: the kernel selects the blocks itself from the indexer's block
 // scores; otherwise the caller's ids are used.
 
+// Device-scope (sc1) accesses to split partials written and read within
+// one launch: coherent across the XCDs' L2 caches. Buffer operations over a
+// partial array (the host keeps it below 2 GiB), so a lane moves 16 or 8
+// bytes at once; 4-byte device-scope stores measured 4x their bytes in
+// memory writes.
+constexpr int kDeviceScope = 16;  // buffer cache policy: sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(const float* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, 0x7FFFFFFF, 0x00020000);
+}
+__device__ __forceinline__ void store_device_scope(__amdgpu_buffer_rsrc_t r, uint32_t off, float4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(
+      __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v), r, off, 0, kDeviceScope);
+}
+__device__ __forceinline__ void store_device_scope(__amdgpu_buffer_rsrc_t r, uint32_t off, float2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(
+      __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, v), r, off, 0, kDeviceScope);
+}
+__device__ __forceinline__ float4 load_device_scope4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kDeviceScope));
+}
+__device__ __forceinline__ float2 load_device_scope2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kDeviceScope));
+}
+
 // Split partials fetched per round of independent loads in the merge.
 constexpr int kMergeChunk = 20;
 
-// Log-sum-exp merge of the n partials of one query-head row (partial k is
-// split slot(k) of the row; slot < 0: empty); this thread combines channels
-// pd .. pd + 3 and returns them normalised. COHERENT: device-scope loads of
-// partials written earlier in the same launch.
-template <bool COHERENT, class Slot>
-__device__ __forceinline__ float4 merge_row(const float* __restrict__ po,
-                                            const float* __restrict__ pm, int n, Slot slot) {
-  auto ld = [](const float* p) {
-    if constexpr (COHERENT)
-      return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    else
-      return *p;
-  };
+// Log-sum-exp merge of the n partials of one query-head row, this thread's
+// channels (4 of them), returned normalised. fetch(k, v, ml) loads partial k
+// (k < n; its 4 channels of o and its (m, l)) and returns false for an empty
+// one, which counts as (m, l) = (-inf, 0).
+template <class Fetch>
+__device__ __forceinline__ float4 merge_row(int n, Fetch fetch) {
   const float ninf = -__builtin_huge_valf();
   float M = ninf, den = 0.0f, o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int s0 = 0; s0 < n; s0 += kMergeChunk) {
@@ -168,16 +185,9 @@ __device__ __forceinline__ float4 merge_row(const float* __restrict__ po,
     float2 ml[kMergeChunk];
 #pragma unroll
     for (int k = 0; k < kMergeChunk; ++k) {
-      const int s = slot(s0 + k);
-      const bool in = s0 + k < n && s >= 0;
-      if constexpr (COHERENT) {
-        v[k] = in ? make_float4(ld(po + s * kHeadDim), ld(po + s * kHeadDim + 1),
-                                ld(po + s * kHeadDim + 2), ld(po + s * kHeadDim + 3))
-                  : make_float4(0, 0, 0, 0);
-        ml[k] = in ? make_float2(ld(pm + s * 2), ld(pm + s * 2 + 1)) : make_float2(ninf, 0.0f);
-      } else {
-        v[k] = in ? *reinterpret_cast<const float4*>(po + s * kHeadDim) : make_float4(0, 0, 0, 0);
-        ml[k] = in ? *reinterpret_cast<const float2*>(pm + s * 2) : make_float2(ninf, 0.0f);
+      if (!(s0 + k < n && fetch(s0 + k, v[k], ml[k]))) {
+        v[k] = make_float4(0, 0, 0, 0);
+        ml[k] = make_float2(ninf, 0.0f);
       }
     }
     float Mc = M;

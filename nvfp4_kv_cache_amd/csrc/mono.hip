@@ -174,10 +174,16 @@ __device__ __forceinline__ void merge_pair(const MonoArgs& m, int qt, int kh, ui
   // thread: head tid / 32 of this KV head, channels 4 (tid % 32) .. + 3
   const int64_t row = int64_t(qt) * t.num_q_heads + kh * kHeadsPerKv + (tid >> 5);
   const int pd = (tid & 31) * 4;
-  const int nsp = t.num_splits;
+  const int64_t nsp = t.num_splits;
+  const auto ro = partial_rsrc(t.part_o), rm = partial_rsrc(t.part_ml);
   *reinterpret_cast<float4*>(t.out + row * kHeadDim + pd) =
-      merge_row<true>(t.part_o + row * nsp * kHeadDim + pd, t.part_ml + row * nsp * 2, kTopK + 1,
-                      [&](int k) { return slot[k]; });
+      merge_row(kTopK + 1, [&](int k, float4& v, float2& ml) {
+        const int s = slot[k];  // selected block (-1: none)
+        if (s < 0) return false;
+        v = load_device_scope4(ro, uint32_t(((row * nsp + s) * kHeadDim + pd) * 4));
+        ml = load_device_scope2(rm, uint32_t((row * nsp + s) * 8));
+        return true;
+      });
 }
 
 template <int QG>
