@@ -74,7 +74,7 @@ extern "C" {
 typedef enum msa_status {
   MSA_OK = 0,
   MSA_ERR_INVALID_ARG = 1, /* null pointer, negative size, misalignment */
-  MSA_ERR_UNSUPPORTED = 2, /* a shape this build does not implement */
+  MSA_ERR_UNSUPPORTED = 2, /* a shape the library does not implement */
   MSA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
   MSA_ERR_HIP = 4          /* the HIP runtime refused a launch */
 } msa_status;
