@@ -79,9 +79,18 @@ inline bool misaligned(const void* p, uintptr_t m) { return (reinterpret_cast<ui
 // serial work per wavefront is a quarter block. Measured against whole
 // blocks per wavefront at 17 slots: 2.3 us faster per step at 4 pairs, 1.5 us
 // at 16, 0.4 us slower at 32 (more workgroups than the chip runs evenly).
-// Otherwise whole blocks per wavefront: one block per wave while that keeps
-// the workgroup count under ~1024, else R blocks per wave.
+// Otherwise whole blocks per wavefront, R slots per wavefront and
+// ceil(num_sel / 4R) splits per pair. The chip holds kResidentWgs of these
+// workgroups at once (two per CU at the kernel's 183 VGPRs): R = 1, else 2,
+// when that grid fits in one round, otherwise one split per pair (R =
+// ceil(num_sel / 4)), which also needs no merge kernel. Measured at 17
+// slots, us per launch (R = 1 / 2 / 3 / 5): 32 pairs 16.1 / 19.9 / 23.4 /
+// 27.3; 96 pairs 19.9 / 24.3 / 23.7 / 27.6; 160 pairs 30.4 / 25.2 / 29.8 /
+// 27.8; 192 pairs 31.8 / 31.3 / 30.1 / 28.1; 512 pairs 70.0 / 59.6 / 54.7 /
+// 39.9; a grid of at most 1,024 workgroups, the earlier rule, took R = 3 at
+// 512 pairs.
 constexpr int64_t kSharedMaxWgs = 384;
+constexpr int64_t kResidentWgs = 512;
 struct AttnPlan {
   int tok;           // tokens of a block per wavefront: 32 or 128
   int slots_per_wg;  // selected slots per workgroup
@@ -89,9 +98,13 @@ struct AttnPlan {
 };
 inline AttnPlan attn_plan(int64_t pairs, int num_sel) {
   if (pairs * num_sel <= kSharedMaxWgs) return AttnPlan{kBlockTokens / kAttnWaves, 1, num_sel};
-  int R = 1;
-  while (R < num_sel && pairs * ((num_sel + kAttnWaves * R - 1) / (kAttnWaves * R)) > 1024) ++R;
-  return AttnPlan{kBlockTokens, kAttnWaves * R, (num_sel + kAttnWaves * R - 1) / (kAttnWaves * R)};
+  auto splits = [&](int r) { return (num_sel + kAttnWaves * r - 1) / (kAttnWaves * r); };
+  int R = (num_sel + kAttnWaves - 1) / kAttnWaves;  // one split
+  if (pairs * splits(1) <= kResidentWgs)
+    R = 1;
+  else if (pairs * splits(2) <= kResidentWgs)
+    R = 2;
+  return AttnPlan{kBlockTokens, kAttnWaves * R, splits(R)};
 }
 
 

@@ -156,6 +156,31 @@ def test_attention_launch_forms(nb, nseq):
         assert not fails, "\n".join(fails[:20])
 
 
+# With whole blocks per wavefront the plan takes 1 or 2 slots per wavefront
+# while the grid fits the 512 workgroups the chip holds at once, else one
+# split per (query token, KV head) pair, written without the merge kernel:
+# 160 pairs run 2 slots per wavefront (3 splits), 192 pairs and 8 x 8 query
+# tokens (256 pairs) one split.
+@pytest.mark.parametrize("nseq,q", [(40, 1), (48, 1), (8, 8)],
+                         ids=["2-slots-3-splits", "one-split", "one-split-q8"])
+def test_attention_plan_many_pairs(nb, nseq, q):
+    rng = np.random.default_rng(nseq * 10 + q)
+    lens = [int(x) for x in rng.integers(17 * 128 + 1, 24 * 128, size=nseq)]
+    lens[0] = 16 * 128 + 3                        # fewer than 17 blocks: every block
+    say(f"attention plan, {nseq} sequences x {q} query tokens")
+    wl = tiny_config(lens, q, seed=70 + nseq)
+    pools = S.fill_pools(wl, nb)
+    inp = S.device_inputs(wl)
+    for fused in (True, False):
+        ids, sc, o = _to_np(S.run_step(nb, wl, pools, inp, fused=fused))
+        _structural(wl, ids)
+        assert np.all(np.isfinite(o))
+        fails = []
+        for b in (0, 1, nseq // 2, nseq - 1):
+            fails += S.check_sequence(wl, b, ids, sc, o)
+        assert not fails, "\n".join(fails[:20])
+
+
 @pytest.mark.parametrize("heads", [1, 2, 8])
 def test_head_counts(nb, heads):
     # every kernel takes the number of index-key / KV heads at run time (1..8,

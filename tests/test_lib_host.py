@@ -43,17 +43,20 @@ def test_status_strings(L):
 def _attn_splits(pairs, num_sel):
     # the launch plan: few (query token, KV head) pairs -> one workgroup per
     # selected block; otherwise one block per wavefront (4 per workgroup),
-    # R blocks per wavefront while the workgroup count exceeds 1024
+    # 1 or 2 slots per wavefront while the grid fits the 512 workgroups the
+    # chip holds at once, else one split per pair
     if pairs * num_sel <= 384:
         return num_sel
-    r = 1
-    while r < num_sel and pairs * -(-num_sel // (4 * r)) > 1024:
-        r += 1
-    return -(-num_sel // (4 * r))
+    for r in (1, 2):
+        if pairs * -(-num_sel // (4 * r)) <= 512:
+            return -(-num_sel // (4 * r))
+    return 1
 
 
 @pytest.mark.parametrize("seqs,q,heads,sel", [(16, 8, 32, 17), (8, 1, 32, 17), (32, 1, 32, 17),
-                                              (1, 1, 32, 17), (2, 1, 8, 64), (45, 1, 32, 17)])
+                                              (1, 1, 32, 17), (2, 1, 8, 64), (45, 1, 32, 17),
+                                              (24, 1, 32, 17), (40, 1, 32, 17), (48, 1, 32, 17),
+                                              (96, 1, 32, 17), (4, 1, 32, 64)])
 def test_workspace_sizes(L, seqs, q, heads, sel):
     assert nb.msa_indexer_workspace_bytes(8, 1, 2048) == 8 * 2048 * 4
     assert nb.msa_indexer_workspace_bytes(0, 1, 10) == 0
