@@ -253,19 +253,7 @@ static msa_status launch_scan(const msa_pool_desc* idx, const uint8_t* idx_codes
   a.q_per_seq = q_per_seq;
   a.bscore = block_scores;
   const int qg = (MSA_HEADS_PER_KV * q_per_seq + 15) / 16;
-  // blocks per workgroup, halved while the grid would not cover the chip
-  // several times over. Measured with one query token: 3 is best for a few
-  // long sequences (8 x 256K), 8 for many sequences of mixed length (45
-  // requests, 30K..210K), where much of the grid bound is empty; the grid
-  // bound num_seqs x max_blocks is what the host knows. With 5..8 query
-  // tokens a workgroup's blocks cost four times the arithmetic and the chip
-  // holds about 1,024 workgroups at once (120 VGPRs, 33 KB of LDS each):
-  // halving stops at that grid. Measured at 16 x 64K with 8 query tokens:
-  // 8 blocks per workgroup (1,024 workgroups) 66.6 us, 4 (2,048) 70.4 us,
-  // 2 79.1 us.
-  int bpw = (qg == 1 && int64_t(num_seqs) * max_blocks <= 32768) ? 3 : 8;
-  const int64_t min_grid = qg >= 4 ? 1024 : 2048;
-  while (bpw > 1 && int64_t(num_seqs) * ((max_blocks + bpw - 1) / bpw) < min_grid) bpw >>= 1;
+  const int bpw = scan_blocks_per_wg(num_seqs, max_blocks, qg);
   a.blocks_per_wg = bpw;
   const dim3 grid((max_blocks + bpw - 1) / bpw, num_seqs);
   const dim3 block(64 * idx->num_heads);

@@ -304,11 +304,9 @@ extern "C" msa_status msa_decode_mono(
   s.q_per_seq = q_per_seq;
   s.bscore = reinterpret_cast<float*>(ws + lay.scores);
   s.seq_skip = nullptr;
-  // blocks per scan workgroup: the standalone scan's rule (a few blocks per
-  // workgroup, halved while the grid would not cover the chip)
+  // blocks per scan workgroup: the standalone scan's rule
   const int qg = (MSA_HEADS_PER_KV * q_per_seq + 15) / 16;
-  int bpw = (qg == 1 && int64_t(num_seqs) * max_blocks <= 32768) ? 3 : 8;
-  while (bpw > 1 && int64_t(num_seqs) * ((max_blocks + bpw - 1) / bpw) < 2048) bpw >>= 1;
+  const int bpw = scan_blocks_per_wg(num_seqs, max_blocks, qg);
   s.blocks_per_wg = bpw;
 
   AttnArgs& t = m.t;

@@ -107,6 +107,24 @@ __device__ __forceinline__ float2 row_pair_max(const float* part, int hs, int H,
 // the current block's codes are consumed, and more resident waves hide the
 // latency better than a second register buffer would (measured with 1 and 8
 // query tokens).
+// Blocks per scan workgroup for num_seqs sequences of up to max_blocks
+// blocks and qg 16-row MFMA groups per index head. Halved while the grid
+// would not cover the chip several times over. Measured with one query
+// token: 3 is best for a few long sequences (8 x 256K), 8 for many sequences
+// of mixed length (45 requests, 30K..210K), where much of the grid bound is
+// empty; the grid bound num_seqs x max_blocks is what the host knows. With
+// 5..8 query tokens a workgroup's blocks cost four times the arithmetic and
+// the chip holds about 1,024 workgroups at once (120 VGPRs, 33 KB of LDS
+// each): halving stops at that grid. Measured at 16 x 64K with 8 query
+// tokens: 8 blocks per workgroup (1,024 workgroups) 66.6 us, 4 (2,048)
+// 70.4 us, 2 79.1 us.
+inline int scan_blocks_per_wg(int64_t num_seqs, int64_t max_blocks, int qg) {
+  int bpw = (qg == 1 && num_seqs * max_blocks <= 32768) ? 3 : 8;
+  const int64_t min_grid = qg >= 4 ? 1024 : 2048;
+  while (bpw > 1 && num_seqs * ((max_blocks + bpw - 1) / bpw) < min_grid) bpw >>= 1;
+  return bpw;
+}
+
 // Workgroup x of the G scan workgroups of sequence b, one wavefront per
 // index-key head. LDS from the caller: part = [2][H][2*QG][128] floats,
 // lut = 128 table rows, pages = kMaxBlocksPerWg entries. COHERENT: the block
