@@ -333,8 +333,10 @@ size_t msa_decode_mono_workspace_bytes(int32_t num_seqs, int32_t q_per_seq, int3
  * and KV head is computed while the scan runs, and per (query token, KV head)
  * a last workgroup waits for both, selects the 16 + 1 blocks from the scores
  * and merges only their partials. That costs max_blocks x 73,728 bytes of K/V
- * reads per sequence instead of 17 x 73,728, so the launch is bounded:
- * num_seqs * q_per_seq * 4 * max_blocks <= 8192 (else MSA_ERR_UNSUPPORTED).
+ * reads per sequence instead of 17 x 73,728, so the launch is bounded to the
+ * shapes where that costs less than the launches it saves:
+ * num_seqs * q_per_seq * 4 * max_blocks <= 1024, e.g. 1 x 32K, 2 x 16K,
+ * 8 x 4K tokens with one query token (else MSA_ERR_UNSUPPORTED).
  *   idx, idx_codes, idx_scales, q_idx_fp8, head_w   as msa_indexer_scan; the
  *                index pool must have 4 heads
  *   kv, k_*, v_*, q_fp8, num_q_heads, block_table, max_blocks, seq_lens,

@@ -26,7 +26,8 @@
 // So the scan and the attention run side by side, and the selection and the
 // merge are the only steps after the scan. The price is attention over every
 // block instead of 17 (max_blocks x 73,728 bytes of K/V per sequence), which
-// is why the entry point bounds the grid (low concurrency, short contexts).
+// is why the entry point bounds the grid (low concurrency, short contexts:
+// query tokens x 4 KV heads x max_blocks <= 1,024).
 //
 // The values are those of the three-kernel path: the scan and the block
 // partials are the same code, the selection sees the same scores, and the
@@ -62,8 +63,12 @@ __constant__ Fp8Lut kMonoLut = make_fp8_lut();
 
 // Bound on a merge workgroup's wait: 20 ms of the 100 MHz real-time clock.
 constexpr uint64_t kMonoWaitTicks = 2000000;
-// Bound on block workgroups per launch: T_q x KV heads x max_blocks.
-constexpr int64_t kMonoMaxBlockWgs = 8192;
+// Bound on block workgroups per launch: T_q x KV heads x max_blocks. Past
+// it, attending every block costs more than the launches it saves: measured
+// against the multi-launch step (one query token): 512 workgroups (1 x 16K)
+// 14.1 vs 16.1 us, 1,024 (1 x 32K, 2 x 16K) 16.2 vs 16.6 and 16.5 vs 16.9 us,
+// 1,536 (1 x 48K) 21.4 vs 17.6 us, 2,048 (1 x 64K) 25.3 vs 17.9 us.
+constexpr int64_t kMonoMaxBlockWgs = 1024;
 // Counters per arrival count, and the word stride between them (64 bytes).
 constexpr int kSubCounters = 8;
 constexpr int kCounterStride = 16;

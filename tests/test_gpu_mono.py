@@ -107,7 +107,7 @@ MONO_CASES = [
     ([300, 2200], 2, True),
     ([5, 2304], 2, True),
     ([3, 4000], 3, False),
-    ([8, 5000], 8, False),
+    ([3900], 8, False),
     ([8 * 128 + 3, 19 * 128 + 7], 4, False),
 ]
 

@@ -250,9 +250,10 @@ def test_mono_rejects_before_launch(L):
     assert call(topk=8) == 2
     assert call(qps=9) == 2
     assert call(idx=ctypes.byref(_desc(bt=64))) == 2
-    assert call(mb=2049) == 2                            # 4 x 2049 block workgroups > 8192
-    assert call(ns=2, qps=8, mb=129) == 2                # 16 x 4 x 129 > 8192
-    assert call(ns=2, qps=8, mb=128, ptr=None) == 1      # at the bound: reaches the null check
+    assert call(mb=257) == 2                             # 4 x 257 block workgroups > 1024
+    assert call(ns=2, qps=8, mb=17) == 2                 # 16 x 4 x 17 > 1024
+    assert call(ns=2, qps=8, mb=16, ptr=None) == 1       # at the bound: reaches the null check
+    assert call(mb=256, ptr=None) == 1                   # 1 x 32K tokens: at the bound
     assert call(scale=0.0) == 1
     assert call(ns=0) == 0
     assert call(ptr=None) == 1
