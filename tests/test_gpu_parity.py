@@ -452,10 +452,11 @@ def test_graph_replay_matches_eager(nb):
         assert np.array_equal(out["o"].cpu().numpy(), ref[2]), rep
 
 
-@pytest.mark.parametrize("mb", [3000, 2050, 2049, 1500, 18])
+@pytest.mark.parametrize("mb", [3000, 2050, 2049, 1500, 66, 65, 40, 19, 18])
 def test_select_many_equal_scores(nb, mb):
     # 2049 blocks = 2048 candidates, the most held in registers; 2050 and up
-    # re-read the scores from memory
+    # re-read the scores from memory; 65 blocks (64 candidates) and fewer are
+    # ranked directly, 66 and more go through the threshold first
     say(f"selection with random, all-equal and adversarial scores, {mb} blocks")
     tq = 6
     lens = torch.tensor([mb * 128] * tq, dtype=torch.int32, device="cuda")
