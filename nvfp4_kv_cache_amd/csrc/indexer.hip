@@ -75,12 +75,17 @@ __global__ __launch_bounds__(512) void shared_scan_kernel(const SharedScanArgs s
   const int H = a.num_heads;
   const int Q = a.q_per_seq;
   const int Hq = a.num_q_heads;
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
+  // ids through the builtins: this file is built without IEEE NaN handling,
+  // so the device library's id functions are not inlined here, and a called
+  // one returns its value in a register the compiler cannot treat as uniform
+  // (each buffer load then needed a loop over the descriptor's values)
+  const int tid = int(__builtin_amdgcn_workitem_id_x());
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
   const int slice = lane >> 4;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int j = blockIdx.x, g = blockIdx.y;
-  const int c0 = kChunk * int(blockIdx.z);
+  const int j = int(__builtin_amdgcn_workgroup_id_x()), g = int(__builtin_amdgcn_workgroup_id_y());
+  const int c0 = kChunk * int(__builtin_amdgcn_workgroup_id_z());
   // uniform over the workgroup: nothing to do past the group's shared blocks
   // or past its member tokens
   if (j >= min(sa.group_blocks[g], a.max_blocks)) return;
@@ -89,7 +94,7 @@ __global__ __launch_bounds__(512) void shared_scan_kernel(const SharedScanArgs s
   const int lead = sa.group_seqs[m0];
   if (lead < 0 || lead >= sa.num_seqs) return;
 
-  for (int i = threadIdx.x; i < 128; i += blockDim.x) lut[i] = make_uint2(kIdxLut.lo[i], kIdxLut.hi[i]);
+  for (int i = tid; i < 128; i += 64 * H) lut[i] = make_uint2(kIdxLut.lo[i], kIdxLut.hi[i]);
   const int p = a.block_table[int64_t(lead) * a.max_blocks + j];
   const bool page_ok = p >= 0 && p < a.num_pages;
   TileLoads t;
@@ -100,8 +105,8 @@ __global__ __launch_bounds__(512) void shared_scan_kernel(const SharedScanArgs s
   // group_seqs[m0 + k / Q], query token k % Q), looked up once while the
   // block's loads are in flight
   const int T = (m1 - m0) * Q;
-  if (threadIdx.x < kChunk) {
-    const int k = c0 + int(threadIdx.x);
+  if (tid < kChunk) {
+    const int k = c0 + tid;
     int row = 0, pos = -1;
     if (k < T) {
       const int m = k / Q, qi = k - m * Q;
@@ -112,8 +117,8 @@ __global__ __launch_bounds__(512) void shared_scan_kernel(const SharedScanArgs s
         if (L >= Q && L <= a.max_blocks * kBlockTokens) pos = L - Q + qi;
       }
     }
-    tok_row[threadIdx.x] = row;
-    tok_pos[threadIdx.x] = pos;
+    tok_row[tid] = row;
+    tok_pos[tid] = pos;
   }
   __syncthreads();  // the lookup table and the token list
   v8i kop[8];
@@ -189,8 +194,9 @@ __global__ __launch_bounds__(64) void select_kernel(const float* __restrict__ bs
                                                     int32_t* __restrict__ out_ids,
                                                     float* __restrict__ out_scores) {
   __shared__ SelectScratch scratch;
-  const int row = blockIdx.x;
-  const int lane = threadIdx.x;
+  // ids through the builtins, as in shared_scan_kernel
+  const int row = int(__builtin_amdgcn_workgroup_id_x());
+  const int lane = int(__builtin_amdgcn_workitem_id_x());
   const float* src = bscore + int64_t(row) * max_blocks;
   float x0[kSelPerLane];
   load_score_chunk(src, max_blocks, 0, lane, x0);  // in flight while the length is read
