@@ -80,8 +80,10 @@ __global__ __launch_bounds__(kInsertThreads) void qkv_rope_insert_kernel(const I
   // [token][query, key class][A, B][channel]
   __shared__ __attribute__((aligned(16))) float tab[kInsertTokens][2][2][128];
   __shared__ uint16_t rowinfo[kMaxRowsPerToken];  // kind << 8 | head, per row of a token
-  const int tid = threadIdx.x;
-  const int64_t t0 = int64_t(blockIdx.x) * kInsertTokens;
+  // ids through the builtins: this file is built without IEEE NaN handling,
+  // so the device library's id functions would not be inlined but called
+  const int tid = int(__builtin_amdgcn_workitem_id_x());
+  const int64_t t0 = int64_t(__builtin_amdgcn_workgroup_id_x()) * kInsertTokens;
   const int ntok = int(min(int64_t(kInsertTokens), a.num_tokens - t0));
   const int nrows = ntok * a.rows;  // the workgroup's head rows, token-major
   const int half = a.rotary_dim >> 1;

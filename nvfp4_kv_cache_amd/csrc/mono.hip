@@ -20,9 +20,10 @@
 //      whether or not the selection will take it, store it at device scope
 //      and count themselves in the pair's arrival counter;
 //   3. merge workgroups, one per (query token, KV head), which wait for the
-//      sequence's scan and the pair's partials, select the 16 + 1 blocks
-//      from the scores (topk_select.h) and merge only those blocks' partials
-//      by log-sum-exp, in ascending block order.
+//      sequence's scan, select the 16 + 1 blocks from the scores
+//      (topk_select.h) while the partials are still being computed, wait for
+//      the pair's partials and merge only the selected blocks' partials by
+//      log-sum-exp, in ascending block order.
 // So the scan and the attention run side by side, and the selection and the
 // merge are the only steps after the scan. The price is attention over every
 // block instead of 17 (max_blocks x 73,728 bytes of K/V per sequence), which
