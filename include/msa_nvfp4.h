@@ -366,6 +366,21 @@ msa_status msa_decode_mono(const msa_pool_desc* idx, const uint8_t* idx_codes,
                            int32_t topk, int32_t* out_ids, float softmax_scale, float* out,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Measurement: a plain streaming read of `bytes` bytes at `buf`, the read
+ * ceiling a bandwidth-bound kernel of this library is compared with (the
+ * index scan streams the whole index cache once per step: MiniMax-M3.1-Flash
+ * serving summary, section "Sparse attention still scans an index"). Each
+ * workgroup reads one contiguous chunk of chunk_bytes with the index scan's
+ * loads (16-byte non-temporal, 8 in flight per lane) and folds them with
+ * XOR; sink (uint32 [ceil(bytes / chunk_bytes)], device) is written only if
+ * a fold hits a fixed pattern, so the traffic is the buffer's bytes.
+ * buf 16-byte aligned; bytes and chunk_bytes multiples of 16, chunk_bytes in
+ * (0, 2^30]. One kernel on `stream`.
+ */
+msa_status msa_read_probe(const void* buf, int64_t bytes, int64_t chunk_bytes, uint32_t* sink,
+                          void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -60,6 +60,7 @@ SIGNATURES = {
     "msa_decode_mono_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
     "msa_decode_mono": (ctypes.c_int, [_DESC, _P, _P, _P, _P, _DESC, _P, _P, _P, _P, _P, _I32, _P,
                                        _I32, _P, _I32, _I32, _I32, _P, _F32, _P, _P, _SZ, _P]),
+    "msa_read_probe": (ctypes.c_int, [_P, _I64, _I64, _P, _P]),
     "msa_qkv_rope_insert": (ctypes.c_int, [_P, _I64, _P, _P, _DESC, _P, _P, _P, _P, _DESC, _P, _P,
                                            _P, _P, _F32, _I32, _F32, _P, _P, _P]),
 }
@@ -422,9 +423,41 @@ def msa_decode_mono_workspace_bytes(num_seqs: int, q_per_seq: int, num_q_heads: 
 
 def mono_workspace(num_seqs, q_per_seq, num_q_heads, max_blocks, device="cuda"):
     """Workspace for msa_decode_mono, zero-filled (its counters must start at
-    zero; every call leaves them zero)."""
+    zero; a call whose waits all end in time leaves them zero)."""
     n = msa_decode_mono_workspace_bytes(num_seqs, q_per_seq, num_q_heads, max_blocks)
     return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def mono_check(workspace, num_seqs, q_per_seq, num_q_heads, max_blocks):
+    """Read the error word msa_decode_mono leaves in the last 32 bits of its
+    workspace (waits for the stream). If a bounded wait of an earlier call
+    timed out (error word 1), the counters may hold stale arrivals: the whole
+    counter region, error word included, is zeroed and MsaError is raised."""
+    n = msa_decode_mono_workspace_bytes(num_seqs, q_per_seq, num_q_heads, max_blocks)
+    err = int(workspace[n - 4:n].view(torch.int32).item())
+    if err == 0:
+        return
+    # counters: (num_seqs + pairs) arrival counts of 8 x 16 words, num_seqs
+    # reader counters of 16 words, the error word; 256-byte aligned at the end
+    pairs = num_seqs * q_per_seq * (num_q_heads // 8)
+    words = (num_seqs + pairs) * 128 + num_seqs * 16 + 1
+    region = -(-words * 4 // 256) * 256
+    torch.cuda.current_stream().synchronize()
+    workspace[n - region:n].zero_()
+    torch.cuda.current_stream().synchronize()
+    raise MsaError("msa_decode_mono: a bounded wait timed out (the output of the affected query "
+                   "tokens is zero and their ids -1); the workspace counters were reset")
+
+
+class MonoPrepared(Prepared):
+    """A prepared msa_decode_mono call; check() reads its error word."""
+
+    def __init__(self, args, keep, shape):
+        super().__init__("msa_decode_mono", args, keep)
+        self._shape = shape
+
+    def check(self):
+        mono_check(*self._shape)
 
 
 def mono_block_scores(workspace, num_seqs, q_per_seq, max_blocks):
@@ -436,10 +469,15 @@ def mono_block_scores(workspace, num_seqs, q_per_seq, max_blocks):
 
 def msa_decode_mono(idx_codes, idx_scales, q_idx_fp8, head_w, k_codes, k_scales, v_codes,
                     v_scales, q_fp8, block_table, seq_lens, q_per_seq, softmax_scale, out,
-                    workspace, out_ids=None, topk=TOPK, prepare=False):
+                    workspace, out_ids=None, topk=TOPK, prepare=False, check=True):
     """The whole decode step (index scan, selection, sparse attention) in one
     launch: out float32 [B*Q, Hq, 128], ids into out_ids int32 [B*Q, 17] when
-    given; workspace from mono_workspace()."""
+    given; workspace from mono_workspace().
+
+    check=True (direct calls): wait for the stream and read the launch's
+    error word (mono_check): a timed-out wait raises MsaError after the
+    workspace counters are reset. prepare=True returns a MonoPrepared, whose
+    check() does the same when the caller chooses to synchronise."""
     _check_pool(idx_codes, idx_scales, "idx")
     num_seqs, max_blocks, tq, hq = _check_attn_inputs(k_codes, k_scales, v_codes, v_scales, q_fp8,
                                                       block_table, seq_lens, q_per_seq, out,
@@ -453,9 +491,29 @@ def msa_decode_mono(idx_codes, idx_scales, q_idx_fp8, head_w, k_codes, k_scales,
         if out_ids.shape != (tq, topk + 1):
             raise ValueError("out_ids must be [T_q, topk + 1]")
     idesc, kdesc = pool_desc(idx_codes), pool_desc(k_codes)
-    return _issue("msa_decode_mono", (
-        ctypes.byref(idesc), _ptr(idx_codes), _ptr(idx_scales), _ptr(q_idx_fp8), _ptr(head_w),
-        ctypes.byref(kdesc), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales),
-        _ptr(q_fp8), hq, _ptr(block_table), max_blocks, _ptr(seq_lens), num_seqs, q_per_seq, topk,
-        _ptr(out_ids), float(softmax_scale), _ptr(out), _ptr(workspace), workspace.numel(),
-        _stream()), prepare, keep=(idesc, kdesc))
+    args = (ctypes.byref(idesc), _ptr(idx_codes), _ptr(idx_scales), _ptr(q_idx_fp8), _ptr(head_w),
+            ctypes.byref(kdesc), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales),
+            _ptr(q_fp8), hq, _ptr(block_table), max_blocks, _ptr(seq_lens), num_seqs, q_per_seq,
+            topk, _ptr(out_ids), float(softmax_scale), _ptr(out), _ptr(workspace),
+            workspace.numel(), _stream())
+    shape = (workspace, num_seqs, q_per_seq, hq, max_blocks)
+    if prepare:
+        return MonoPrepared(args, (idesc, kdesc), shape)
+    _issue("msa_decode_mono", args, False)
+    if check:
+        mono_check(*shape)
+    return None
+
+
+def msa_read_probe(buf, chunk_bytes, sink, prepare=False):
+    """Plain streaming read of the device tensor buf (its bytes, a multiple
+    of 16) in chunks of chunk_bytes per workgroup; sink int32 with at least
+    ceil(bytes / chunk_bytes) entries."""
+    if not isinstance(buf, torch.Tensor) or buf.device.type != "cuda" or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous GPU tensor")
+    _need(sink, "sink", torch.int32, 1)
+    n = buf.numel() * buf.element_size()
+    if sink.numel() < -(-n // chunk_bytes):
+        raise ValueError("sink needs one entry per chunk")
+    return _issue("msa_read_probe", (_ptr(buf), n, int(chunk_bytes), _ptr(sink), _stream()),
+                  prepare)

@@ -69,12 +69,31 @@ def check_selection(bscores, ids, topk: int = 16, rel: float = REL):
     return None
 
 
-def check_attention(out, ref, max_abs: float = ATTN_MAX_ABS, mean_abs: float = ATTN_MEAN_ABS):
-    d = np.abs(np.asarray(out, dtype=np.float64) - np.asarray(ref, dtype=np.float64))
+def attention_error(out, ref):
+    """(max |out - ref|, mean |out - ref|) over every element, in float64;
+    (inf, inf) when either side holds a non-finite value or the shapes differ."""
+    a = np.asarray(out, dtype=np.float64)
+    b = np.asarray(ref, dtype=np.float64)
+    if a.shape != b.shape or a.size == 0:
+        return float("inf"), float("inf")
+    d = np.abs(a - b)
     if not np.all(np.isfinite(d)):
+        return float("inf"), float("inf")
+    return float(d.max()), float(d.mean())
+
+
+def check_attention(out, ref, max_abs: float = ATTN_MAX_ABS, mean_abs: float = ATTN_MEAN_ABS):
+    """None when out is within both bars of ref (max-abs AND mean-abs error),
+    else a message. Non-finite values and shape mismatches always fail."""
+    a = np.asarray(out, dtype=np.float64)
+    b = np.asarray(ref, dtype=np.float64)
+    if a.shape != b.shape or a.size == 0:
+        return f"attention shape {a.shape} vs oracle {b.shape}"
+    mx, mean = attention_error(a, b)
+    if not np.isfinite(mx):
         return "non-finite output"
-    if d.max() > max_abs or d.mean() > mean_abs:
-        return f"attention error max {d.max():.3g} mean {d.mean():.3g}"
+    if mx > max_abs or mean > mean_abs:
+        return f"attention error max {mx:.3g} mean {mean:.3g}"
     return None
 
 

@@ -141,15 +141,35 @@ def oracle_kv(wl, b, blocks, overrides=None):
     return kv
 
 
-def check_sequence(wl, b, ids, scores, o, overrides=None, check_scores=True):
-    """Oracle checks of one sequence's query tokens. Returns a list of failures."""
+def record_attention_error(label, errs):
+    """Print (and, when MSA_ATTN_ERROR_LOG names a file, append as a JSON
+    line) the attention error a check reached: the largest max-abs and the
+    largest mean-abs error over its query tokens, against the 2e-2 / 2e-3
+    bars."""
+    import json
+    if not errs:
+        return
+    mx = max(e[0] for e in errs)
+    mean = max(e[1] for e in errs)
+    print(f"[attn-error] {label}: max-abs {mx:.3e} (bar 2e-2), mean-abs {mean:.3e} (bar 2e-3) "
+          f"over {len(errs)} query tokens", flush=True)
+    path = os.environ.get("MSA_ATTN_ERROR_LOG")
+    if path:
+        with open(path, "a") as fh:
+            fh.write(json.dumps({"check": label, "query_tokens": len(errs), "max_abs": mx,
+                                 "mean_abs": mean}) + "\n")
+
+
+def check_sequence(wl, b, ids, scores, o, overrides=None, check_scores=True, label=None):
+    """Oracle checks of one sequence's query tokens. Returns a list of
+    failures; prints the attention error reached (record_attention_error)."""
     from oracle import msa
-    from oracle.acceptance import check_attention, check_selection
+    from oracle.acceptance import attention_error, check_attention, check_selection
     bscores = oracle_block_scores(wl, b, overrides)
     rows = [b * wl.q_per_seq + i for i in range(wl.q_per_seq)]
     kv = oracle_kv(wl, b, np.concatenate([ids[r] for r in rows]), overrides)
     q_attn = fp8_values(wl.q_attn())
-    fails = []
+    fails, errs = [], []
     scale = 1.0 / math.sqrt(128)
     for i, pos in enumerate(wl.positions(b)):
         row = rows[i]
@@ -168,9 +188,11 @@ def check_sequence(wl, b, ids, scores, o, overrides=None, check_scores=True):
                 fails.append(f"seq {b} q {i}: block scores off by {rel:.3g} rel")
         ref_o = msa.sparse_attention(q_attn[row], kv[synth.STREAM_K], kv[synth.STREAM_V], gids,
                                      pos, scale)
+        errs.append(attention_error(o[row], ref_o))
         msg = check_attention(o[row], ref_o)
         if msg:
             fails.append(f"seq {b} q {i}: {msg}")
+    record_attention_error(label or f"{wl.name} seq {b}", errs)
     return fails
 
 

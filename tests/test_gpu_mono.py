@@ -109,6 +109,12 @@ MONO_CASES = [
     ([3, 4000], 3, False),
     ([3900], 8, False),
     ([8 * 128 + 3, 19 * 128 + 7], 4, False),
+    # more than 64 candidates: the selection's threshold and compaction on
+    # device-scope score loads, up to the entry point's bound of 1,024 block
+    # workgroups (1 x 32K, 2 x 16K with one query token)
+    ([16384], 1, True),
+    ([32768], 1, True),
+    ([16384, 16384 - 37], 1, True),
 ]
 
 
@@ -186,3 +192,20 @@ def test_mono_full_size_tiny_workload(nb):
     say(f"mono on {wl.name}")
     fails, _ = _check(nb, wl, True)
     assert not fails, "\n".join(fails)
+
+
+def test_mono_many_equal_scores(nb):
+    """1 x 16K where 120 of the 127 candidate blocks alias one physical page,
+    so more than 64 candidates tie at the threshold and the selection ranks
+    them by arg-max rounds on device-scope loads: the lowest aliased blocks
+    win the ties, bit-identical to the three-kernel path."""
+    say("mono with 120 tied candidates (aliased page)")
+    wl = tiny_config([16384], 1, seed=91, spare_pages=0, permute=False)
+    bt = wl.block_table
+    bt[0, 7:127] = bt[0, 3]                     # blocks 3 and 7..126 share a page
+    fails, (ids, bsc, o, ws, pools, inp) = _check(nb, wl, True)
+    assert not fails, "\n".join(fails)
+    sc = bsc[0, :127]
+    assert np.count_nonzero(sc == sc[3]) == 121
+    want = sorted(int(x) for x in np.lexsort((np.arange(127), -sc))[:16]) + [127]
+    assert ids[0].tolist() == want

@@ -600,3 +600,100 @@ def test_shared_prefix_scan_without_groups_is_plain_scan(nb):
                                torch.zeros(0, **i32), 0, torch.zeros(wl.num_seqs, **i32), got)
     torch.cuda.synchronize()
     assert torch.equal(ref.view(torch.int32), got.view(torch.int32))
+
+
+# msa_sparse_attn_decode with the caller's selection and num_sel from 1 to
+# 64 slots, through each form of the launch plan: one workgroup per slot
+# (the four wavefronts share each block) while pairs x num_sel <= 384, else
+# whole blocks per wavefront with 1 or 2 slots per wavefront and the split
+# merge, or one split per pair written directly. (num_sel, lengths, query
+# tokens per sequence, plan exercised.)
+def _numsel_lens(n, lo, hi, seed):
+    return [int(x) for x in np.random.default_rng(seed).integers(lo, hi, size=n)]
+
+
+NUMSEL = [
+    (1, [3000, 700, 129], 1, "shared-block waves"),
+    (1, _numsel_lens(100, 300, 700, 1), 1, "whole blocks, 1 slot per wave"),
+    (5, [3000, 2000, 129, 40], 2, "shared-block waves"),
+    (5, _numsel_lens(25, 1000, 3000, 2), 1, "whole blocks, 2 splits"),
+    (33, [5000, 4000], 1, "shared-block waves, 33 partials merged"),
+    (33, [5000, 4000, 3000], 1, "whole blocks, 9 splits"),
+    (33, _numsel_lens(16, 4300, 6000, 3), 1, "whole blocks, 2 slots per wave, 5 splits"),
+    (33, [5000, 4300], 4, "whole blocks, 9 splits, 4 query tokens"),
+    (64, [9000], 1, "shared-block waves, 64 partials merged"),
+    (64, [9000, 8500], 1, "whole blocks, 16 splits"),
+    (64, _numsel_lens(12, 8300, 9500, 4), 1, "whole blocks, 2 slots per wave, 8 splits"),
+    (64, _numsel_lens(40, 8300, 9000, 5), 1, "whole blocks, one split of 16 slots per wave"),
+]
+
+
+def _numsel_ids(wl, num_sel, rng):
+    """int32 [T_q, num_sel]: distinct visible blocks in random order; some
+    rows also hold entries the kernel must ignore (-1, a block past the
+    query token's position, a block past the block table), and one row
+    holds nothing usable."""
+    ids = np.full((wl.num_q_tokens, num_sel), -1, dtype=np.int32)
+    for b in range(wl.num_seqs):
+        for i, pos in enumerate(wl.positions(b)):
+            r = b * wl.q_per_seq + i
+            nvis = pos // 128 + 1
+            junk = []
+            if num_sel >= 4 and r % 3 == 1:
+                junk = [-1, wl.max_blocks + 3]
+                if nvis < wl.max_blocks:
+                    junk.append(nvis)              # past this token's position
+            k = min(num_sel - len(junk), nvis)
+            row = list(rng.choice(nvis, size=k, replace=False)) + junk
+            rng.shuffle(row)
+            ids[r, :len(row)] = row
+    if wl.num_q_tokens > 2:
+        ids[2] = -1                                # nothing usable: zero output
+        ids[2, 0] = wl.max_blocks + 1
+    return ids
+
+
+@pytest.mark.parametrize("num_sel,lens,q,plan", NUMSEL,
+                         ids=[f"{n}sel-{len(ls)}x{q}-{p.split(',')[0].replace(' ', '_')}"
+                              for n, ls, q, p in NUMSEL])
+def test_attention_num_sel(nb, num_sel, lens, q, plan):
+    from oracle import msa
+    from oracle.acceptance import attention_error, check_attention
+    say(f"msa_sparse_attn_decode num_sel={num_sel}, {len(lens)} sequences x {q}: {plan}")
+    wl = tiny_config(lens, q, seed=300 + num_sel + len(lens))
+    pools = S.fill_pools(wl, nb)
+    inp = S.device_inputs(wl)
+    rng = np.random.default_rng(num_sel * 1000 + len(lens))
+    ids = _numsel_ids(wl, num_sel, rng)
+    kc, ks = pools[synth.STREAM_K]
+    vc, vs = pools[synth.STREAM_V]
+    tq = wl.num_q_tokens
+    ws = nb.attn_workspace(wl.num_seqs, q, wl.num_q_heads, num_sel)
+    o = torch.full((tq, wl.num_q_heads, 128), float("nan"), dtype=torch.float32, device="cuda")
+    scale = 1.0 / math.sqrt(128)
+    nb.msa_sparse_attn_decode(kc, ks, vc, vs, inp["q_attn"], inp["block_table"], inp["seq_lens"],
+                              q, torch.from_numpy(ids).cuda(), scale, o, ws)
+    torch.cuda.synchronize()
+    on = o.cpu().numpy()
+    assert np.all(np.isfinite(on))
+    if tq > 2:
+        assert np.all(on[2] == 0)
+    q_attn = S.fp8_values(wl.q_attn())
+    seqs = sorted({0, 1 % wl.num_seqs, wl.num_seqs // 2, wl.num_seqs - 1})
+    fails, errs = [], []
+    for b in seqs:
+        rows = [b * q + i for i in range(q)]
+        blocks = [int(x) for r in rows for x in ids[r] if 0 <= x < wl.blocks_of(b)]
+        kv = S.oracle_kv(wl, b, blocks)
+        for i, pos in enumerate(wl.positions(b)):
+            r = rows[i]
+            if r == 2 and tq > 2:
+                continue
+            ref = msa.sparse_attention(q_attn[r], kv[synth.STREAM_K], kv[synth.STREAM_V], ids[r],
+                                       pos, scale)
+            errs.append(attention_error(on[r], ref))
+            msg = check_attention(on[r], ref)
+            if msg:
+                fails.append(f"seq {b} q {i}: {msg}")
+    S.record_attention_error(f"num_sel {num_sel}, {plan}", errs)
+    assert not fails, "\n".join(fails[:20])
