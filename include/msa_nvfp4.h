@@ -24,8 +24,9 @@
  *    msa_pool_desc pointers, which are host memory read during the call.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  *    stream); an entry point enqueues one or two kernels on it. The library
- *    allocates nothing and keeps no state between calls; two calls may run
- *    concurrently only if they use different workspaces.
+ *    allocates nothing and, apart from the device array behind
+ *    msa_indexer_decode_noalloc, keeps no state between calls; two calls may
+ *    run concurrently only if they use different workspaces.
  *  - Arguments are checked on the host before anything is launched; a failed
  *    check returns a status and launches nothing. MSA_ERR_HIP reports a failed
  *    kernel launch. Device data (block tables, sequence lengths, selected ids,
@@ -144,6 +145,31 @@ msa_status msa_indexer_decode(const msa_pool_desc* idx, const uint8_t* idx_codes
                               const int32_t* seq_lens, int32_t num_seqs, int32_t q_per_seq,
                               int32_t topk, int32_t* out_ids, float* out_scores,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * msa_indexer_decode for callers that cannot allocate device memory or pass
+ * a workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation. The same arguments without the workspace, and the
+ * same results: the block scores live in a device array of the library
+ * (MSA_NOALLOC_MAX_SCORES fp32 values, 4 MiB, one copy per GPU, held until the
+ * process ends) instead of the caller's workspace.
+ *   num_seqs * q_per_seq * max_blocks must not exceed MSA_NOALLOC_MAX_SCORES
+ *   (else MSA_ERR_WORKSPACE, nothing launched).
+ * The first call on a device looks the array's address up (no allocation);
+ * every call on one GPU shares the array, so calls that may overlap on one
+ * GPU (other streams, other threads) race on it and must be serialised by
+ * the caller. Its contents need no initialisation: each call writes every
+ * score it reads. Other arguments, device-side checks and errors as
+ * msa_indexer_decode.
+ */
+#define MSA_NOALLOC_MAX_SCORES (1 << 20)
+msa_status msa_indexer_decode_noalloc(const msa_pool_desc* idx, const uint8_t* idx_codes,
+                                      const uint8_t* idx_scales, const uint8_t* q_fp8,
+                                      const float* head_w, int32_t num_q_heads,
+                                      const int32_t* block_table, int32_t max_blocks,
+                                      const int32_t* seq_lens, int32_t num_seqs,
+                                      int32_t q_per_seq, int32_t topk, int32_t* out_ids,
+                                      float* out_scores, void* stream);
 
 /*
  * The indexer in two stages, for callers that keep the block scores (for

@@ -46,6 +46,8 @@ SIGNATURES = {
     "msa_indexer_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
     "msa_indexer_decode": (ctypes.c_int, [_DESC, _P, _P, _P, _P, _I32, _P, _I32, _P, _I32, _I32,
                                           _I32, _P, _P, _P, _SZ, _P]),
+    "msa_indexer_decode_noalloc": (ctypes.c_int, [_DESC, _P, _P, _P, _P, _I32, _P, _I32, _P, _I32,
+                                                  _I32, _I32, _P, _P, _P]),
     "msa_indexer_scan": (ctypes.c_int, [_DESC, _P, _P, _P, _P, _I32, _P, _I32, _P, _I32, _I32,
                                         _P, _P]),
     "msa_indexer_scan_shared": (ctypes.c_int, [_DESC, _P, _P, _P, _P, _I32, _P, _I32, _P, _I32,
@@ -274,6 +276,31 @@ def msa_indexer_decode(idx_codes, idx_scales, q_fp8, head_w, block_table, seq_le
         ctypes.byref(desc), _ptr(idx_codes), _ptr(idx_scales), _ptr(q_fp8), _ptr(head_w), hq,
         _ptr(block_table), max_blocks, _ptr(seq_lens), num_seqs, q_per_seq, topk, _ptr(out_ids),
         _ptr(out_scores), _ptr(workspace), workspace.numel(), _stream()), prepare, keep=(desc,))
+
+
+NOALLOC_MAX_SCORES = 1 << 20   # MSA_NOALLOC_MAX_SCORES
+
+
+def msa_indexer_decode_noalloc(idx_codes, idx_scales, q_fp8, head_w, block_table, seq_lens,
+                               q_per_seq, out_ids, out_scores=None, topk=TOPK, prepare=False):
+    """msa_indexer_decode without a workspace: the block scores live in the
+    library's own device array (at most NOALLOC_MAX_SCORES = T_q x max_blocks
+    entries); calls on one GPU share it and must not overlap."""
+    _check_pool(idx_codes, idx_scales, "idx")
+    num_seqs, max_blocks, tq, hq = _check_indexer_inputs(q_fp8, head_w, block_table, seq_lens,
+                                                         q_per_seq)
+    _need(out_ids, "out_ids", torch.int32, 2)
+    if out_ids.shape != (tq, topk + 1):
+        raise ValueError("out_ids must be [T_q, topk+1]")
+    if out_scores is not None:
+        _need(out_scores, "out_scores", torch.float32, 2)
+        if out_scores.shape != out_ids.shape:
+            raise ValueError("out_scores must match out_ids")
+    desc = pool_desc(idx_codes)
+    return _issue("msa_indexer_decode_noalloc", (
+        ctypes.byref(desc), _ptr(idx_codes), _ptr(idx_scales), _ptr(q_fp8), _ptr(head_w), hq,
+        _ptr(block_table), max_blocks, _ptr(seq_lens), num_seqs, q_per_seq, topk, _ptr(out_ids),
+        _ptr(out_scores), _stream()), prepare, keep=(desc,))
 
 
 def _check_indexer_inputs(q_fp8, head_w, block_table, seq_lens, q_per_seq):

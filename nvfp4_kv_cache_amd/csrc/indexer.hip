@@ -22,6 +22,8 @@
 // and maximised over the block's visible tokens, giving one fp32 block score
 // per (query token, block). The selection kernel then picks, per query
 // token, the top-16 blocks plus the most recent one.
+#include <atomic>
+
 #include "msa_nvfp4.h"
 #include "nvfp4_tile.h"
 #include "topk_select.h"
@@ -382,15 +384,15 @@ extern "C" size_t msa_indexer_workspace_bytes(int32_t num_seqs, int32_t q_per_se
   return msa::align256(size_t(num_seqs) * q_per_seq * max_blocks * 4);
 }
 
-extern "C" msa_status msa_indexer_decode(const msa_pool_desc* idx, const uint8_t* idx_codes,
-                                         const uint8_t* idx_scales, const uint8_t* q_fp8,
-                                         const float* head_w, int32_t num_q_heads,
-                                         const int32_t* block_table, int32_t max_blocks,
-                                         const int32_t* seq_lens, int32_t num_seqs,
-                                         int32_t q_per_seq, int32_t topk, int32_t* out_ids,
-                                         float* out_scores, void* workspace,
-                                         size_t workspace_bytes, void* stream) {
-  using namespace msa;
+namespace msa {
+
+// Host checks of msa_indexer_decode's arguments other than the workspace.
+static msa_status check_decode(const msa_pool_desc* idx, const uint8_t* idx_codes,
+                               const uint8_t* idx_scales, const uint8_t* q_fp8,
+                               const float* head_w, int32_t num_q_heads,
+                               const int32_t* block_table, int32_t max_blocks,
+                               const int32_t* seq_lens, int32_t num_seqs, int32_t q_per_seq,
+                               int32_t topk, const int32_t* out_ids, const float* out_scores) {
   if (!idx) return MSA_ERR_INVALID_ARG;
   msa_status st = check_indexer_shape(num_seqs, q_per_seq, max_blocks);
   if (st != MSA_OK) return st;
@@ -407,10 +409,80 @@ extern "C" msa_status msa_indexer_decode(const msa_pool_desc* idx, const uint8_t
       misaligned(head_w, 3) || misaligned(block_table, 3) || misaligned(seq_lens, 3) ||
       misaligned(out_ids, 3) || misaligned(out_scores, 3))
     return MSA_ERR_INVALID_ARG;
+  return MSA_OK;
+}
+
+// The block scores of msa_indexer_decode_noalloc live in this array instead
+// of a caller's workspace: one copy per GPU the library runs on, resident
+// until the process ends. Host code never passes the array's name to a
+// kernel (on the host it is only a stand-in for the symbol); it uses the
+// device address hipGetSymbolAddress returns, looked up once per device.
+static __device__ __align__(256) float scratch[MSA_NOALLOC_MAX_SCORES];
+
+constexpr int kMaxDevices = 64;
+static std::atomic<float*> g_scratch[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up on the first
+// call for that device; two threads racing here store the same address).
+static msa_status scratch_address(float** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MSA_ERR_HIP;
+  float* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return MSA_ERR_HIP;
+    p = static_cast<float*>(q);
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return MSA_OK;
+}
+
+}  // namespace msa
+
+extern "C" msa_status msa_indexer_decode(const msa_pool_desc* idx, const uint8_t* idx_codes,
+                                         const uint8_t* idx_scales, const uint8_t* q_fp8,
+                                         const float* head_w, int32_t num_q_heads,
+                                         const int32_t* block_table, int32_t max_blocks,
+                                         const int32_t* seq_lens, int32_t num_seqs,
+                                         int32_t q_per_seq, int32_t topk, int32_t* out_ids,
+                                         float* out_scores, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  using namespace msa;
+  msa_status st = check_decode(idx, idx_codes, idx_scales, q_fp8, head_w, num_q_heads,
+                               block_table, max_blocks, seq_lens, num_seqs, q_per_seq, topk,
+                               out_ids, out_scores);
+  if (st != MSA_OK || num_seqs == 0) return st;
   const size_t need = msa_indexer_workspace_bytes(num_seqs, q_per_seq, max_blocks);
   if (!workspace || workspace_bytes < need || misaligned(workspace, 255)) return MSA_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* scores = static_cast<float*>(workspace);
+  st = launch_scan(idx, idx_codes, idx_scales, q_fp8, head_w, num_q_heads, block_table, max_blocks,
+                   seq_lens, num_seqs, q_per_seq, scores, s);
+  if (st != MSA_OK) return st;
+  return launch_select(scores, seq_lens, max_blocks, num_seqs, q_per_seq, out_ids, out_scores, s);
+}
+
+extern "C" msa_status msa_indexer_decode_noalloc(const msa_pool_desc* idx,
+                                                 const uint8_t* idx_codes,
+                                                 const uint8_t* idx_scales, const uint8_t* q_fp8,
+                                                 const float* head_w, int32_t num_q_heads,
+                                                 const int32_t* block_table, int32_t max_blocks,
+                                                 const int32_t* seq_lens, int32_t num_seqs,
+                                                 int32_t q_per_seq, int32_t topk,
+                                                 int32_t* out_ids, float* out_scores,
+                                                 void* stream) {
+  using namespace msa;
+  msa_status st = check_decode(idx, idx_codes, idx_scales, q_fp8, head_w, num_q_heads,
+                               block_table, max_blocks, seq_lens, num_seqs, q_per_seq, topk,
+                               out_ids, out_scores);
+  if (st != MSA_OK || num_seqs == 0) return st;
+  if (int64_t(num_seqs) * q_per_seq * max_blocks > int64_t(MSA_NOALLOC_MAX_SCORES))
+    return MSA_ERR_WORKSPACE;
+  float* scores = nullptr;
+  st = scratch_address(&scores);
+  if (st != MSA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
   st = launch_scan(idx, idx_codes, idx_scales, q_fp8, head_w, num_q_heads, block_table, max_blocks,
                    seq_lens, num_seqs, q_per_seq, scores, s);
   if (st != MSA_OK) return st;

@@ -103,6 +103,26 @@ def test_indexer_rejects_before_launch(L):
     assert call(desc=ctypes.byref(_desc(bt=64))) == 2
 
 
+def test_noalloc_indexer_rejects_before_launch(L):
+    # the same argument checks as msa_indexer_decode, and more block scores
+    # than the library's device array holds is refused (nothing launched)
+    f = L.msa_indexer_decode_noalloc
+    d = ctypes.byref(_desc())
+
+    def call(desc=d, q=32, mb=4, ns=1, qps=1, topk=16, ptr=256):
+        return f(desc, ptr, ptr, ptr, ptr, q, ptr, mb, ptr, ns, qps, topk, ptr, None, None)
+    assert nb.NOALLOC_MAX_SCORES == 1 << 20
+    assert call(desc=None) == 1
+    assert call(q=16) == 2
+    assert call(topk=8) == 2
+    assert call(qps=9) == 2
+    assert call(ns=0) == 0
+    assert call(ptr=None) == 1
+    assert call(ptr=4096 + 8) == 1
+    assert call(ns=1025, mb=1024) == 3           # 1,049,600 scores > 2^20
+    assert call(ns=128, qps=8, mb=1025) == 3     # 1,049,600 scores > 2^20
+
+
 def test_attention_rejects_before_launch(L):
     f = L.msa_sparse_attn_decode
     d = ctypes.byref(_desc())
