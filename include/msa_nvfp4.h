@@ -36,7 +36,13 @@
  *    codes, scales, queries, workspaces, outputs.
  *  - Supported shapes: head_dim 128, block_tokens 128, topk 16, and 8 query
  *    heads per KV / index-key head (num_q_heads == 8 * num_heads); other
- *    values return MSA_ERR_UNSUPPORTED.
+ *    values return MSA_ERR_UNSUPPORTED. The GQA ratio is fixed at 8 because
+ *    the 8 query heads of a KV / index-key head fill half of a 16-row FP8
+ *    matrix-core tile (two query tokens fill all of it in the scan): the
+ *    tiles, the head-pair exchange of the scan and the attention's softmax
+ *    rows are laid out for exactly 8 heads. (A general integer ratio would
+ *    need other tile shapes; the workloads this library serves use 32 query
+ *    heads over 4 KV heads.)
  *
  * Paged pool layout (one pool per cache: K, V and index keys), per page of
  * 128 token slots; a token in slot s lives in page s / 128, row s % 128:
@@ -46,7 +52,10 @@
  *   scales uint8 [num_pages][num_heads][1024]  E4M3 scale of row r, channels
  *          16g .. 16g+15 (g = 0..7) at byte ((g/2)*16 + r%16)*16 + (r/16)*2 + g%2
  *          of its (page, head): tile-major, so one 16-byte load gives a
- *          lane all 8 row-tiles' scales of its rows and 32-channel slice
+ *          lane all 8 row-tiles' scales of its rows and 32-channel slice.
+ *          (The same bytes as a row-major [128][8] array per (page, head),
+ *          permuted: a row-major array would need 8 scattered 2-byte loads
+ *          per lane per block instead of one 16-byte load.)
  *
  * Sequences: sequence b has seq_lens[b] tokens in its pages, including its
  * q_per_seq query tokens (their keys are already written). Query token i of
@@ -339,7 +348,11 @@ msa_status msa_sparse_attn_select_decode(const msa_pool_desc* kv, const uint8_t*
  * Workspace bytes msa_decode_mono needs: the fp32 block scores
  * [num_seqs * q_per_seq][max_blocks] (at offset 0), the attention partials of
  * every block, and the launch's arrival counters. Zero-fill it before its
- * first use: the counters must start at zero, and every call leaves them zero.
+ * first use: the counters must start at zero, and a call leaves them zero as
+ * long as none of its bounded waits times out (the error word, below, stays
+ * 0). After a timeout the counters may hold late arrivals: zero the counter
+ * region again (the caller's, once the stream is idle) before reusing the
+ * workspace.
  */
 size_t msa_decode_mono_workspace_bytes(int32_t num_seqs, int32_t q_per_seq, int32_t num_q_heads,
                                        int32_t max_blocks);
@@ -380,7 +393,9 @@ size_t msa_decode_mono_workspace_bytes(int32_t num_seqs, int32_t q_per_seq, int3
  * still bounded (20 ms), and one that times out gives that query token zero
  * output and ids -1 and sets the error word, the last 32-bit word of the
  * msa_decode_mono_workspace_bytes(...) bytes, to 1; it stays set until the
- * caller zeroes it.
+ * caller zeroes it. The counter region is the last
+ * align256(4 * ((num_seqs + pairs) * 128 + num_seqs * 16 + 1)) bytes of
+ * those, pairs = num_seqs * q_per_seq * 4.
  */
 msa_status msa_decode_mono(const msa_pool_desc* idx, const uint8_t* idx_codes,
                            const uint8_t* idx_scales, const uint8_t* q_idx_fp8,

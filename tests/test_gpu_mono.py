@@ -209,3 +209,24 @@ def test_mono_many_equal_scores(nb):
     assert np.count_nonzero(sc == sc[3]) == 121
     want = sorted(int(x) for x in np.lexsort((np.arange(127), -sc))[:16]) + [127]
     assert ids[0].tolist() == want
+
+
+def test_mono_error_word_raises_and_resets_counters(nb):
+    """The binding reads the launch's error word after a direct call; a set
+    word (a bounded wait that timed out) raises MsaError and zeroes the whole
+    counter region, so the next call starts from zero counters. The timeout
+    is simulated from the host by setting the word and a stale counter."""
+    say("mono error word: raise and reset")
+    wl = tiny_config([2500, 700], 1, seed=17)
+    pools = S.fill_pools(wl, nb)
+    inp = S.device_inputs(wl)
+    ids, bsc, o, ws = _run_mono(nb, wl, pools, inp)
+    n = nb.msa_decode_mono_workspace_bytes(wl.num_seqs, 1, wl.num_q_heads, wl.max_blocks)
+    ws[n - 4:n].view(torch.int32).fill_(1)          # error word
+    ws[n - 256:n - 252].view(torch.int32).fill_(3)   # a stale arrival in the counter region
+    with pytest.raises(nb.MsaError, match="timed out"):
+        nb.mono_check(ws, wl.num_seqs, 1, wl.num_q_heads, wl.max_blocks)
+    assert _sync_region_zero(ws, wl)
+    again = _run_mono(nb, wl, pools, inp, ws)
+    assert np.array_equal(again[0], ids)
+    assert np.array_equal(again[2].view(np.uint32), o.view(np.uint32))
