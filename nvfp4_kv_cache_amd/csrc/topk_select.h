@@ -64,12 +64,13 @@ __device__ __forceinline__ float load_score(const float* p) {
 
 // One chunk of a query token's block scores: lane l gets entries
 // c0 + l + 64 k. The loads go through a buffer descriptor over the row
-// (row_len entries; a buffer load past the record count returns 0 and reads
-// nothing), with one 32-bit lane offset plus the constant stride of k:
-// nothing is predicated, so all 32 loads are in flight at once, and no
-// per-element 64-bit address is formed. The whole offset is a lane (vector)
-// offset, which the descriptor's range check covers (the scalar offset
-// operand is left 0). Entries past the candidates are masked by index later.
+// (row_len entries), with one 32-bit lane offset and the stride of k in the
+// scalar offset operand: nothing is predicated, so all 32 loads are in flight
+// at once, no per-element 64-bit address is formed, and no vector register
+// holds a per-k offset. The descriptor's range check covers the lane offset
+// plus the scalar offset (an in-bounds probe on gfx950: a load whose scalar
+// offset alone passes the record count returns 0), so entries past the row
+// read as 0 and touch no memory; they are masked by index later anyway.
 // COHERENT: device-scope loads.
 template <bool COHERENT = false>
 __device__ __forceinline__ void load_score_chunk(const float* row, int row_len, int c0, int lane,
@@ -80,7 +81,7 @@ __device__ __forceinline__ void load_score_chunk(const float* row, int row_len, 
 #pragma unroll
   for (int k = 0; k < kSelPerLane; ++k)
     x[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                         r, off + uint32_t(64 * k * int(sizeof(float))), 0,
+                                         r, off, 64 * k * int(sizeof(float)),
                                          COHERENT ? kDeviceScopeLoad : 0));
 }
 
