@@ -576,8 +576,8 @@ def main():
     # A batch whose sequences share leading pages (a cached common prefix)
     # is scanned with msa_indexer_scan_shared: each shared block is read and
     # dequantised once for all the sequences that share it.
-    groups = shared_groups(wl)
-    dedup = groups[3] > 0
+    groups = shared_groups(wl, nb)
+    dedup = groups[2] > 0
     if dedup:
         scan = nb.msa_indexer_scan_shared(ic, isc, inp["q_idx"], inp["w"], inp["block_table"],
                                           inp["seq_lens"], wl.q_per_seq, *groups, bscores,
@@ -787,8 +787,8 @@ def main():
                    "kv_heads": wl.num_kv_heads, "index_heads": wl.num_idx_heads,
                    "q_heads": wl.num_q_heads, "head_dim": 128, "block_tokens": 128,
                    "topk": wl.topk,
-                   "shared_prefix_groups": int(len(groups[2])),
-                   "shared_prefix_blocks": [int(x) for x in groups[2].cpu().tolist()]},
+                   "shared_prefix_groups": int(len(groups[0])),
+                   "shared_prefix_blocks": [int(x) for x in groups[1].cpu().tolist()]},
         "achieved_hbm_gbs": round(step_bytes / (med * 1e-6) / 1e9, 1),
         "hbm_frac_of_peak": round(step_bytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": int(step_bytes),

@@ -200,39 +200,59 @@ msa_status msa_indexer_scan(const msa_pool_desc* idx, const uint8_t* idx_codes,
 /*
  * msa_indexer_scan for a batch in which groups of sequences share leading
  * blocks: the same physical pages at the same logical block indices, as a
- * cached common prefix gives. Each shared block is read and dequantised once
- * per call and scored against the query tokens of every member of its group;
- * the other blocks are scanned as by msa_indexer_scan. The block scores are
- * the values msa_indexer_scan writes for the same inputs. (MiniMax-M3.1-Flash
- * serving summary, section "AMD uses different conversion and communication
- * mechanisms": shared prefixes reduce repeated dequantisation across
- * requests.)
- *   num_groups         groups of sequences, 0 .. 65535 (0: msa_indexer_scan)
- *   group_start        int32 [num_groups + 1], device: the members of group g
- *                      are group_seqs[group_start[g] .. group_start[g + 1])
- *   group_seqs         int32 sequence ids, device; a sequence is in at most
- *                      one group
- *   group_blocks       int32 [num_groups], device: leading blocks group g
- *                      shares; for every member b and j < group_blocks[g],
- *                      block_table[b][j] == block_table[first member][j]
- *   max_group_blocks   host: >= every group_blocks[g], in [1, max_blocks]
+ * cached common prefix gives (MiniMax-M3.1-Flash serving summary, section
+ * "AMD uses different conversion and communication mechanisms": shared
+ * prefixes reduce repeated dequantisation across requests). One launch: each
+ * shared block is read once and dequantised once, into registers, and scored
+ * against the query tokens of every member of its group; the other blocks
+ * are scanned as by msa_indexer_scan, by the same kernel. The block scores
+ * are the values msa_indexer_scan writes for the same inputs.
+ * Groups (device arrays; msa_shared_prefix_groups derives them from a host
+ * copy of the block table):
+ *   num_groups         0 .. 65535 (0: msa_indexer_scan)
+ *   group_lead         int32 [num_groups]: a sequence whose pages define the
+ *                      group's shared pages
+ *   group_blocks       int32 [num_groups]: leading blocks the group shares
+ *   max_group_blocks   host: >= every group_blocks entry, in [1, max_blocks]
  *                      (ignored when num_groups == 0)
- *   seq_shared_blocks  int32 [num_seqs], device: group_blocks of the group
- *                      of sequence b, 0 for a sequence in no group
- * Other arguments as msa_indexer_scan. group_start must be non-decreasing
- * and index group_seqs; other breaches of these rules give wrong scores but
- * no out-of-bounds access (member ids outside the batch are skipped, block
- * counts are clamped to max_blocks).
+ *   seq_group          int32 [num_seqs]: the group of each sequence, -1: none
+ * Block j of sequence b is scored by its group's shared pass when
+ * g = seq_group[b] is in [0, num_groups), j < min(group_blocks[g],
+ * max_blocks), group_lead[g] is a sequence of the batch, and b's page of
+ * block j equals the lead's; otherwise by the regular scan. Any group arrays
+ * therefore give the scores of msa_indexer_scan; groups that do not match
+ * the block table only share less. Other arguments as msa_indexer_scan.
  */
 msa_status msa_indexer_scan_shared(const msa_pool_desc* idx, const uint8_t* idx_codes,
                                    const uint8_t* idx_scales, const uint8_t* q_fp8,
                                    const float* head_w, int32_t num_q_heads,
                                    const int32_t* block_table, int32_t max_blocks,
                                    const int32_t* seq_lens, int32_t num_seqs, int32_t q_per_seq,
-                                   int32_t num_groups, const int32_t* group_start,
-                                   const int32_t* group_seqs, const int32_t* group_blocks,
-                                   int32_t max_group_blocks, const int32_t* seq_shared_blocks,
-                                   float* block_scores, void* stream);
+                                   int32_t num_groups, const int32_t* group_lead,
+                                   const int32_t* group_blocks, int32_t max_group_blocks,
+                                   const int32_t* seq_group, float* block_scores, void* stream);
+
+/*
+ * Shared-prefix groups of a batch, derived on the host from a HOST copy of
+ * its block table and sequence lengths (a serving engine keeps both): the
+ * sequences with a valid length (q_per_seq <= seq_lens[b] <= max_blocks * 128)
+ * are grouped by the page of their block 0; a group of two or more members
+ * shares the longest run of leading blocks whose pages are the same, and
+ * not negative, in every member, within every member's own blocks
+ * (ceil(seq_lens / 128)); its lead is its lowest-numbered member. Groups are
+ * numbered in the order of their leads.
+ *   block_table int32 [num_seqs][max_blocks], seq_lens int32 [num_seqs]: host
+ *   group_lead, group_blocks: host int32 arrays of num_seqs entries (the first
+ *               *num_groups are written); seq_group: host int32 [num_seqs]
+ *               (-1 for a sequence in no group)
+ *   *num_groups, *max_group_blocks: host outputs (0, 0 with no group)
+ * The outputs, copied to the device, are msa_indexer_scan_shared's group
+ * arguments. Runs on the calling thread; no device work.
+ */
+msa_status msa_shared_prefix_groups(const int32_t* block_table, int32_t max_blocks,
+                                    const int32_t* seq_lens, int32_t num_seqs, int32_t q_per_seq,
+                                    int32_t* group_lead, int32_t* group_blocks, int32_t* seq_group,
+                                    int32_t* num_groups, int32_t* max_group_blocks);
 
 /*
  * msa_indexer_select reads block_scores (as written by msa_indexer_scan) and

@@ -54,38 +54,6 @@ class Workload:
         ids = [self.block_table[b, : self.blocks_of(b)] for b in range(self.num_seqs)]
         return np.unique(np.concatenate(ids)).astype(np.int64)
 
-    def shared_prefix_groups(self):
-        """Groups of sequences whose leading logical blocks map to the same
-        physical pages (a cached common prefix), from the block table:
-        sequences are grouped by their first page, and a group shares the
-        longest run of leading pages common to all of its members (at most
-        each member's own block count). Groups of one are dropped.
-        Returns numpy int32 arrays (group_start [G+1], group_seqs,
-        group_blocks [G], seq_shared_blocks [B])."""
-        by_first = {}
-        for b in range(self.num_seqs):
-            if self.blocks_of(b) > 0:
-                by_first.setdefault(int(self.block_table[b, 0]), []).append(b)
-        start, seqs, blocks = [0], [], []
-        shared = np.zeros(self.num_seqs, dtype=np.int32)
-        for members in by_first.values():
-            if len(members) < 2:
-                continue
-            n = min(self.blocks_of(b) for b in members)
-            ref = self.block_table[members[0], :n]
-            for b in members[1:]:
-                same = self.block_table[b, :n] == ref
-                n = int(np.argmin(same)) if not same.all() else n
-                ref = ref[:n]
-            if n == 0:
-                continue
-            seqs += members
-            start.append(len(seqs))
-            blocks.append(n)
-            shared[members] = n
-        return (np.asarray(start, dtype=np.int32), np.asarray(seqs, dtype=np.int32),
-                np.asarray(blocks, dtype=np.int32), shared)
-
     def num_heads_of(self, stream: int) -> int:
         return self.num_idx_heads if stream == synth.STREAM_IDX else self.num_kv_heads
 

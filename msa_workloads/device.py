@@ -62,13 +62,14 @@ def fill_pools(wl, nb, device="cuda", garbage=True, chunk_pages=256, overrides=N
     return pools
 
 
-def shared_groups(wl, device="cuda"):
-    """The workload's shared-prefix groups as device int32 tensors plus the
-    largest group block count: (group_start, group_seqs, group_blocks,
-    max_group_blocks, seq_shared_blocks)."""
-    start, seqs, blocks, shared = wl.shared_prefix_groups()
-    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)  # noqa: E731
-    return (to(start), to(seqs), to(blocks), int(blocks.max()) if len(blocks) else 0, to(shared))
+def shared_groups(wl, nb, device="cuda"):
+    """The workload's shared-prefix groups as the library derives them from
+    a host copy of the block table (nb.msa_shared_prefix_groups): device
+    tensors (group_lead, group_blocks), the host int max_group_blocks, and
+    the device tensor seq_group."""
+    bt = torch.from_numpy(np.ascontiguousarray(wl.block_table, dtype=np.int32))
+    lens = torch.tensor(wl.seq_lens, dtype=torch.int32)
+    return nb.msa_shared_prefix_groups(bt, lens, wl.q_per_seq, device=device)
 
 
 def device_inputs(wl, device="cuda"):

@@ -51,7 +51,8 @@ SIGNATURES = {
     "msa_indexer_scan": (ctypes.c_int, [_DESC, _P, _P, _P, _P, _I32, _P, _I32, _P, _I32, _I32,
                                         _P, _P]),
     "msa_indexer_scan_shared": (ctypes.c_int, [_DESC, _P, _P, _P, _P, _I32, _P, _I32, _P, _I32,
-                                               _I32, _I32, _P, _P, _P, _I32, _P, _P, _P]),
+                                               _I32, _I32, _P, _P, _I32, _P, _P, _P]),
+    "msa_shared_prefix_groups": (ctypes.c_int, [_P, _I32, _P, _I32, _I32, _P, _P, _P, _P, _P]),
     "msa_indexer_select": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _I32, _P, _P, _P]),
     "msa_attn_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
     "msa_sparse_attn_decode": (ctypes.c_int, [_DESC, _P, _P, _P, _P, _P, _I32, _P, _I32, _P,
@@ -334,33 +335,61 @@ def msa_indexer_scan(idx_codes, idx_scales, q_fp8, head_w, block_table, seq_lens
         _stream()), prepare, keep=(desc,))
 
 
+def msa_shared_prefix_groups(block_table, seq_lens, q_per_seq, device=None):
+    """Shared-prefix groups of a batch, derived by the library on the host
+    from a host copy of the block table int32 [B, max_blocks] and seq_lens
+    int32 [B] (torch CPU tensors). Returns (group_lead, group_blocks,
+    max_group_blocks, seq_group): int32 tensors (on `device` when given) and
+    a host int, msa_indexer_scan_shared's group arguments."""
+    for t, name in ((block_table, "block_table"), (seq_lens, "seq_lens")):
+        _need(t, name, torch.int32, device=False)
+        if t.device.type != "cpu":
+            raise ValueError(f"{name} must be a host (CPU) tensor")
+    if block_table.dim() != 2 or seq_lens.dim() != 1 or seq_lens.shape[0] != block_table.shape[0]:
+        raise ValueError("block_table must be [B, max_blocks] and seq_lens [B]")
+    num_seqs, max_blocks = block_table.shape
+    n = max(num_seqs, 1)
+    lead = torch.empty(n, dtype=torch.int32)
+    blocks = torch.empty(n, dtype=torch.int32)
+    group = torch.empty(n, dtype=torch.int32)
+    ng, mgb = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(lib().msa_shared_prefix_groups(
+        _ptr(block_table), max_blocks, _ptr(seq_lens), num_seqs, int(q_per_seq), _ptr(lead),
+        _ptr(blocks), _ptr(group), ctypes.byref(ng), ctypes.byref(mgb)), "msa_shared_prefix_groups")
+    out = (lead[:ng.value].clone(), blocks[:ng.value].clone(), group[:num_seqs].clone())
+    if device is not None:
+        out = tuple(t.to(device) for t in out)
+    return out[0], out[1], int(mgb.value), out[2]
+
+
 def msa_indexer_scan_shared(idx_codes, idx_scales, q_fp8, head_w, block_table, seq_lens, q_per_seq,
-                            group_start, group_seqs, group_blocks, max_group_blocks,
-                            seq_shared_blocks, block_scores, prepare=False):
-    """msa_indexer_scan with shared leading blocks read and dequantised once per
-    group: group_start int32 [G+1], group_seqs int32, group_blocks int32 [G],
-    seq_shared_blocks int32 [B] (device), max_group_blocks >= every
-    group_blocks entry (host int)."""
+                            group_lead, group_blocks, max_group_blocks, seq_group, block_scores,
+                            prepare=False):
+    """msa_indexer_scan with the blocks of shared prefixes read and
+    dequantised once per group, in the same launch: group_lead int32 [G],
+    group_blocks int32 [G], seq_group int32 [B] (device; from
+    msa_shared_prefix_groups), max_group_blocks >= every group_blocks entry
+    (host int)."""
     _check_pool(idx_codes, idx_scales, "idx")
     num_seqs, max_blocks, tq, hq = _check_indexer_inputs(q_fp8, head_w, block_table, seq_lens,
                                                          q_per_seq)
     _need(block_scores, "block_scores", torch.float32, 2)
     if block_scores.shape != (tq, max_blocks):
         raise ValueError("block_scores must be [T_q, max_blocks]")
-    for t, name in ((group_start, "group_start"), (group_seqs, "group_seqs"),
-                    (group_blocks, "group_blocks"), (seq_shared_blocks, "seq_shared_blocks")):
+    for t, name in ((group_lead, "group_lead"), (group_blocks, "group_blocks"),
+                    (seq_group, "seq_group")):
         _need(t, name, torch.int32, 1)
-    num_groups = group_start.shape[0] - 1
-    if num_groups < 0 or group_blocks.shape[0] != num_groups:
-        raise ValueError("group_start must be [G+1] and group_blocks [G]")
-    if seq_shared_blocks.shape[0] != num_seqs:
-        raise ValueError("seq_shared_blocks must be [num_seqs]")
+    num_groups = group_lead.shape[0]
+    if group_blocks.shape[0] != num_groups:
+        raise ValueError("group_lead and group_blocks must both be [G]")
+    if seq_group.shape[0] != num_seqs:
+        raise ValueError("seq_group must be [num_seqs]")
     desc = pool_desc(idx_codes)
     return _issue("msa_indexer_scan_shared", (
         ctypes.byref(desc), _ptr(idx_codes), _ptr(idx_scales), _ptr(q_fp8), _ptr(head_w), hq,
         _ptr(block_table), max_blocks, _ptr(seq_lens), num_seqs, q_per_seq, num_groups,
-        _ptr(group_start), _ptr(group_seqs), _ptr(group_blocks), int(max_group_blocks),
-        _ptr(seq_shared_blocks), _ptr(block_scores), _stream()), prepare, keep=(desc,))
+        _ptr(group_lead), _ptr(group_blocks), int(max_group_blocks), _ptr(seq_group),
+        _ptr(block_scores), _stream()), prepare, keep=(desc,))
 
 
 def msa_indexer_select(block_scores, seq_lens, q_per_seq, out_ids, out_scores=None, topk=TOPK,

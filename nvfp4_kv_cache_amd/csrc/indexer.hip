@@ -22,7 +22,10 @@
 // and maximised over the block's visible tokens, giving one fp32 block score
 // per (query token, block). The selection kernel then picks, per query
 // token, the top-16 blocks plus the most recent one.
+#include <algorithm>
 #include <atomic>
+#include <unordered_map>
+#include <vector>
 
 #include "msa_nvfp4.h"
 #include "nvfp4_tile.h"
@@ -35,66 +38,31 @@ static_assert(kTopK == MSA_TOPK, "selection size");
 
 __constant__ Fp8Lut kIdxLut = make_fp8_lut();
 
-// QG: 16-row MFMA groups per index head = ceil(8 * q_per_seq / 16).
-// One block in flight per wave: the next block's loads are issued as soon as
-// the current block's codes are consumed, and more resident waves hide the
-// latency better than a second register buffer would (measured with 1 and 8
-// query tokens).
-template <int QG>
-__global__ __launch_bounds__(512) void indexer_kernel(const IndexerArgs a) {
-  extern __shared__ float part[];  // [2][H][2*QG][128] partial token scores per index head
-  __shared__ uint2 lut[128];
-  __shared__ int pages[kMaxBlocksPerWg];
-  scan_workgroup<QG, false>(a, blockIdx.x, gridDim.x, blockIdx.y, kIdxLut, part, lut, pages);
-}
-
-// Shared pass for sequences that share leading blocks (the same physical
-// pages at the same logical blocks): workgroup (j, g, c) reads block j of
-// group g, one wavefront per index head, dequantises its 8 tiles into
-// registers and scores them against query tokens 8c .. 8c + 7 of the group's
-// members (64 MFMA rows: token 8c + R/8, head R%8); the chunks of a block run
-// side by side and share its read through L2, so a block is dequantised once
-// per 8 member tokens instead of once per member. The
-// arithmetic per token is the regular scan's, in the same order (the same
-// MFMA operands, the ReLU-weighted sum of a lane's 4 heads, the head-pair
-// exchange, the sum over index heads in head order, the maxima), so the
-// block scores are the same values the regular scan writes.
-struct SharedScanArgs {
-  IndexerArgs a;
-  const int32_t* group_start;   // [num_groups + 1]
-  const int32_t* group_seqs;    // member sequence ids
-  const int32_t* group_blocks;  // [num_groups] shared leading blocks
-  int num_seqs;
-};
-
-__global__ __launch_bounds__(512) void shared_scan_kernel(const SharedScanArgs sa) {
-  constexpr int QG = 4;      // 16-row groups per chunk
-  constexpr int kChunk = 8;  // query tokens per chunk
-  __shared__ float part[MSA_MAX_HEADS][kChunk][kBlockTokens];  // partial token scores
-  __shared__ uint2 lut[128];
-  __shared__ int tok_row[kChunk], tok_pos[kChunk];  // query row b*Q + qi, position (-1: none)
-  const IndexerArgs& a = sa.a;
+// One shared-prefix workgroup: block j of group g, one wavefront per index
+// head. The block (the group lead's page) is read once and dequantised once
+// into registers, then scored against the query tokens of every sequence of
+// the group whose block j maps to the same page, two tokens at a time (16
+// MFMA rows: token R/8, head R%8 of the wave's 8). The arithmetic per token
+// is the regular scan's, in the same order (the same MFMA operands, the
+// ReLU-weighted sum of a lane's 4 heads, the head-pair exchange, the sum over
+// index heads in head order, the maximum over the visible tokens), so the
+// block scores are the values the regular scan would write. LDS from the
+// caller: part = [2][H][2][128] floats, lut = 128 table rows.
+__device__ __forceinline__ void shared_workgroup(const IndexerArgs& a, int j, int g, float* part,
+                                                 uint2* lut) {
+  __shared__ int memb[65];  // member sequences of the current chunk of 64, then their count
   const int H = a.num_heads;
   const int Q = a.q_per_seq;
   const int Hq = a.num_q_heads;
-  // ids through the builtins: this file is built without IEEE NaN handling,
-  // so the device library's id functions are not inlined here, and a called
-  // one returns its value in a register the compiler cannot treat as uniform
-  // (each buffer load then needed a loop over the descriptor's values)
   const int tid = int(__builtin_amdgcn_workitem_id_x());
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int slice = lane >> 4;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int j = int(__builtin_amdgcn_workgroup_id_x()), g = int(__builtin_amdgcn_workgroup_id_y());
-  const int c0 = kChunk * int(__builtin_amdgcn_workgroup_id_z());
   // uniform over the workgroup: nothing to do past the group's shared blocks
-  // or past its member tokens
-  if (j >= min(sa.group_blocks[g], a.max_blocks)) return;
-  const int m0 = sa.group_start[g], m1 = sa.group_start[g + 1];
-  if (m1 <= m0 || c0 >= (m1 - m0) * Q) return;
-  const int lead = sa.group_seqs[m0];
-  if (lead < 0 || lead >= sa.num_seqs) return;
+  if (g >= a.num_groups || j >= min(a.group_blocks[g], a.max_blocks)) return;
+  const int lead = a.group_lead[g];
+  if (lead < 0 || lead >= a.num_seqs) return;
 
   for (int i = tid; i < 128; i += 64 * H) lut[i] = make_uint2(kIdxLut.lo[i], kIdxLut.hi[i]);
   const int p = a.block_table[int64_t(lead) * a.max_blocks + j];
@@ -103,90 +71,129 @@ __global__ __launch_bounds__(512) void shared_scan_kernel(const SharedScanArgs s
   issue_loads(t, a.codes + int64_t(wave_u) * kCodePage, a.scales + int64_t(wave_u) * kScalePage,
               p, page_ok, int64_t(H) * kCodePage, int64_t(H) * kScalePage,
               (lane & 15) * kCodeRow + slice * 16, scale_word_offset(slice, lane & 15));
-  // this chunk's member tokens (token k of the group: sequence
-  // group_seqs[m0 + k / Q], query token k % Q), looked up once while the
-  // block's loads are in flight
-  const int T = (m1 - m0) * Q;
-  if (tid < kChunk) {
-    const int k = c0 + tid;
-    int row = 0, pos = -1;
-    if (k < T) {
-      const int m = k / Q, qi = k - m * Q;
-      const int bb = sa.group_seqs[m0 + m];
-      if (bb >= 0 && bb < sa.num_seqs) {
-        const int L = a.seq_lens[bb];
-        row = bb * Q + qi;
-        if (L >= Q && L <= a.max_blocks * kBlockTokens) pos = L - Q + qi;
-      }
-    }
-    tok_row[tid] = row;
-    tok_pos[tid] = pos;
-  }
-  __syncthreads();  // the lookup table and the token list
+  __syncthreads();  // the lookup table
   v8i kop[8];
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) {
     const uint32_t sj = tile_scales(t.s, jj);
     kop[jj] = dequant32(t.c[jj], lut[sj & 0x7F], lut[(sj >> 8) & 0x7F]);
   }
-
   const int part_lane = (lane >> 5) * kBlockTokens + (lane & 31);
-  // query operands and weights of tokens c0 .. c0 + 7
-  v8i qop[QG];
-  float wv[QG][4];
-#pragma unroll
-  for (int rg = 0; rg < QG; ++rg) {
-    const int R = 16 * rg + (lane & 15);
-    qop[rg] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-    if (tok_pos[R >> 3] >= 0) {
-      const uint4* qp = reinterpret_cast<const uint4*>(
-          a.q + (int64_t(tok_row[R >> 3]) * Hq + wave * kHeadsPerKv + (R & 7)) * kHeadDim +
-          slice * 32);
-      qop[rg] = q_operand(qp[0], qp[1]);
+  const int part_stride = H * 2 * kBlockTokens;
+  int u_all = 0;  // token pairs processed so far (partial buffer parity)
+  for (int c0 = 0; c0 < a.num_seqs; c0 += 64) {
+    if (c0 > 0) __syncthreads();  // the previous chunk's last reduction has read memb
+    // this chunk's members: the sequences of group g whose block j is the
+    // lead's page and whose length is valid; each lane of wave 0 tests one
+    if (wave_u == 0) {
+      const int bb = c0 + lane;
+      bool m = false;
+      if (bb < a.num_seqs && a.seq_group[bb] == g) {
+        const int L = a.seq_lens[bb];
+        m = L >= Q && L <= a.max_blocks * kBlockTokens &&
+            a.block_table[int64_t(bb) * a.max_blocks + j] == p;
+      }
+      const uint64_t mask = __ballot(m);
+      if (m) memb[__popcll(mask & ((uint64_t(1) << lane) - 1))] = bb;
+      if (lane == 0) memb[64] = __popcll(mask);
     }
+    __syncthreads();  // memb
+    const int T = __builtin_amdgcn_readfirstlane(memb[64]) * Q;  // member query tokens
+    for (int u = 0; 2 * u < T; ++u, ++u_all) {
+      const int buf = u_all & 1;
+      // operands of tokens 2u, 2u + 1: row R of a 16-row group is token
+      // 2u + R/8, head R%8 of this wave's index head
+      v8i qop = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+      float wv[4];
+      {
+        const int R = lane & 15;
+        const int tk = 2 * u + (R >> 3);
+        if (tk < T) {
+          const int bb = memb[tk / Q];
+          const int row = bb * Q + tk % Q;
+          const uint4* qp = reinterpret_cast<const uint4*>(
+              a.q + (int64_t(row) * Hq + wave * kHeadsPerKv + (R & 7)) * kHeadDim + slice * 32);
+          qop = q_operand(qp[0], qp[1]);
+        }
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int R2 = 16 * rg + 4 * slice + v;
-      wv[rg][v] = tok_pos[R2 >> 3] >= 0
-                      ? a.w[int64_t(tok_row[R2 >> 3]) * Hq + wave * kHeadsPerKv + (R2 & 7)]
-                      : 0.0f;
-    }
-  }
-  // ReLU-weighted head sums per token, head pairs combined, to LDS
-  float* pw = &part[wave][0][0] + part_lane;
+        for (int v = 0; v < 4; ++v) {
+          const int R2 = 4 * slice + v;
+          const int tk2 = 2 * u + (R2 >> 3);
+          wv[v] = 0.0f;
+          if (tk2 < T) {
+            const int bb = memb[tk2 / Q];
+            wv[v] = a.w[(int64_t(bb) * Q + tk2 % Q) * Hq + wave * kHeadsPerKv + (R2 & 7)];
+          }
+        }
+      }
+      // ReLU-weighted head sums per token, head pairs combined, to LDS
+      float* pw = part + buf * part_stride + wave * 2 * kBlockTokens + part_lane;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float s2[2][QG];
+      for (int i = 0; i < 4; ++i) {
+        float s2[2];
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-#pragma unroll
-      for (int rg = 0; rg < QG; ++rg) {
-        const v4f acc = mfma_fp8_16x16x128(qop[rg], kop[2 * i + e], v4f{0.0f, 0.0f, 0.0f, 0.0f});
-        float s = wv[rg][0] * fmaxf(acc[0], 0.0f);
-        s += wv[rg][1] * fmaxf(acc[1], 0.0f);
-        s += wv[rg][2] * fmaxf(acc[2], 0.0f);
-        s += wv[rg][3] * fmaxf(acc[3], 0.0f);
-        s2[e][rg] = s;
+        for (int e = 0; e < 2; ++e) {
+          const v4f acc = mfma_fp8_16x16x128(qop, kop[2 * i + e], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+          float sc = wv[0] * fmaxf(acc[0], 0.0f);
+          sc += wv[1] * fmaxf(acc[1], 0.0f);
+          sc += wv[2] * fmaxf(acc[2], 0.0f);
+          sc += wv[3] * fmaxf(acc[3], 0.0f);
+          s2[e] = sc;
+        }
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(s2[0]),
+                                                         __float_as_uint(s2[1]), false, false);
+        pw[32 * i] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      }
+      __syncthreads();
+      // sum over index heads and maximum over the visible tokens of the
+      // pair, by one wavefront
+      if (wave_u == u_all % H) {
+        const int tk = 2 * u + (lane >> 5);
+        int lim = -1;
+        int row = 0;
+        if (tk < T) {
+          const int bb = memb[tk / Q];
+          const int L = a.seq_lens[bb];
+          row = bb * Q + tk % Q;
+          lim = L - Q + tk % Q - j * kBlockTokens;
+        }
+        const float2 mx = row_pair_max(part + buf * part_stride, 2 * kBlockTokens, H, 0, lim, lane);
+        const int rl = __shfl(row, lane * 32, 64);   // lane 0: row of token 2u, lane 1: 2u + 1
+        const int ll = __shfl(lim, lane * 32, 64);
+        if (lane < 2 && 2 * u + lane < T && ll >= 0)
+          a.bscore[int64_t(rl) * a.max_blocks + j] = page_ok ? (lane ? mx.y : mx.x) : 0.0f;
       }
     }
-#pragma unroll
-    for (int rg = 0; rg < QG; ++rg) {
-      const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(s2[0][rg]),
-                                                       __float_as_uint(s2[1][rg]), false, false);
-      pw[2 * rg * kBlockTokens + 32 * i] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
+}
+
+// QG: 16-row MFMA groups per index head = ceil(8 * q_per_seq / 16).
+// Grid (G, shared_rows + num_seqs): the first shared_rows rows are the
+// shared-prefix workgroups (row-major over (group, block)), dispatched first
+// so that they run beside the regular scan; row shared_rows + b holds the G
+// scan workgroups of sequence b.
+// One block in flight per wave: the next block's loads are issued as soon as
+// the current block's codes are consumed, and more resident waves hide the
+// latency better than a second register buffer would (measured with 1 and 8
+// query tokens).
+// SHARED: the launch holds shared-prefix workgroups (msa_indexer_scan_shared);
+// their role is compiled only into this form, whose register allocation it
+// raises (112 VGPRs against 84 for the plain scan with one query token).
+template <int QG, bool SHARED>
+__global__ __launch_bounds__(512) void indexer_kernel(const IndexerArgs a) {
+  extern __shared__ float part[];  // [2][H][2*QG][128] partial token scores per index head
+  __shared__ uint2 lut[128];
+  __shared__ ScanList list;
+  int y = blockIdx.y;
+  if constexpr (SHARED) {
+    if (y < a.shared_rows) {
+      const int u = y * int(gridDim.x) + int(blockIdx.x);
+      shared_workgroup(a, u % a.max_group_blocks, u / a.max_group_blocks, part, lut);
+      return;
     }
+    y -= a.shared_rows;
   }
-  __syncthreads();
-  // sum over index heads and maximum over the visible tokens, one token
-  // pair per wavefront
-  for (int u = wave_u; u < kChunk / 2; u += H) {
-    const int tq = 2 * u + (lane >> 5);
-    const float2 mx = row_pair_max(&part[0][0][0], kChunk * kBlockTokens, H, 2 * u,
-                                   tok_pos[tq] - j * kBlockTokens, lane);
-    const int q = 2 * u + lane;
-    if (lane < 2 && j * kBlockTokens <= tok_pos[q])
-      a.bscore[int64_t(tok_row[q]) * a.max_blocks + j] = page_ok ? (lane ? mx.y : mx.x) : 0.0f;
-  }
+  scan_workgroup<QG, false>(a, blockIdx.x, gridDim.x, y, kIdxLut, part, lut, list);
 }
 
 // Selection kernel: one wavefront per query token (topk_select.h).
@@ -196,7 +203,10 @@ __global__ __launch_bounds__(64) void select_kernel(const float* __restrict__ bs
                                                     int32_t* __restrict__ out_ids,
                                                     float* __restrict__ out_scores) {
   __shared__ SelectScratch scratch;
-  // ids through the builtins, as in shared_scan_kernel
+  // ids through the builtins: this file is built without IEEE NaN handling,
+  // so the device library's id functions are not inlined here, and a called
+  // one returns its value in a register the compiler cannot treat as uniform
+  // (each buffer load then needed a loop over the descriptor's values)
   const int row = int(__builtin_amdgcn_workgroup_id_x());
   const int lane = int(__builtin_amdgcn_workitem_id_x());
   const float* src = bscore + int64_t(row) * max_blocks;
@@ -240,14 +250,22 @@ static bool misaligned(const void* p, uintptr_t m) { return (reinterpret_cast<ui
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Shared-prefix groups of a scan (device arrays), or none.
+struct SharedGroups {
+  const int32_t* seq_group = nullptr;
+  const int32_t* group_lead = nullptr;
+  const int32_t* group_blocks = nullptr;
+  int num_groups = 0;
+  int max_group_blocks = 0;
+};
+
 static msa_status launch_scan(const msa_pool_desc* idx, const uint8_t* idx_codes,
                               const uint8_t* idx_scales, const uint8_t* q_fp8, const float* head_w,
                               int32_t num_q_heads, const int32_t* block_table, int32_t max_blocks,
                               const int32_t* seq_lens, int32_t num_seqs, int32_t q_per_seq,
                               float* block_scores, hipStream_t s,
-                              const int32_t* seq_skip = nullptr, IndexerArgs* args_out = nullptr) {
+                              const SharedGroups& sg = SharedGroups()) {
   IndexerArgs a;
-  a.seq_skip = seq_skip;
   a.codes = idx_codes;
   a.scales = idx_scales;
   a.num_pages = idx->num_pages;
@@ -260,20 +278,40 @@ static msa_status launch_scan(const msa_pool_desc* idx, const uint8_t* idx_codes
   a.seq_lens = seq_lens;
   a.q_per_seq = q_per_seq;
   a.bscore = block_scores;
+  a.num_seqs = num_seqs;
+  const bool shared = sg.num_groups > 0;
+  a.seq_group = shared ? sg.seq_group : nullptr;
+  a.group_lead = sg.group_lead;
+  a.group_blocks = sg.group_blocks;
+  a.num_groups = shared ? sg.num_groups : 0;
+  a.max_group_blocks = shared ? sg.max_group_blocks : 1;
   const int qg = (MSA_HEADS_PER_KV * q_per_seq + 15) / 16;
   const int bpw = scan_blocks_per_wg(num_seqs, max_blocks, qg);
   a.blocks_per_wg = bpw;
-  const dim3 grid((max_blocks + bpw - 1) / bpw, num_seqs);
+  const int gx = (max_blocks + bpw - 1) / bpw;
+  // the shared-prefix workgroups fill whole leading rows of the grid
+  const int64_t shared_wgs = int64_t(a.num_groups) * a.max_group_blocks;
+  a.shared_rows = int((shared_wgs + gx - 1) / gx);
+  if (int64_t(num_seqs) + a.shared_rows > 65535) return MSA_ERR_UNSUPPORTED;
+  const dim3 grid(gx, num_seqs + a.shared_rows);
   const dim3 block(64 * idx->num_heads);
-  if (args_out) *args_out = a;
   const int qg_pow2 = qg == 1 ? 1 : (qg == 2 ? 2 : 4);
   const size_t lds = size_t(2) * idx->num_heads * (2 * qg_pow2) * MSA_BLOCK_TOKENS * sizeof(float);
-  if (qg_pow2 == 1)
-    hipLaunchKernelGGL((indexer_kernel<1>), grid, block, lds, s, a);
-  else if (qg_pow2 == 2)
-    hipLaunchKernelGGL((indexer_kernel<2>), grid, block, lds, s, a);
-  else
-    hipLaunchKernelGGL((indexer_kernel<4>), grid, block, lds, s, a);
+  if (shared) {
+    if (qg_pow2 == 1)
+      hipLaunchKernelGGL((indexer_kernel<1, true>), grid, block, lds, s, a);
+    else if (qg_pow2 == 2)
+      hipLaunchKernelGGL((indexer_kernel<2, true>), grid, block, lds, s, a);
+    else
+      hipLaunchKernelGGL((indexer_kernel<4, true>), grid, block, lds, s, a);
+  } else {
+    if (qg_pow2 == 1)
+      hipLaunchKernelGGL((indexer_kernel<1, false>), grid, block, lds, s, a);
+    else if (qg_pow2 == 2)
+      hipLaunchKernelGGL((indexer_kernel<2, false>), grid, block, lds, s, a);
+    else
+      hipLaunchKernelGGL((indexer_kernel<4, false>), grid, block, lds, s, a);
+  }
   return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
 }
 
@@ -318,9 +356,8 @@ extern "C" msa_status msa_indexer_scan_shared(
     const msa_pool_desc* idx, const uint8_t* idx_codes, const uint8_t* idx_scales,
     const uint8_t* q_fp8, const float* head_w, int32_t num_q_heads, const int32_t* block_table,
     int32_t max_blocks, const int32_t* seq_lens, int32_t num_seqs, int32_t q_per_seq,
-    int32_t num_groups, const int32_t* group_start, const int32_t* group_seqs,
-    const int32_t* group_blocks, int32_t max_group_blocks, const int32_t* seq_shared_blocks,
-    float* block_scores, void* stream) {
+    int32_t num_groups, const int32_t* group_lead, const int32_t* group_blocks,
+    int32_t max_group_blocks, const int32_t* seq_group, float* block_scores, void* stream) {
   using namespace msa;
   if (!idx) return MSA_ERR_INVALID_ARG;
   msa_status st = check_indexer_shape(num_seqs, q_per_seq, max_blocks);
@@ -336,29 +373,81 @@ extern "C" msa_status msa_indexer_scan_shared(
   if (num_seqs == 0) return MSA_OK;
   if (!idx_codes || !idx_scales || !q_fp8 || !head_w || !block_table || !seq_lens || !block_scores)
     return MSA_ERR_INVALID_ARG;
-  if (num_groups > 0 && (!group_start || !group_seqs || !group_blocks || !seq_shared_blocks))
-    return MSA_ERR_INVALID_ARG;
+  if (num_groups > 0 && (!group_lead || !group_blocks || !seq_group)) return MSA_ERR_INVALID_ARG;
   if (misaligned(idx_codes, 15) || misaligned(idx_scales, 15) || misaligned(q_fp8, 15) ||
       misaligned(head_w, 3) || misaligned(block_table, 3) || misaligned(seq_lens, 3) ||
-      misaligned(block_scores, 3) || misaligned(group_start, 3) || misaligned(group_seqs, 3) ||
-      misaligned(group_blocks, 3) || misaligned(seq_shared_blocks, 3))
+      misaligned(block_scores, 3) || misaligned(group_lead, 3) || misaligned(group_blocks, 3) ||
+      misaligned(seq_group, 3))
     return MSA_ERR_INVALID_ARG;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  SharedScanArgs sa;
-  st = launch_scan(idx, idx_codes, idx_scales, q_fp8, head_w, num_q_heads, block_table, max_blocks,
-                   seq_lens, num_seqs, q_per_seq, block_scores, s,
-                   num_groups > 0 ? seq_shared_blocks : nullptr, &sa.a);
-  if (st != MSA_OK || num_groups == 0) return st;
-  sa.group_start = group_start;
-  sa.group_seqs = group_seqs;
-  sa.group_blocks = group_blocks;
-  sa.num_seqs = num_seqs;
-  // z: chunks of 8 member tokens (a group has at most num_seqs members)
-  const int64_t chunks = (int64_t(num_seqs) * q_per_seq + 7) / 8;
-  hipLaunchKernelGGL(shared_scan_kernel,
-                     dim3(unsigned(max_group_blocks), unsigned(num_groups), unsigned(chunks)),
-                     dim3(64 * idx->num_heads), 0, s, sa);
-  return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
+  SharedGroups sg;
+  sg.seq_group = seq_group;
+  sg.group_lead = group_lead;
+  sg.group_blocks = group_blocks;
+  sg.num_groups = num_groups;
+  sg.max_group_blocks = max_group_blocks;
+  return launch_scan(idx, idx_codes, idx_scales, q_fp8, head_w, num_q_heads, block_table, max_blocks,
+                     seq_lens, num_seqs, q_per_seq, block_scores,
+                     static_cast<hipStream_t>(stream), sg);
+}
+
+extern "C" msa_status msa_shared_prefix_groups(const int32_t* block_table, int32_t max_blocks,
+                                               const int32_t* seq_lens, int32_t num_seqs,
+                                               int32_t q_per_seq, int32_t* group_lead,
+                                               int32_t* group_blocks, int32_t* seq_group,
+                                               int32_t* num_groups, int32_t* max_group_blocks) {
+  if (num_seqs < 0 || max_blocks <= 0 || q_per_seq <= 0) return MSA_ERR_INVALID_ARG;
+  if (!num_groups || !max_group_blocks) return MSA_ERR_INVALID_ARG;
+  *num_groups = 0;
+  *max_group_blocks = 0;
+  if (num_seqs == 0) return MSA_OK;
+  if (!block_table || !seq_lens || !group_lead || !group_blocks || !seq_group)
+    return MSA_ERR_INVALID_ARG;
+  // candidate groups: sequences with a valid length keyed by their first
+  // page (pages < 0 map nothing), in the order of their first member
+  std::unordered_map<int32_t, int32_t> by_first;
+  std::vector<std::vector<int32_t>> members;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    seq_group[b] = -1;
+    const int32_t L = seq_lens[b];
+    if (L < q_per_seq || int64_t(L) > int64_t(max_blocks) * MSA_BLOCK_TOKENS) continue;
+    const int32_t p0 = block_table[int64_t(b) * max_blocks];
+    if (p0 < 0) continue;
+    auto it = by_first.find(p0);
+    if (it == by_first.end()) {
+      by_first.emplace(p0, int32_t(members.size()));
+      members.push_back({b});
+    } else {
+      members[it->second].push_back(b);
+    }
+  }
+  // a group of two or more shares the longest run of leading blocks whose
+  // pages are the same (and mapped) in every member, within every member's
+  // own blocks; the lead is its first member
+  int32_t ng = 0, mgb = 0;
+  for (const auto& m : members) {
+    if (m.size() < 2) continue;
+    const int32_t lead = m[0];
+    const int32_t* lt = block_table + int64_t(lead) * max_blocks;
+    int32_t n = max_blocks;
+    for (int32_t b : m) n = std::min(n, (seq_lens[b] + MSA_BLOCK_TOKENS - 1) / MSA_BLOCK_TOKENS);
+    int32_t run = 0;
+    while (run < n && lt[run] >= 0) ++run;
+    for (size_t i = 1; i < m.size() && run > 0; ++i) {
+      const int32_t* bt = block_table + int64_t(m[i]) * max_blocks;
+      int32_t k = 0;
+      while (k < run && bt[k] == lt[k]) ++k;
+      run = k;
+    }
+    if (run == 0) continue;
+    group_lead[ng] = lead;
+    group_blocks[ng] = run;
+    for (int32_t b : m) seq_group[b] = ng;
+    mgb = std::max(mgb, run);
+    ++ng;
+  }
+  *num_groups = ng;
+  *max_group_blocks = mgb;
+  return MSA_OK;
 }
 
 extern "C" msa_status msa_indexer_select(const float* block_scores, const int32_t* seq_lens,

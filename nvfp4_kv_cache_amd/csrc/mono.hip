@@ -199,11 +199,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
   const int id = blockIdx.x;
   if (id < m.n_scan) {
     __shared__ uint2 lut[128];
-    __shared__ int pages[kMaxBlocksPerWg];
+    __shared__ ScanList list;
     const int b = id / m.scan_per_seq;
     const int x = id - b * m.scan_per_seq;
     scan_workgroup<QG, true>(m.s, x, m.scan_per_seq, b, kMonoLut, reinterpret_cast<float*>(smem),
-                             lut, pages);
+                             lut, list);
     arrive(m.scan_cnt + int64_t(b) * kCountWords, x);
   } else if (id < m.n_scan + m.n_block) {
     const int u = id - m.n_scan;
@@ -309,7 +309,11 @@ extern "C" msa_status msa_decode_mono(
   s.seq_lens = seq_lens;
   s.q_per_seq = q_per_seq;
   s.bscore = reinterpret_cast<float*>(ws + lay.scores);
-  s.seq_skip = nullptr;
+  s.num_seqs = num_seqs;
+  s.seq_group = nullptr;
+  s.num_groups = 0;
+  s.max_group_blocks = 1;
+  s.shared_rows = 0;
   // blocks per scan workgroup: the standalone scan's rule
   const int qg = (MSA_HEADS_PER_KV * q_per_seq + 15) / 16;
   const int bpw = scan_blocks_per_wg(num_seqs, max_blocks, qg);

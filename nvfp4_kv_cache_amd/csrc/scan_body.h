@@ -28,10 +28,40 @@ struct IndexerArgs {
   int q_per_seq;
   int blocks_per_wg;
   float* bscore;       // [num_seqs * q_per_seq][max_blocks]
-  const int32_t* seq_skip;  // [num_seqs] leading blocks scored by the shared pass, or null
+  int num_seqs;
+  // shared prefixes (seq_group null: none). Block j of sequence b belongs to
+  // the shared pass, and not to the regular scan, when g = seq_group[b] is a
+  // group (0 <= g < num_groups), j < min(group_blocks[g], max_blocks), the
+  // lead l = group_lead[g] is a sequence of the batch, and block_table[b][j]
+  // equals block_table[l][j]: the same page, read and dequantised once for
+  // every sequence of the group
+  const int32_t* seq_group;     // [num_seqs] group of each sequence, -1: none
+  const int32_t* group_lead;    // [num_groups] sequence whose pages define the group
+  const int32_t* group_blocks;  // [num_groups] leading blocks the group shares
+  int num_groups;
+  int max_group_blocks;         // >= every group_blocks entry, <= max_blocks
+  int shared_rows;              // leading grid rows of shared-prefix workgroups
 };
 
 constexpr int kMaxBlocksPerWg = 8;  // blocks per scan workgroup (page list size)
+
+// The blocks a scan workgroup scores: physical page (-1: outside the pool),
+// logical block, and how many.
+struct ScanList {
+  int page[kMaxBlocksPerWg];
+  int blk[kMaxBlocksPerWg];
+  int count;
+};
+
+// The lead sequence of the shared prefix that covers block j of sequence b
+// (the shared pass scores that block when b's page equals the lead's), or -1.
+__device__ __forceinline__ int shared_lead(const IndexerArgs& a, int b, int j) {
+  if (!a.seq_group) return -1;
+  const int g = a.seq_group[b];
+  if (g < 0 || g >= a.num_groups || j >= min(a.group_blocks[g], a.max_blocks)) return -1;
+  const int lead = a.group_lead[g];
+  return (lead >= 0 && lead < a.num_seqs) ? lead : -1;
+}
 
 // One block's worth of this wave's loads: 8 tiles x 16 code bytes and the
 // 16-byte scale word (2 scale bytes per tile) per lane.
@@ -127,13 +157,12 @@ inline int scan_blocks_per_wg(int64_t num_seqs, int64_t max_blocks, int qg) {
 
 // Workgroup x of the G scan workgroups of sequence b, one wavefront per
 // index-key head. LDS from the caller: part = [2][H][2*QG][128] floats,
-// lut = 128 table rows, pages = kMaxBlocksPerWg entries. COHERENT: the block
-// scores are stored at device scope (write-through), for a consumer in the
-// same launch.
+// lut = 128 table rows, the block list. COHERENT: the block scores are
+// stored at device scope (write-through), for a consumer in the same launch.
 template <int QG, bool COHERENT>
 __device__ __forceinline__ void scan_workgroup(const IndexerArgs& a, int x, int G, int b,
                                                const Fp8Lut& lut_src, float* part, uint2* lut,
-                                               int* pages) {
+                                               ScanList& list) {
 
   const int H = a.num_heads;
   const int Q = a.q_per_seq;
@@ -149,17 +178,28 @@ __device__ __forceinline__ void scan_workgroup(const IndexerArgs& a, int x, int 
   const int nb_last = seq_ok ? (L - 1) / kBlockTokens + 1 : 0;
   // workgroup x of a sequence takes blocks x, x + G, x + 2G, ... (G = grid
   // width), so the workgroups running at any moment read neighbouring pages;
-  // blocks below the sequence's shared prefix are left to the shared pass
+  // a block of a shared prefix whose page is the group lead's is left to the
+  // shared pass. Wave 0 builds the list (at most 8 blocks, one lane each).
   const int total = nb_last > x ? min(a.blocks_per_wg, (nb_last - x + G - 1) / G) : 0;
-  const int skip = a.seq_skip ? a.seq_skip[b] : 0;
-  const int k0 = x < skip ? min(total, (skip - x + G - 1) / G) : 0;
-  const int first = x + k0 * G;
-  const int count = total - k0;
   const int64_t qrow0 = int64_t(b) * Q;
   const int Hq = a.num_q_heads;
-  if (int(threadIdx.x) < count) {
-    const int p = a.block_table[int64_t(b) * a.max_blocks + first + threadIdx.x * G];
-    pages[threadIdx.x] = (p >= 0 && p < a.num_pages) ? p : -1;
+  if (threadIdx.x < 64) {
+    const int t = threadIdx.x;
+    const int j = x + t * G;
+    bool keep = t < total;
+    int p = -1;
+    if (keep) {
+      p = a.block_table[int64_t(b) * a.max_blocks + j];
+      const int lead = shared_lead(a, b, j);
+      if (lead >= 0 && a.block_table[int64_t(lead) * a.max_blocks + j] == p) keep = false;
+    }
+    const uint64_t m = __ballot(keep);
+    if (keep) {
+      const int pos = __popcll(m & ((uint64_t(1) << t) - 1));
+      list.page[pos] = (p >= 0 && p < a.num_pages) ? p : -1;
+      list.blk[pos] = j;
+    }
+    if (t == 0) list.count = __popcll(m);
   }
 
   // Query operands (rows: query token R/8, head wave*8 + R%8) and weights.
@@ -193,9 +233,9 @@ __device__ __forceinline__ void scan_workgroup(const IndexerArgs& a, int x, int 
   const uint8_t* scales_w = a.scales + int64_t(wave_u) * kScalePage;
   const uint32_t code_lane = (lane & 15) * kCodeRow + slice * 16;
   const uint32_t scale_lane = scale_word_offset(slice, lane & 15);
-  const int count_u = __builtin_amdgcn_readfirstlane(count);
+  const int count_u = __builtin_amdgcn_readfirstlane(list.count);
   auto issue = [&](TileLoads& t, int k) {
-    const int page = __builtin_amdgcn_readfirstlane(pages[min(k, kMaxBlocksPerWg - 1)]);
+    const int page = __builtin_amdgcn_readfirstlane(list.page[min(k, kMaxBlocksPerWg - 1)]);
     issue_loads(t, codes_w, scales_w, page, k < count_u && page >= 0, page_codes, page_scales,
                 code_lane, scale_lane);
   };
@@ -244,8 +284,8 @@ __device__ __forceinline__ void scan_workgroup(const IndexerArgs& a, int x, int 
   // w + H, ...).
   const int pairs = (Q + 1) >> 1;
   auto reduce_part = [&](int k, int buf) {
-    const int blk = first + k * G;
-    const bool page_ok = pages[k] >= 0;
+    const int blk = list.blk[k];
+    const bool page_ok = list.page[k] >= 0;
     for (int u = wave_u; u < pairs; u += H) {
       const int qi = 2 * u + (lane >> 5);
       const int lim = qi < Q ? L - Q + qi - blk * kBlockTokens : -1;

@@ -50,8 +50,8 @@ def run_step(nb, wl, pools, inp, ws_idx=None, ws_attn=None, out=None, fused=True
     scale = 1.0 / math.sqrt(128)
     if fused:
         bscores = ws_idx[: tq * wl.max_blocks * 4].view(torch.float32).view(tq, wl.max_blocks)
-        groups = shared_groups(wl, device=dev)
-        if groups[3] > 0:
+        groups = shared_groups(wl, nb, device=dev)
+        if groups[2] > 0:
             nb.msa_indexer_scan_shared(ic, isc, inp["q_idx"], inp["w"], inp["block_table"],
                                        inp["seq_lens"], wl.q_per_seq, *groups, bscores)
         else:

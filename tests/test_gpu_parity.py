@@ -529,43 +529,60 @@ def test_workload_parity(nb, ci):
 
 
 # Shared-prefix scan: groups of sequences whose leading blocks map to the
-# same pages are scored with one read and dequantisation per shared block;
-# the block scores must be the plain scan's, bit for bit, and the decode on
-# them must pass the oracle. Cases: a member whose last shared block is only
-# partly visible (L = 130, Q = 2), two groups plus an ungrouped sequence,
-# nine members with Q = 1 (two 8-token chunks), three members with Q = 8.
+# same pages (derived by the library from the block table) are scored with
+# one read and one dequantisation per shared block, in the scan's own
+# launch; the block scores must be the plain scan's, bit for bit, and the
+# decode on them must pass the oracle. Cases: a member whose last shared
+# block is only partly visible (L = 130, Q = 2), two groups plus an
+# ungrouped sequence, nine members with Q = 1, three members with Q = 8,
+# and 70 members (two chunks of 64 sequences in a shared workgroup).
 SHARED = [
     ([1000, 700, 3000, 130, 2600, 900], 2, [([0, 1, 3], 6), ([2, 4], 20)]),
     ([2300] * 9 + [500], 1, [(list(range(9)), 17)]),
     ([4100, 4000, 3000], 8, [([0, 1, 2], 23)]),
+    ([700 + 13 * i for i in range(70)], 1, [(list(range(70)), 5)]),
 ]
 
 
-@pytest.mark.parametrize("lens,q,shared", SHARED)
-def test_shared_prefix_scan(nb, lens, q, shared):
-    from msa_workloads.device import shared_groups
-    say(f"shared prefix scan lens={lens} q={q} shared={shared}")
-    wl = tiny_config(lens, q, seed=70 + q, shared=shared)
-    pools = S.fill_pools(wl, nb)
-    inp = S.device_inputs(wl)
-    groups = shared_groups(wl)
-    assert groups[3] > 0
+def _plain_and_shared(nb, wl, inp, pools, groups):
     ic, isc = pools[synth.STREAM_IDX]
     tq = wl.num_q_tokens
     ref = torch.full((tq, wl.max_blocks), -1.0, dtype=torch.float32, device="cuda")
     got = torch.full((tq, wl.max_blocks), -2.0, dtype=torch.float32, device="cuda")
-    nb.msa_indexer_scan(ic, isc, inp["q_idx"], inp["w"], inp["block_table"], inp["seq_lens"], q, ref)
+    nb.msa_indexer_scan(ic, isc, inp["q_idx"], inp["w"], inp["block_table"], inp["seq_lens"],
+                        wl.q_per_seq, ref)
     nb.msa_indexer_scan_shared(ic, isc, inp["q_idx"], inp["w"], inp["block_table"],
-                               inp["seq_lens"], q, *groups, got)
+                               inp["seq_lens"], wl.q_per_seq, *groups, got)
     torch.cuda.synchronize()
     ref_np, got_np = ref.cpu().numpy(), got.cpu().numpy()
+    lens = inp["seq_lens"].cpu().numpy()          # the lengths the kernels saw
+    Q = wl.q_per_seq
     for b in range(wl.num_seqs):
-        for i, pos in enumerate(wl.positions(b)):
-            r = b * q + i
-            nbk = pos // 128 + 1
+        L = int(lens[b])
+        if not Q <= L <= wl.max_blocks * 128:      # invalid length: neither writes the rows
+            assert np.all(ref_np[b * Q:(b + 1) * Q] == -1.0)
+            assert np.all(got_np[b * Q:(b + 1) * Q] == -2.0), f"seq {b}: written despite its length"
+            continue
+        for i in range(Q):
+            r = b * Q + i
+            nbk = (L - Q + i) // 128 + 1
             assert np.array_equal(ref_np[r, :nbk].view(np.uint32), got_np[r, :nbk].view(np.uint32)), \
                 f"seq {b} token {i}: shared-prefix scores differ from the plain scan"
+    return got
+
+
+@pytest.mark.parametrize("lens,q,shared", SHARED, ids=["two-groups", "nine", "q8", "seventy"])
+def test_shared_prefix_scan(nb, lens, q, shared):
+    from msa_workloads.device import shared_groups
+    say(f"shared prefix scan {len(lens)} sequences q={q} shared={[(len(m), n) for m, n in shared]}")
+    wl = tiny_config(lens, q, seed=70 + q, shared=shared)
+    pools = S.fill_pools(wl, nb)
+    inp = S.device_inputs(wl)
+    groups = shared_groups(wl, nb)
+    assert groups[2] > 0 and len(groups[0]) == len(shared)
+    got = _plain_and_shared(nb, wl, inp, pools, groups)
     # the decode step on the shared-prefix scores, against the oracle
+    tq = wl.num_q_tokens
     ids = torch.empty((tq, wl.topk + 1), dtype=torch.int32, device="cuda")
     sc = torch.empty((tq, wl.topk + 1), dtype=torch.float32, device="cuda")
     o = torch.empty((tq, wl.num_q_heads, 128), dtype=torch.float32, device="cuda")
@@ -579,9 +596,32 @@ def test_shared_prefix_scan(nb, lens, q, shared):
     ids_np, sc_np, o_np = _to_np(dict(ids=ids, scores=sc, o=o))
     _structural(wl, ids_np)
     fails = []
-    for b in range(wl.num_seqs):
+    for b in sorted({0, 1, wl.num_seqs // 2, wl.num_seqs - 1}):
         fails += S.check_sequence(wl, b, ids_np, sc_np, o_np)
     assert not fails, "\n".join(fails[:20])
+
+
+def test_shared_prefix_scan_with_wrong_groups(nb):
+    """Group arrays that do not match the block table only share less: a
+    member whose pages differ from the lead's, a lead outside the batch, a
+    group id past num_groups, a group longer than the table, a sequence of
+    invalid length in a group, and a member listed in a group it does not
+    share pages with. Every score must still be the plain scan's."""
+    say("shared prefix scan with group arrays that do not match the block table")
+    wl = tiny_config([3000, 2600, 2900, 2500, 1900, 3100], 2, seed=81,
+                     shared=[([0, 1, 2], 12), ([3, 4], 9)])
+    pools = S.fill_pools(wl, nb)
+    inp = S.device_inputs(wl)
+    lens = inp["seq_lens"].clone()
+    lens[4] = 1                                   # invalid length, still in group 1
+    inp["seq_lens"] = lens
+    i32 = dict(dtype=torch.int32, device="cuda")
+    lead = torch.tensor([0, 3, 77], **i32)         # group 2: lead outside the batch
+    blocks = torch.tensor([14, 40, 5], **i32)      # group 0 claims 14 (12 shared), group 1 past the table
+    seq_group = torch.tensor([0, 0, 0, 1, 1, 0], **i32)   # seq 5 shares nothing with the lead
+    _plain_and_shared(nb, wl, inp, pools, (lead, blocks, wl.max_blocks, seq_group))
+    seq_group = torch.tensor([2, 5, 0, -1, 1, 1], **i32)  # ids past num_groups, the lead outside
+    _plain_and_shared(nb, wl, inp, pools, (lead, blocks, wl.max_blocks, seq_group))
 
 
 def test_shared_prefix_scan_without_groups_is_plain_scan(nb):
@@ -596,8 +636,8 @@ def test_shared_prefix_scan_without_groups_is_plain_scan(nb):
     nb.msa_indexer_scan(ic, isc, inp["q_idx"], inp["w"], inp["block_table"], inp["seq_lens"], 2, ref)
     i32 = dict(dtype=torch.int32, device="cuda")
     nb.msa_indexer_scan_shared(ic, isc, inp["q_idx"], inp["w"], inp["block_table"],
-                               inp["seq_lens"], 2, torch.zeros(1, **i32), torch.zeros(0, **i32),
-                               torch.zeros(0, **i32), 0, torch.zeros(wl.num_seqs, **i32), got)
+                               inp["seq_lens"], 2, torch.zeros(0, **i32), torch.zeros(0, **i32), 0,
+                               torch.full((wl.num_seqs,), -1, **i32), got)
     torch.cuda.synchronize()
     assert torch.equal(ref.view(torch.int32), got.view(torch.int32))
 

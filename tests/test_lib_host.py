@@ -181,10 +181,9 @@ def test_shared_prefix_scan_rejects_before_launch(L):
     f = L.msa_indexer_scan_shared
     d = ctypes.byref(_desc())
 
-    def call(desc=d, q=32, mb=4, ns=1, qps=1, ng=1, gs=256, gq=256, gb=256, mgb=2, ssb=256,
-             bs=256, ptr=256):
-        return f(desc, ptr, ptr, ptr, ptr, q, ptr, mb, ptr, ns, qps, ng, gs, gq, gb, mgb, ssb, bs,
-                 None)
+    def call(desc=d, q=32, mb=4, ns=1, qps=1, ng=1, gl=256, gb=256, mgb=2, sg=256, bs=256,
+             ptr=256):
+        return f(desc, ptr, ptr, ptr, ptr, q, ptr, mb, ptr, ns, qps, ng, gl, gb, mgb, sg, bs, None)
     assert call(desc=None) == 1
     assert call(q=24) == 2
     assert call(qps=9) == 2
@@ -193,14 +192,81 @@ def test_shared_prefix_scan_rejects_before_launch(L):
     assert call(mgb=0) == 1                      # groups need shared blocks
     assert call(mgb=5) == 1                      # more than max_blocks
     assert call(ns=0) == 0
-    assert call(gs=None) == 1
-    assert call(gq=None) == 1
+    assert call(gl=None) == 1
     assert call(gb=None) == 1
-    assert call(ssb=None) == 1
-    assert call(gs=4096 + 2) == 1                # misaligned group arrays
-    assert call(ssb=4096 + 1) == 1
-    assert call(bs=None) == 1
-    assert call(ptr=None) == 1
+    assert call(sg=None) == 1
+    assert call(gl=4096 + 2) == 1                # misaligned group arrays
+
+
+def _groups_reference(bt, lens, q):
+    """The grouping rule read directly: valid sequences keyed by their block-0
+    page (>= 0), in order of first appearance; a key with two or more members
+    shares the largest r such that every member has at least r blocks and
+    the same non-negative pages in blocks 0..r-1 as the first member."""
+    nb = [(int(L) + 127) // 128 for L in lens]
+    valid = [q <= int(L) <= bt.shape[1] * 128 for L in lens]
+    keys = []
+    members = {}
+    for b in range(len(lens)):
+        if valid[b] and bt[b, 0] >= 0:
+            k = int(bt[b, 0])
+            if k not in members:
+                keys.append(k)
+                members[k] = []
+            members[k].append(b)
+    lead, blocks, group = [], [], [-1] * len(lens)
+    for k in keys:
+        m = members[k]
+        if len(m) < 2:
+            continue
+        best = 0
+        for r in range(1, bt.shape[1] + 1):
+            if all(r <= nb[x] and all(bt[x, i] == bt[m[0], i] >= 0 for i in range(r)) for x in m):
+                best = r
+        if best == 0:
+            continue
+        for x in m:
+            group[x] = len(lead)
+        lead.append(m[0])
+        blocks.append(best)
+    return lead, blocks, group
+
+
+def test_shared_prefix_groups_match_the_rule(L):
+    import numpy as np
+    import torch
+    from msa_workloads import get_config, tiny_config
+    cases = [get_config(4), get_config(2), get_config(0),
+             tiny_config([1000, 700, 3000, 130, 2600, 900], 2, seed=72,
+                         shared=[([0, 1, 3], 6), ([2, 4], 20)]),
+             tiny_config([2300] * 9 + [500], 1, seed=71, shared=[(list(range(9)), 17)])]
+    rng = np.random.default_rng(5)
+    for t in range(30):                          # random aliasing, invalid lengths and pages
+        ns, mb = int(rng.integers(1, 12)), int(rng.integers(1, 9))
+        bt = rng.integers(-1, 4, size=(ns, mb)).astype(np.int32)
+        bt[rng.random(ns) < 0.5, 0] = 1
+        lens = rng.integers(-2, mb * 128 + 40, size=ns).astype(np.int32)
+        cases.append((bt, lens, int(rng.integers(1, 3))))
+    for c in cases:
+        bt, lens, q = (c if isinstance(c, tuple) else
+                       (c.block_table.astype(np.int32), np.asarray(c.seq_lens, np.int32), c.q_per_seq))
+        lead, blocks, mgb, group = nb.msa_shared_prefix_groups(torch.from_numpy(bt),
+                                                                torch.from_numpy(lens), q)
+        want = _groups_reference(bt, lens, q)
+        assert lead.tolist() == want[0] and blocks.tolist() == want[1], (bt, lens)
+        assert group.tolist() == want[2]
+        assert mgb == (max(want[1]) if want[1] else 0)
+    # the ragged workload: one group of all 45 requests sharing 128 blocks
+    w4 = get_config(4)
+    lead, blocks, mgb, group = nb.msa_shared_prefix_groups(
+        torch.from_numpy(w4.block_table.astype(np.int32)), torch.tensor(w4.seq_lens, dtype=torch.int32), 1)
+    assert lead.tolist() == [0] and blocks.tolist() == [128] and mgb == 128
+    assert group.tolist() == [0] * 45
+    f = L.msa_shared_prefix_groups
+    out = (ctypes.c_int32 * 4)()
+    assert f(None, 4, None, 0, 1, None, None, None, ctypes.byref(out, 0), ctypes.byref(out, 4)) == 0
+    assert f(None, 4, None, 2, 1, None, None, None, ctypes.byref(out, 0), ctypes.byref(out, 4)) == 1
+    assert f(None, 0, None, 0, 1, None, None, None, ctypes.byref(out, 0), ctypes.byref(out, 4)) == 1
 
 
 def test_scale_layout_view_matches_header_formula():
