@@ -69,6 +69,13 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain 1 GiB device-to-device copy (the reference kernel "
                         "for scaling HBM byte counters) and exit")
+    p.add_argument("--record-traffic", action="store_true",
+                   help="write profiles/traffic_indexer_scan_<workload>.json from the four "
+                        "rocprofv3 --pmc output folders given below, and exit")
+    p.add_argument("--fetch-dir")
+    p.add_argument("--write-dir")
+    p.add_argument("--copy-fetch-dir")
+    p.add_argument("--copy-write-dir")
     p.add_argument("--cpu-blocks", type=int, default=2048,
                    help="index blocks of one sequence the CPU oracle scans (time is scaled "
                         "to the whole context when fewer)")
@@ -119,7 +126,9 @@ def scan_bytes_per_workgroup(wl):
     return bpw * wl.num_idx_heads * 128 * IDX_BYTES_PER_TOKEN_HEAD // 16 * 16
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_indexer_scan_long_context_8x256k.json")
+def traffic_file(workload_name: str) -> str:
+    """The committed HBM-counter record of the index scan on a workload."""
+    return os.path.join(ROOT, "profiles", f"traffic_indexer_scan_{workload_name}.json")
 
 
 SCAN_SOURCES = ("indexer.hip", "scan_body.h", "nvfp4_tile.h")
@@ -142,13 +151,78 @@ def measured_traffic(workload_name: str, path=None, sources=SCAN_SOURCES):
     """HBM bytes per launch from a committed rocprofv3 counter record, or
     None when there is none for this workload or the kernel changed."""
     try:
-        with open(path or TRAFFIC_FILE) as fh:
+        with open(path or traffic_file(workload_name)) as fh:
             rec = json.load(fh)
     except (OSError, ValueError):
         return None
     if rec.get("workload") != workload_name or rec.get("kernel_source_sha256") != kernel_source_digest(sources):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def _counter_means(run_dir: str, counter: str) -> dict:
+    """Mean Counter_Value (KiB) per dispatch and dispatch count, by kernel
+    name, from the run_counter_collection.csv rocprofv3 --pmc wrote."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    acc = {}
+    for f in files:
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                if row.get("Counter_Name") != counter:
+                    continue
+                k = acc.setdefault(row["Kernel_Name"], [0.0, 0])
+                k[0] += float(row["Counter_Value"])
+                k[1] += 1
+    return {name: (v / n, n) for name, (v, n) in acc.items()}
+
+
+def record_traffic(args):
+    """Write profiles/traffic_indexer_scan_<workload>.json from four
+    rocprofv3 --pmc runs: FETCH_SIZE and WRITE_SIZE of a bench.py run on the
+    workload, and of bench.py --copy-calibration (a plain 1 GiB copy, whose
+    known bytes scale each counter). The record carries the sha256 of the
+    scan's sources; bench.py reports it only while they are unchanged."""
+    import numpy as np
+    from msa_workloads import get_config
+
+    wl = get_config(args.workload)
+    fetch = _counter_means(args.fetch_dir, "FETCH_SIZE")
+    write = _counter_means(args.write_dir, "WRITE_SIZE")
+    cfetch = _counter_means(args.copy_fetch_dir, "FETCH_SIZE")
+    cwrite = _counter_means(args.copy_write_dir, "WRITE_SIZE")
+
+    def pick(d, key):
+        names = [n for n in d if key in n]
+        if len(names) != 1:
+            raise SystemExit(f"expected one kernel matching {key!r}, found {names}")
+        return d[names[0]], names[0]
+    (f_kib, f_n), kname = pick(fetch, "indexer_kernel")
+    (w_kib, w_n), _ = pick(write, "indexer_kernel")
+    (cf_kib, _), _ = pick(cfetch, "copyBuffer")
+    (cw_kib, _), _ = pick(cwrite, "copyBuffer")
+    n = 1 << 30
+    fs, ws = n / 1024 / cf_kib, n / 1024 / cw_kib
+    ids = np.zeros((wl.num_q_tokens, wl.topk + 1), dtype=np.int32)
+    # a page mapped by several sequences (a shared prefix) is read once
+    nblk = sum(wl.blocks_of(b) for b in range(wl.num_seqs))
+    dedup = len(wl.pages_in_use()) < nblk
+    alg = algorithmic_bytes(wl, ids, dedup=dedup)[0]
+    hbm = int(round(f_kib * 1024 * fs + w_kib * 1024 * ws))
+    rec = {"workload": wl.name, "kernel": kname,
+           "kernel_source_sha256": kernel_source_digest(),
+           "fetch_kib_per_dispatch": round(f_kib, 3), "write_kib_per_dispatch": round(w_kib, 3),
+           "dispatches": [f_n, w_n], "copy_fetch_kib_per_dispatch": round(cf_kib, 3),
+           "copy_write_kib_per_dispatch": round(cw_kib, 3), "copy_bytes_read": n,
+           "copy_bytes_written": n, "fetch_scale": round(fs, 5), "write_scale": round(ws, 5),
+           "hbm_bytes_per_launch": hbm, "algorithmic_bytes_per_launch": int(alg),
+           "traffic_over_algorithmic": round(hbm / alg, 4)}
+    with open(traffic_file(wl.name), "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec))
 
 
 def copy_calibration():
@@ -536,6 +610,11 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.record_traffic:
+        if args.workload is None:
+            args.workload = 2
+        record_traffic(args)
         return
     if args.insert:
         insert_bench(args)

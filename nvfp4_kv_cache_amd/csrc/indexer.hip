@@ -11,7 +11,10 @@
 //
 // Two kernels. The scan kernel has grid (block chunks, sequences) and one
 // wavefront per index-key head; workgroup x of a sequence takes blocks x,
-// x + G, x + 2G, ... (G = grid width). Per 128-token block a wave streams its
+// x + G, x + 2G, ... (G = grid width); with shared prefixes its leading
+// rows hold the shared-prefix workgroups (shared_workgroup below), which
+// score each shared block once for all the sequences of its group. Per
+// 128-token block a wave streams its
 // head's 8 KiB of codes and 1 KiB of scales in coalesced 16-byte
 // non-temporal loads (lane l: token row 16j + l%16, 32-channel slice l/16),
 // turns them into FP8 MFMA operands through the LDS lookup table, and
