@@ -98,8 +98,10 @@ typedef struct msa_pool_desc {
   int64_t num_pages;    /* pages in the pool; > 0 */
 } msa_pool_desc;
 
-/* Human-readable name of a status code (static storage). */
-const char* msa_status_string(msa_status s);
+/* Human-readable name of a status code (static storage); any other value
+ * (the argument is a plain int, so no value is out of range) gives
+ * "unknown msa_status". */
+const char* msa_status_string(int32_t status);
 
 /*
  * Cache writer: quantise fp32 rows to NVFP4 and store them into a pool.

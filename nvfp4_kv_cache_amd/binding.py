@@ -41,7 +41,7 @@ _F32 = ctypes.c_float
 _DESC = ctypes.POINTER(PoolDesc)
 
 SIGNATURES = {
-    "msa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "msa_status_string": (ctypes.c_char_p, [_I32]),
     "msa_nvfp4_quantize": (ctypes.c_int, [_DESC, _P, _P, _I64, _P, _P, _P]),
     "msa_indexer_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
     "msa_indexer_decode": (ctypes.c_int, [_DESC, _P, _P, _P, _P, _I32, _P, _I32, _P, _I32, _I32,

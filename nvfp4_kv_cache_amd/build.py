@@ -1,6 +1,7 @@
 """Build libmsa_nvfp4.so (HIP, gfx950) in-tree with hipcc.
 
-    python -m nvfp4_kv_cache_amd.build
+    python -m nvfp4_kv_cache_amd.build              # the library
+    python -m nvfp4_kv_cache_amd.build --sanitize   # host-sanitized copy for the host tests
 
 Every HIP source under csrc/ is compiled for gfx950 with packed-FP32
 instructions disabled, then linked into one shared library next to this file.
@@ -40,31 +41,46 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *FLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
+def _compile(src: str, out_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(out_dir, os.path.basename(src)[:-4] + ".o")
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer for the C shim
+# (argument checks, group derivation, launch set-up); the device code is
+# built as usual. Each -fsanitize= applies to the host compilation only.
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
+SAN_BUILD = os.path.join(PKG, "_build_sanitize")
+SAN_LIB = os.path.join(SAN_BUILD, "libmsa_nvfp4_sanitize.so")
+
+
+def build(verbose: bool = True, sanitize: bool = False) -> str:
+    out_dir = SAN_BUILD if sanitize else BUILD
+    out_lib = SAN_LIB if sanitize else LIB
+    os.makedirs(out_dir, exist_ok=True)
     srcs = sources()
+    extra = SANITIZE if sanitize else []
+
+    def comp(src):
+        return _compile(src, out_dir, extra)
     with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+        objs = list(ex.map(comp, srcs))
+    tmp = out_lib + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra, *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out_lib)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources for {ARCH}")
-    return LIB
+        print(f"built {out_lib} from {len(srcs)} sources for {ARCH}")
+    return out_lib
 
 
 if __name__ == "__main__":
-    build()
+    build(sanitize="--sanitize" in sys.argv)
     sys.exit(0)

@@ -1,8 +1,8 @@
 // status.hip -- status strings of the C ABI.
 #include "msa_nvfp4.h"
 
-extern "C" const char* msa_status_string(msa_status s) {
-  switch (s) {
+extern "C" const char* msa_status_string(int32_t status) {
+  switch (status) {
     case MSA_OK: return "MSA_OK";
     case MSA_ERR_INVALID_ARG: return "MSA_ERR_INVALID_ARG: null pointer, bad size or misaligned buffer";
     case MSA_ERR_UNSUPPORTED: return "MSA_ERR_UNSUPPORTED: shape not implemented by this library";

@@ -32,3 +32,9 @@ def pytest_collection_modifyitems(config, items):
 def pytest_sessionstart(session):
     import _support
     _support.tune_host_malloc()
+    # MSA_TEST_LIB: run the tests on another build of the library (the
+    # host-sanitized one: python -m nvfp4_kv_cache_amd.build --sanitize)
+    lib = os.environ.get("MSA_TEST_LIB")
+    if lib:
+        import nvfp4_kv_cache_amd.binding as binding
+        binding.LIB_PATH = lib

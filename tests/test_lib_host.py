@@ -348,3 +348,32 @@ def test_mono_rejects_before_launch(L):
     assert call(ws=None) == 3
     assert call(ws=4096 + 16) == 3                       # workspace not 256-byte aligned
     assert call(wsb=64) == 3
+
+
+def test_host_checks_under_asan_and_ubsan():
+    """The host tests above, again in a child process on the library built
+    with host-side AddressSanitizer and UndefinedBehaviorSanitizer
+    (python -m nvfp4_kv_cache_amd.build --sanitize; __graft_entry__.build()
+    builds it): every argument check, the group derivation and the launch
+    set-up run without a memory error or undefined behaviour. No GPU is
+    touched (every call in those tests is rejected before a launch)."""
+    import subprocess
+    import sys
+    from nvfp4_kv_cache_amd import build as B
+    if os.environ.get("MSA_TEST_LIB"):
+        pytest.skip("already running on another build of the library")
+    if not os.path.exists(B.SAN_LIB):
+        pytest.skip("host-sanitized library not built")
+    r = subprocess.run([B.HIPCC, "--print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True)
+    asan = r.stdout.strip()
+    if r.returncode != 0 or not os.path.exists(asan):
+        pytest.skip("no AddressSanitizer runtime found")
+    env = dict(os.environ, LD_PRELOAD=asan, MSA_TEST_LIB=B.SAN_LIB,
+               ASAN_OPTIONS="detect_leaks=0:halt_on_error=1",
+               UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
+    r = subprocess.run([sys.executable, "-m", "pytest", os.path.abspath(__file__), "-q",
+                        "-p", "no:cacheprovider", "-k", "not asan_and_ubsan"],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, (r.stdout[-3000:] + r.stderr[-3000:])
+    assert " passed" in r.stdout
