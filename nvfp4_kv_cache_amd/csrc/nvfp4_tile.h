@@ -98,18 +98,20 @@ constexpr Fp8Lut make_fp8_lut() {
   return t;
 }
 
-// amax thresholds for the scale: 6 x the midpoints between consecutive E4M3
-// values, exact in fp32 (at most 7 significant bits); padded with +inf.
-struct ScaleThresholds {
-  float t[128];
+// amax bounds of the scale bytes: b[k] and b[k + 1] are 6 x the midpoints
+// of E4M3 byte k with its lower and upper neighbour, exact in fp32 (at most
+// 7 significant bits); b[0] = -1 lies below every amax and b[127] = +inf
+// above every finite one (byte 126, 448, is the largest finite E4M3).
+struct ScaleBounds {
+  float b[128];
 };
 
-constexpr ScaleThresholds make_scale_thresholds() {
-  ScaleThresholds r{};
+constexpr ScaleBounds make_scale_bounds() {
+  ScaleBounds r{};
+  r.b[0] = -1.0f;
   for (int k = 0; k < 126; ++k)
-    r.t[k] = float(3 * (e4m3_units(k) + e4m3_units(k + 1))) * (1.0f / 2048.0f);
-  r.t[126] = __builtin_huge_valf();
-  r.t[127] = __builtin_huge_valf();
+    r.b[k + 1] = float(3 * (e4m3_units(k) + e4m3_units(k + 1))) * (1.0f / 2048.0f);
+  r.b[127] = __builtin_huge_valf();
   return r;
 }
 

@@ -5,8 +5,8 @@
 // every element, and writes 8 code bytes plus 1 scale byte into the token's
 // page row. Both roundings are decided by exact fp32 comparisons: amax
 // against 6 x (midpoint of two E4M3 values) and |x| against
-// s x (midpoint of two E2M1 values); every such threshold has at most 7
-// significant bits, so no division and no rounding of the thresholds occur.
+// s x (midpoint of two E2M1 values); every such bound has at most 7
+// significant bits, so no division and no rounding of the bounds occur.
 // Format: NVFP4 as reproduced by the pages' 34,560 bytes per token
 // (MiniMax-M3.1-Flash lands in vLLM on day one, first paragraph).
 #include "msa_nvfp4.h"
@@ -14,13 +14,13 @@
 
 namespace msa {
 
-__constant__ ScaleThresholds kScaleThr = make_scale_thresholds();
+__constant__ ScaleBounds kScaleBnd = make_scale_bounds();
 
 __global__ __launch_bounds__(256) void nvfp4_quantize_kernel(
     const float* __restrict__ src, const int64_t* __restrict__ slot_mapping, int64_t num_groups,
     int num_heads, int64_t num_slots, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
-  __shared__ float thr[128];
-  if (threadIdx.x < 128) thr[threadIdx.x] = kScaleThr.t[threadIdx.x];
+  __shared__ float bnd[128];
+  if (threadIdx.x < 128) bnd[threadIdx.x] = kScaleBnd.b[threadIdx.x];
   __syncthreads();
 
   const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_kernel(
     x[4 * i + 3] = v.w;
   }
   uint32_t packed[2];
-  const int sb = nvfp4_encode_group(x, thr, packed);
+  const int sb = nvfp4_encode_group(x, bnd, packed);
 
   const int64_t page = slot / kBlockTokens;
   const int row = int(slot % kBlockTokens);

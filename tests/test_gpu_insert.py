@@ -104,19 +104,29 @@ def test_insert_bit_exact_without_norm_and_rope(nb, hkv, hidx, t):
         assert np.array_equal(gs, os_)
 
 
-@pytest.mark.parametrize("rot,theta,norm", [(128, 1e4, True), (64, 1e6, True), (96, 5e5, False),
-                                            (32, 1e4, True), (0, 1e4, True)])
-def test_insert_with_norm_and_rope_matches_oracle(nb, rot, theta, norm):
-    hkv, hidx, t = 4, 4, 53
-    say(f"[insert norm/rope] rot={rot} theta={theta} norm={norm}")
+# norm: which heads carry RMSNorm weights ("qk" both, "q" / "k" one class).
+# Head counts (1, 3) and (3, 1) put rows of several kinds (keys, values,
+# index keys) into one wavefront pass of eight rows; (8, 8) is the largest.
+@pytest.mark.parametrize("rot,theta,norm,hkv,hidx", [
+    (128, 1e4, "qk", 4, 4), (64, 1e6, "qk", 4, 4), (96, 5e5, "", 4, 4), (32, 1e4, "qk", 4, 4),
+    (0, 1e4, "qk", 4, 4), (128, 1e4, "", 4, 4), (128, 1e6, "q", 1, 3), (128, 1e4, "k", 3, 1),
+    (64, 1e4, "qk", 1, 3), (0, 1e4, "k", 3, 1), (128, 1e4, "qk", 8, 8), (32, 5e5, "q", 2, 1)])
+def test_insert_with_norm_and_rope_matches_oracle(nb, rot, theta, norm, hkv, hidx):
+    t = 53
+    say(f"[insert norm/rope] rot={rot} theta={theta} norm={norm!r} hkv={hkv} hidx={hidx}")
     width = (8 * hkv + 8 * hidx + 2 * hkv + hidx) * 128
-    rows = synth.projection_rows(7 + rot, t, width)
+    rows = synth.projection_rows(7 + rot + 10 * hkv + hidx, t, width)
+    # token 0's first value head: signed zeros and every E2M1 midpoint of
+    # scale 1 (amax 6), which the value path must pass through unchanged
+    vrow = (8 * hkv + 8 * hidx + hkv) * 128
+    rows[0, vrow:vrow + 16] = torch.tensor([-0.0, 0.0, 0.25, -0.75, 1.25, -1.75, 2.5, -3.5, 5.0,
+                                            6.0, -0.0, 0.5, -1.0, 1.5, -2.0, 3.0])
     pages = 3
     slots = np.random.default_rng(rot).permutation(pages * 128)[:t].astype(np.int64)
     pos = np.concatenate([[0, 1, 2], np.random.default_rng(1).integers(0, 262144, size=t - 4),
                           [262143]])
-    qn = synth.norm_weights(3, 0) if norm else None
-    kn = synth.norm_weights(3, 1) if norm else None
+    qn = synth.norm_weights(3, 0) if "q" in norm else None
+    kn = synth.norm_weights(3, 1) if "k" in norm else None
     host, q, qi = _run(nb, rows, pos, slots, pages, hkv, hidx, qn, kn, 1e-6, rot, theta)
     oq, oqi, ok, ov, oki = I.transform(_bits(rows), pos, hkv, hidx,
                                        None if qn is None else qn.numpy(),
