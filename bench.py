@@ -181,15 +181,15 @@ def _counter_means(run_dir: str, counter: str) -> dict:
 
 
 def record_traffic(args):
-    """Write profiles/traffic_indexer_scan_<workload>.json from four
-    rocprofv3 --pmc runs: FETCH_SIZE and WRITE_SIZE of a bench.py run on the
-    workload, and of bench.py --copy-calibration (a plain 1 GiB copy, whose
-    known bytes scale each counter). The record carries the sha256 of the
-    scan's sources; bench.py reports it only while they are unchanged."""
+    """Write profiles/traffic_indexer_scan_<workload>.json (or, with
+    --insert, the cache-insertion record) from four rocprofv3 --pmc runs:
+    FETCH_SIZE and WRITE_SIZE of a bench.py run on the workload, and of
+    bench.py --copy-calibration (a plain 1 GiB copy, whose known bytes scale
+    each counter). The record carries the sha256 of the kernel's sources;
+    bench.py reports it only while they are unchanged."""
     import numpy as np
     from msa_workloads import get_config
 
-    wl = get_config(args.workload)
     fetch = _counter_means(args.fetch_dir, "FETCH_SIZE")
     write = _counter_means(args.write_dir, "WRITE_SIZE")
     cfetch = _counter_means(args.copy_fetch_dir, "FETCH_SIZE")
@@ -200,27 +200,34 @@ def record_traffic(args):
         if len(names) != 1:
             raise SystemExit(f"expected one kernel matching {key!r}, found {names}")
         return d[names[0]], names[0]
-    (f_kib, f_n), kname = pick(fetch, "indexer_kernel")
-    (w_kib, w_n), _ = pick(write, "indexer_kernel")
+    key = "qkv_rope_insert_kernel" if args.insert else "indexer_kernel"
+    (f_kib, f_n), kname = pick(fetch, key)
+    (w_kib, w_n), _ = pick(write, key)
     (cf_kib, _), _ = pick(cfetch, "copyBuffer")
     (cw_kib, _), _ = pick(cwrite, "copyBuffer")
     n = 1 << 30
     fs, ws = n / 1024 / cf_kib, n / 1024 / cw_kib
-    ids = np.zeros((wl.num_q_tokens, wl.topk + 1), dtype=np.int32)
-    # a page mapped by several sequences (a shared prefix) is read once
-    nblk = sum(wl.blocks_of(b) for b in range(wl.num_seqs))
-    dedup = len(wl.pages_in_use()) < nblk
-    alg = algorithmic_bytes(wl, ids, dedup=dedup)[0]
+    if args.insert:
+        name, path, sources = "prefill_insert_16k", INSERT_TRAFFIC_FILE, INSERT_SOURCES
+        alg = insert_algorithmic_bytes(INSERT_TOKENS, INSERT_HKV, INSERT_HIDX)
+    else:
+        wl = get_config(args.workload)
+        name, path, sources = wl.name, traffic_file(wl.name), SCAN_SOURCES
+        ids = np.zeros((wl.num_q_tokens, wl.topk + 1), dtype=np.int32)
+        # a page mapped by several sequences (a shared prefix) is read once
+        nblk = sum(wl.blocks_of(b) for b in range(wl.num_seqs))
+        dedup = len(wl.pages_in_use()) < nblk
+        alg = algorithmic_bytes(wl, ids, dedup=dedup)[0]
     hbm = int(round(f_kib * 1024 * fs + w_kib * 1024 * ws))
-    rec = {"workload": wl.name, "kernel": kname,
-           "kernel_source_sha256": kernel_source_digest(),
+    rec = {"workload": name, "kernel": kname,
+           "kernel_source_sha256": kernel_source_digest(sources),
            "fetch_kib_per_dispatch": round(f_kib, 3), "write_kib_per_dispatch": round(w_kib, 3),
            "dispatches": [f_n, w_n], "copy_fetch_kib_per_dispatch": round(cf_kib, 3),
            "copy_write_kib_per_dispatch": round(cw_kib, 3), "copy_bytes_read": n,
            "copy_bytes_written": n, "fetch_scale": round(fs, 5), "write_scale": round(ws, 5),
            "hbm_bytes_per_launch": hbm, "algorithmic_bytes_per_launch": int(alg),
            "traffic_over_algorithmic": round(hbm / alg, 4)}
-    with open(traffic_file(wl.name), "w") as fh:
+    with open(path, "w") as fh:
         json.dump(rec, fh, indent=1)
     print(json.dumps(rec))
 
@@ -299,16 +306,28 @@ def cpu_baseline(wl, nblk):
 # 2,048 positions of a 256K context), 4 KV heads and 4 index-key heads, so a
 # projection row holds 32 + 32 query heads and 4 + 4 + 4 key/value heads.
 INSERT_TOKENS, INSERT_HKV, INSERT_HIDX = 16384, 4, 4
+# tokens of the launch the CPU oracle is timed on: all of them (about 7 s of
+# CPU work on 16 cores)
+INSERT_CPU_SAMPLE = 16384
 
 
-def insert_algorithmic_bytes(t, hkv, hidx):
-    """Bytes the insertion must move: the bf16 projection rows, positions and
-    slots, the two norm weight vectors; the NVFP4 K / V / index rows and the
-    FP8 queries written."""
+# tokens per workgroup of the insertion kernel (its launch geometry)
+INSERT_TOKENS_PER_WORKGROUP = 2
+
+
+def insert_read_write_bytes(t, hkv, hidx):
+    """Bytes the insertion must read (the bf16 projection rows, positions and
+    slots, the two norm weight vectors) and write (the NVFP4 K / V / index
+    rows and the FP8 queries)."""
     rows = 8 * hkv + 8 * hidx + 2 * hkv + hidx
     read = t * rows * 128 * 2 + t * (4 + 8) + 2 * 128 * 4
     write = t * (2 * hkv + hidx) * IDX_BYTES_PER_TOKEN_HEAD + t * 8 * (hkv + hidx) * 128
-    return read + write
+    return read, write
+
+
+def insert_algorithmic_bytes(t, hkv, hidx):
+    """Bytes the insertion must move (read + written)."""
+    return sum(insert_read_write_bytes(t, hkv, hidx))
 
 
 def insert_cpu_baseline(rows, pos, qn, kn, sample):
@@ -403,24 +422,79 @@ def insert_bench(args):
             fused()
         warmup_run += 10
         torch.cuda.synchronize()
+    # Timed region: cold launches. Before each, a 512 MiB read (a torch sum,
+    # ordinary loads) evicts the previous launch's rows and outputs from the
+    # L2 and last-level caches and leaves them holding clean lines; a short
+    # spin kernel keeps the host's launch latency out; neither is inside the
+    # event pair. Each launch then reads its rows from HBM. (An overwrite
+    # instead leaves up to the last-level cache's size of dirty lines, whose
+    # write-back then lands inside the next launch: reported beside it as
+    # launch_us_after_fill.)
+    evict = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    fill = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    n_cold = max(args.steps, 100)
+
+    def cold(fn, n, dirty=False):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        for i, (e0, e1) in enumerate(ev):
+            if dirty:
+                fill.fill_(i & 0xFF)
+            else:
+                evict.sum()
+            torch.cuda._sleep(100_000)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return np.array([e0.elapsed_time(e1) for e0, e1 in ev]) * 1e3
+
+    print(f"[bench] insert: timed region: {n_cold} cold launches", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    us = timed(fused, args.steps)
-    wall = (time.perf_counter() - t0) / args.steps * 1e6
+    cold_us = cold(fused, n_cold)
+    wall = time.perf_counter() - t0
+    med = float(np.median(cold_us))
+    mean = float(np.mean(cold_us))
+    p10, p90 = (float(x) for x in np.percentile(cold_us, [10, 90]))
+    after_fill = float(np.median(cold(fused, 50, dirty=True)))
+    # secondary: K launches back to back (rows can stay in the caches)
+    us_warm = timed(fused, args.steps)
     for _ in range(3):
         unfused()
     us_unfused = timed(unfused, max(3, args.steps // 5))
     alg = insert_algorithmic_bytes(t, hkv, hidx)
-    achieved = alg / (us * 1e-6) / 1e9
+    achieved = alg / (mean * 1e-6) / 1e9
+
+    # stream ceiling: a plain kernel that reads and writes the insertion's
+    # algorithmic bytes at once (msa_stream_probe: the same read:write mix,
+    # no arithmetic), at the insertion's read bytes per workgroup and at
+    # 1 MiB; mean of 50 cold launches each (same protocol)
+    read_b, write_b = insert_read_write_bytes(t, hkv, hidx)
+    src = torch.full((read_b // 16 * 16,), 3, dtype=torch.uint8, device=dev)
+    dst = torch.empty((write_b // 16 * 16,), dtype=torch.uint8, device=dev)
+    chunks, best = {}, None
+    for chunk in (read_b // t * INSERT_TOKENS_PER_WORKGROUP // 16 * 16, 1 << 20):
+        probe = nb.msa_stream_probe(src, dst, chunk, prepare=True)
+        for _ in range(5):
+            probe()
+        pus = float(np.mean(cold(probe, 50)))
+        gbs = (src.numel() + dst.numel()) / (pus * 1e-6) / 1e9
+        chunks[str(chunk)] = {"us": round(pus, 2), "gbs": round(gbs, 1)}
+        best = gbs if best is None else max(best, gbs)
+    del src, dst, evict, fill
+    stream_ceiling = {"kernel": "stream_probe_kernel (msa_stream_probe)", "read_bytes": read_b,
+                      "write_bytes": write_b, "chunks": chunks, "best_gbs": round(best, 1),
+                      "frac_of_peak": round(best / HBM_PEAK_GBS, 4)}
     res = {
         "metric": "cache-insert tokens/s (bf16 QKV projection rows -> RMSNorm, RoPE, NVFP4 K/V/index pages, FP8 queries)",
-        "value": round(t / (us * 1e-6), 1),
+        "value": round(t / (med * 1e-6), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "warmup_steps_run": warmup_run,
-        "ms_per_step": round(us / 1e3, 5),
+        "ms_per_step": round(med / 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -430,19 +504,31 @@ def insert_bench(args):
                    "index_heads": hidx, "q_heads": 8 * hkv, "index_q_heads": 8 * hidx,
                    "rotary_dim": 128, "rope_theta": 1e4, "rms_norm": True,
                    "positions": "8 x (262,144 - 2,048 .. 262,143)"},
-        "wall_us_per_step": round(wall, 2),
+        "timing": (f"median of {n_cold} cold launches (max(steps, 100)), each timed with HIP "
+                   f"events after a 512 MiB read that evicts the caches (clean) and a spin kernel, "
+                   f"both outside the event pair"),
+        "cold_launches_timed": n_cold,
+        "timed_region_wall_s": round(wall, 4),
+        "launch_us": {"median": round(med, 2), "mean": round(mean, 2), "p10": round(p10, 2),
+                      "p90": round(p90, 2)},
+        "launch_us_after_fill": round(after_fill, 2),
+        "warm_us_per_step": round(us_warm, 2),
         "unfused_us_per_step": round(us_unfused, 2),
         "unfused": "torch elementwise RMSNorm / RoPE / FP8 cast on the fp32 intermediate + 3 x msa_nvfp4_quantize",
         "roofline": {"bound": "hbm", "kernel": "qkv_rope_insert_kernel (msa_qkv_rope_insert)",
+                     "duration": "mean of the cold launches",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "algorithmic_bytes": alg,
                      "traffic": measured_traffic("prefill_insert_16k", INSERT_TRAFFIC_FILE,
-                                                 INSERT_SOURCES)},
+                                                 INSERT_SOURCES),
+                     "stream_ceiling": stream_ceiling,
+                     "frac_of_stream_ceiling": round(achieved / stream_ceiling["best_gbs"], 4)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         print("[bench] insert: cpu baseline (oracle)", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = insert_cpu_baseline(rows, pos_np, qn.cpu().numpy(), kn.cpu().numpy(), 256)
+        res["cpu_baseline"] = insert_cpu_baseline(rows, pos_np, qn.cpu().numpy(), kn.cpu().numpy(),
+                                                  INSERT_CPU_SAMPLE)
     print(json.dumps(res), flush=True)
 
 

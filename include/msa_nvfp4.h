@@ -444,6 +444,27 @@ msa_status msa_decode_mono(const msa_pool_desc* idx, const uint8_t* idx_codes,
 msa_status msa_read_probe(const void* buf, int64_t bytes, int64_t chunk_bytes, uint32_t* sink,
                           void* stream);
 
+/*
+ * Measurement: plain streaming reads and writes at once, the ceiling of a
+ * kernel with a given read:write mix (the cache writer reads the projection
+ * rows and writes the cache rows and FP8 queries: MiniMax-M3.1-Flash serving
+ * summary, section "Reduce both data movement and resource waits").
+ * Workgroup i reads chunk_bytes of src from byte i * chunk_bytes (the
+ * read probe's loads) and writes ceil(write_bytes / grid) bytes of dst
+ * (rounded up to 16) from byte i times that, in 32 KiB steps spread evenly
+ * over its reads (the last with its last read), with 16-byte non-temporal
+ * stores of read words XOR the fold of the words read so far (every load
+ * feeds a store); grid = ceil(read_bytes / chunk_bytes). Nothing outside
+ * [src, src + read_bytes) and [dst, dst + write_bytes) is touched; with
+ * write_bytes 0 nothing is read either.
+ * src and dst 16-byte aligned (dst may be null when write_bytes is 0);
+ * read_bytes > 0 (or both 0: nothing is launched), write_bytes and
+ * chunk_bytes multiples of 16, chunk_bytes in (0, 2^30]. One kernel on
+ * `stream`.
+ */
+msa_status msa_stream_probe(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes,
+                            int64_t chunk_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -9,7 +9,7 @@ from .binding import (  # noqa: F401
     empty_pool, indexer_workspace, lib, mono_block_scores, mono_check, mono_workspace,
     msa_attn_workspace_bytes, msa_decode_mono, msa_decode_mono_workspace_bytes,
     msa_indexer_decode, msa_indexer_decode_noalloc, msa_indexer_scan, msa_indexer_scan_shared,
-    msa_indexer_select, msa_indexer_workspace_bytes, msa_shared_prefix_groups, msa_nvfp4_quantize, msa_qkv_rope_insert, msa_read_probe,
+    msa_indexer_select, msa_indexer_workspace_bytes, msa_shared_prefix_groups, msa_nvfp4_quantize, msa_qkv_rope_insert, msa_read_probe, msa_stream_probe,
     msa_sparse_attn_decode, msa_sparse_attn_select_decode, msa_status_string, pool_desc,
     scales_rows,
 )

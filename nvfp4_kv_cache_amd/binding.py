@@ -64,6 +64,7 @@ SIGNATURES = {
     "msa_decode_mono": (ctypes.c_int, [_DESC, _P, _P, _P, _P, _DESC, _P, _P, _P, _P, _P, _I32, _P,
                                        _I32, _P, _I32, _I32, _I32, _P, _F32, _P, _P, _SZ, _P]),
     "msa_read_probe": (ctypes.c_int, [_P, _I64, _I64, _P, _P]),
+    "msa_stream_probe": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _P]),
     "msa_qkv_rope_insert": (ctypes.c_int, [_P, _I64, _P, _P, _DESC, _P, _P, _P, _P, _DESC, _P, _P,
                                            _P, _P, _F32, _I32, _F32, _P, _P, _P]),
 }
@@ -573,3 +574,15 @@ def msa_read_probe(buf, chunk_bytes, sink, prepare=False):
         raise ValueError("sink needs one entry per chunk")
     return _issue("msa_read_probe", (_ptr(buf), n, int(chunk_bytes), _ptr(sink), _stream()),
                   prepare)
+
+
+def msa_stream_probe(src, dst, chunk_bytes, prepare=False):
+    """Plain streaming read of all of src and write of all of dst (contiguous
+    GPU tensors, byte sizes multiples of 16) at once, src in chunks of
+    chunk_bytes per workgroup and dst split evenly over the workgroups."""
+    for t, nm in ((src, "src"), (dst, "dst")):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or not t.is_contiguous():
+            raise ValueError(f"{nm} must be a contiguous GPU tensor")
+    return _issue("msa_stream_probe", (
+        _ptr(src), src.numel() * src.element_size(), _ptr(dst), dst.numel() * dst.element_size(),
+        int(chunk_bytes), _stream()), prepare)

@@ -8,12 +8,12 @@
 // registers, and what leaves the kernel is the NVFP4 K / V / index-key rows
 // in their pages and the FP8 attention and index queries.
 //
-// One workgroup per four tokens, 256 threads (4 wavefronts): eight lanes per
+// One workgroup per two tokens, 256 threads (4 wavefronts): eight lanes per
 // 128-channel head row, 16 channels (two 16-byte loads) per lane. The
 // workgroup's rows are taken in kind-major order (all query rows, then
 // index-query, key, value and index-key rows), eight rows to a wavefront
 // pass, so a pass holds one kind whenever the head counts are multiples of
-// eight over the four tokens; each wavefront runs its own passes (wave,
+// eight over the two tokens; each wavefront runs its own passes (wave,
 // wave + 4, ...) with the rows of two later passes in flight. Per token,
 // LDS tables fold RMSNorm's weights into RoPE: for each channel c of the
 // query heads and of the key heads, A = w_c cos and B = -+ w_p sin (partner
@@ -113,6 +113,21 @@ __device__ __forceinline__ float dpp(float v) {
 }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Streaming (nontemporal) stores for the query and code rows: nothing in
+// this kernel reads them back, and marking them so measurably shortens the
+// launch (the one-byte scale stores, which the cache merges into lines, are
+// left as ordinary stores: marking them too was slower).
+__device__ __forceinline__ void store_stream(uint8_t* p, uint4 v) {
+  const u32x4 t = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(t, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ void store_stream(uint8_t* p, uint32_t lo, uint32_t hi) {
+  const u32x2 t = {lo, hi};
+  __builtin_nontemporal_store(t, reinterpret_cast<u32x2*>(p));
+}
 
 __device__ __forceinline__ void unpack_bf16(const uint4 (&u)[2], float (&x)[16]) {
   const uint32_t w[8] = {u[0].x, u[0].y, u[0].z, u[0].w, u[1].x, u[1].y, u[1].z, u[1].w};
@@ -125,14 +140,17 @@ __device__ __forceinline__ void unpack_bf16(const uint4 (&u)[2], float (&x)[16])
 
 constexpr int kInsertThreads = 256;  // 4 wavefronts
 constexpr int kInsertWaves = kInsertThreads / 64;
-constexpr int kInsertTokens = 4;     // tokens per workgroup
+constexpr int kInsertTokens = 2;     // tokens per workgroup
+constexpr int kInsertDepth = 3;      // passes of rows held per wavefront
 constexpr int kMaxRowsPerToken = 2 * kHeadsPerKv * MSA_MAX_HEADS + 3 * MSA_MAX_HEADS;
 
 // ROPE: 0 none; 1 rotary_dim 32, 64 or 96 (partner by lane shuffle);
 // 2 rotary_dim 128 (partner by DPP row_half_mirror). NORM: a norm weight
 // vector is given for the query or the key heads.
 template <int ROPE, bool NORM>
-__global__ __launch_bounds__(kInsertThreads)
+// five wavefronts per SIMD (at most 96 VGPRs): the kernel needs both the
+// arithmetic and the loads in flight of the extra wavefront
+__global__ __launch_bounds__(kInsertThreads) __attribute__((amdgpu_waves_per_eu(5)))
 void qkv_rope_insert_kernel(const InsertArgs a) {
   __shared__ float bnd[128];
   __shared__ float2 csn[kInsertTokens][64];  // cos, sin per angle
@@ -164,14 +182,13 @@ void qkv_rope_insert_kernel(const InsertArgs a) {
   // head << 15 | token * heads of the kind + head << 22.
   const int n0 = ntok * hq, n1 = n0 + ntok * hqi, n2 = n1 + ntok * hkv, n3 = n2 + ntok * hkv;
   auto row_entry = [=](int v) -> uint32_t {
-    const int kind = (v >= n0) + (v >= n1) + (v >= n2) + (v >= n3);
-    const int start = kind == 0 ? 0 : kind == 1 ? n0 : kind == 2 ? n1 : kind == 3 ? n2 : n3;
-    const int nh = kind == 0 ? hq : kind == 1 ? hqi : kind == 4 ? hidx : hkv;
-    const int base = kind == 0 ? 0
-                   : kind == 1 ? hq
-                   : kind == 2 ? hq + hqi
-                   : kind == 3 ? hq + hqi + hkv
-                               : hq + hqi + 2 * hkv;
+    // (running selects rather than a switch, which would become a table
+    // in private memory)
+    int kind = 0, start = 0, nh = hq, base = 0;
+    if (v >= n0) kind = 1, start = n0, nh = hqi, base = hq;
+    if (v >= n1) kind = 2, start = n1, nh = hkv, base = hq + hqi;
+    if (v >= n2) kind = 3, start = n2, nh = hkv, base = hq + hqi + hkv;
+    if (v >= n3) kind = 4, start = n3, nh = hidx, base = hq + hqi + 2 * hkv;
     const int off = v - start, tt = off / nh, head = off - tt * nh;
     return uint32_t(tt * rows + base + head) | uint32_t(kind) << 10 | uint32_t(tt) << 13 |
            uint32_t(head) << 15 | uint32_t(off) << 22;
@@ -201,11 +218,13 @@ void qkv_rope_insert_kernel(const InsertArgs a) {
   const int64_t slot_t = tid < ntok ? a.slot_mapping[t0 + tid] : -1;
   const float bnd_t = tid < 128 ? kInsertBnd.b[tid] : 0.0f;
 
-  uint4 ua[2], ub[2], uc[2];
-  uint32_t ia = row_entry(min(wave * 8 + rl, nrows - 1));
-  uint32_t ib = row_entry(min((wave + kInsertWaves) * 8 + rl, nrows - 1)), ic = 0;
-  issue(ia, ua);
-  issue(ib, ub);
+  uint4 ring[kInsertDepth][2];
+  uint32_t info[kInsertDepth];
+#pragma unroll
+  for (int d = 0; d + 1 < kInsertDepth; ++d) {
+    info[d] = row_entry(min((wave + d * kInsertWaves) * 8 + rl, nrows - 1));
+    issue(info[d], ring[d]);
+  }
 
   for (int v = tid; v < nrows; v += kInsertThreads) vmap[v] = row_entry(v);
   if (tid < 128) bnd[tid] = bnd_t;
@@ -328,7 +347,7 @@ void qkv_rope_insert_kernel(const InsertArgs a) {
     if (v >= nrows) return;
     if (kind <= 1) {
       uint8_t* dst = (kind == 0 ? qdst : qidst) + orow * kHeadDim;
-      *reinterpret_cast<uint4*>(dst) = clamp_q ? e4m3_pack16<true>(x) : e4m3_pack16<false>(x);
+      store_stream(dst, clamp_q ? e4m3_pack16<true>(x) : e4m3_pack16<false>(x));
     } else {
       const int64_t slot = slot_s[tt];
       const int64_t nslots = kind == 4 ? idx_slots : kv_slots;
@@ -340,30 +359,27 @@ void qkv_rope_insert_kernel(const InsertArgs a) {
       const int sb = nvfp4_encode_group(x, bnd, packed);
       const int64_t page_head = (slot / kBlockTokens) * nh + head;
       const int prow = int(slot % kBlockTokens);
-      *reinterpret_cast<uint2*>(codes + (page_head * kBlockTokens + prow) * kCodeRow + blk * 8) =
-          make_uint2(packed[0], packed[1]);
+      store_stream(codes + (page_head * kBlockTokens + prow) * kCodeRow + blk * 8, packed[0],
+                   packed[1]);
       scales[page_head * kScalePage + scale_offset(prow, blk)] = uint8_t(sb);
     }
   };
 
-  // wavefront passes wave, wave + 4, ...: three per iteration, in rotating
-  // register sets, each loaded two passes ahead. The loads are issued
-  // unconditionally (past the last pass they re-read the last row, a cache
-  // hit), so the wait before each pass counts exactly the loads issued
-  // after its own.
+  // wavefront passes wave, wave + 4, ...: kInsertDepth per iteration in
+  // rotating register sets, each loaded kInsertDepth - 1 passes ahead. The
+  // loads are issued unconditionally (past the last pass they re-read the
+  // last row, a cache hit), so the wait before each pass counts exactly the
+  // loads issued after its own.
   const int npass = (nrows + 7) >> 3;
-  auto entry = [&](int w) { return vmap[min(w * 8 + rl, nrows - 1)]; };
-  for (int wp = wave; wp < npass; wp += 3 * kInsertWaves) {
-    const int wq = wp + kInsertWaves, wr = wq + kInsertWaves;
-    ic = entry(wr);
-    issue(ic, uc);
-    process(wp, ua, ia);
-    ia = entry(wr + kInsertWaves);
-    issue(ia, ua);
-    if (wq < npass) process(wq, ub, ib);
-    ib = entry(wr + 2 * kInsertWaves);
-    issue(ib, ub);
-    if (wr < npass) process(wr, uc, ic);
+  for (int wp = wave; wp < npass; wp += kInsertDepth * kInsertWaves) {
+#pragma unroll
+    for (int d = 0; d < kInsertDepth; ++d) {
+      constexpr int kAhead = kInsertDepth - 1;
+      const int nd = (d + kAhead) % kInsertDepth;
+      info[nd] = vmap[min((wp + (d + kAhead) * kInsertWaves) * 8 + rl, nrows - 1)];
+      issue(info[nd], ring[nd]);
+      if (d == 0 || wp + d * kInsertWaves < npass) process(wp + d * kInsertWaves, ring[d], info[d]);
+    }
   }
 }
 
