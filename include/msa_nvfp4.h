@@ -305,8 +305,13 @@ msa_status msa_qkv_rope_insert(const uint16_t* qkv, int64_t num_tokens, const in
 
 /*
  * Workspace bytes msa_sparse_attn_decode needs for its split partial results
- * (running max, denominator and unnormalised output per split). No initial
- * contents are required.
+ * (running max, denominator and unnormalised output per split) and, after
+ * them, one arrival counter per (query token, KV head) pair: the pair's last
+ * split to finish merges the partials. 0 when the launch plan has one split
+ * per pair. Zero-fill a workspace once before its first use; every call
+ * leaves the counters zero again, so later calls need no refill (a call
+ * that does not run to completion, or two overlapping calls on one
+ * workspace, void this).
  */
 size_t msa_attn_workspace_bytes(int32_t num_seqs, int32_t q_per_seq, int32_t num_q_heads,
                                 int32_t num_sel);
@@ -323,6 +328,9 @@ size_t msa_attn_workspace_bytes(int32_t num_seqs, int32_t q_per_seq, int32_t num
  *                page is outside [0, num_pages) are ignored
  *   out          float [num_seqs * q_per_seq][num_q_heads][128]; a query
  *                token with no usable block gets zeros
+ *   workspace    msa_attn_workspace_bytes(num_seqs, q_per_seq, num_q_heads,
+ *                num_sel) bytes, 256-byte aligned, zero-filled before its
+ *                first use (MSA_ERR_WORKSPACE if smaller or misaligned)
  * 1 <= num_sel <= 64. The softmax weights enter the P x V product as two
  * FP8 terms, FP8(256 p) + FP8(16 (256 p - FP8(256 p))) / 16 (about 8
  * significant bits); the denominator sums the same rounded terms.
@@ -351,7 +359,7 @@ msa_status msa_sparse_attn_decode(const msa_pool_desc* kv, const uint8_t* k_code
  *   out_ids      int32 [num_seqs * q_per_seq][topk + 1] or NULL: the
  *                selected ids, as msa_indexer_select writes them
  *   workspace    msa_attn_workspace_bytes(num_seqs, q_per_seq, num_q_heads,
- *                topk + 1) bytes, no initial contents
+ *                topk + 1) bytes, zero-filled before its first use
  * Other arguments and device-side checks as msa_sparse_attn_decode; a
  * sequence with seq_lens < q_per_seq or seq_lens > max_blocks * 128 gets ids
  * -1 and zero output.

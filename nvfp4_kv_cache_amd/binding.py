@@ -241,9 +241,11 @@ def msa_attn_workspace_bytes(num_seqs: int, q_per_seq: int, num_q_heads: int, nu
 
 
 def attn_workspace(num_seqs, q_per_seq, num_q_heads, num_sel, device="cuda"):
-    """Workspace for msa_sparse_attn_decode (contents need no initialisation)."""
+    """Workspace for msa_sparse_attn_decode / msa_sparse_attn_select_decode,
+    zero-filled once (its split-arrival counters start at zero, and every
+    call leaves them zero)."""
     n = msa_attn_workspace_bytes(num_seqs, q_per_seq, num_q_heads, num_sel)
-    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
 
 
 def indexer_workspace(num_seqs, q_per_seq, max_blocks, device="cuda"):

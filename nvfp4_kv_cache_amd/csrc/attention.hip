@@ -13,8 +13,9 @@
 // Grid (splits, KV heads, query tokens), 4 wavefronts per workgroup. Split s
 // covers selected slots [s*4R, (s+1)*4R); wave w takes slots s*4R + w + 4k,
 // k < R, each one 128-token block, keeping its own online-softmax state; the
-// waves merge through LDS, and with several splits a second kernel merges
-// the splits' (m, l, o) by log-sum-exp. Per block a wave:
+// waves merge through LDS, and with several splits the last split of each
+// (query token, KV head) pair to finish merges the splits' (m, l, o) by
+// log-sum-exp, counted in the workspace. Per block a wave:
 //   1. dequantises the 8 K tiles into FP8 MFMA operands and computes
 //      S = Q K^T with v_mfma_f32_16x16x128_f8f6f4 (A = the 8 query heads of
 //      this KV head, rows 8..15 zero; B = 16 tokens x 128 channels);
@@ -45,29 +46,11 @@ __constant__ Fp8Lut kAttnLut = make_fp8_lut();
 // scores; otherwise the caller's ids are used.
 template <int TOK, bool kSelects>
 __global__ __launch_bounds__(64 * kAttnWaves)
-__attribute__((amdgpu_waves_per_eu(TOK < kBlockTokens ? 3 : 1))) void sparse_attn_kernel(const AttnArgs a) {
+__attribute__((amdgpu_waves_per_eu(TOK < kBlockTokens ? 3 : 2))) void sparse_attn_kernel(const AttnArgs a) {
   constexpr int MODE = kSelects ? kAttnSelect : kAttnIds;
   const int sp = blockIdx.x, kh = blockIdx.y, qt = blockIdx.z;
   const Fp8Lut& lut_src = kAttnLut;
 #include "attn_workgroup.inc"
-}
-
-// Merge kernel: one workgroup per (query token, KV head); thread (h, 4 ch)
-// combines the splits' (m, l, o) by log-sum-exp.
-__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part_o,
-                                                    const float* __restrict__ part_ml,
-                                                    int num_splits, float* __restrict__ out) {
-  const int tid = threadIdx.x;
-  const int64_t row = int64_t(blockIdx.x) * kHeadsPerKv + (tid >> 5);  // query head row
-  const int pd = (tid & 31) * 4;
-  const float* po = part_o + row * num_splits * kHeadDim + pd;
-  const float* pm = part_ml + row * num_splits * 2;
-  *reinterpret_cast<float4*>(out + row * kHeadDim + pd) =
-      merge_row(num_splits, [&](int s, float4& v, float2& ml) {
-        v = *reinterpret_cast<const float4*>(po + s * kHeadDim);
-        ml = *reinterpret_cast<const float2*>(pm + s * 2);
-        return true;
-      });
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -119,7 +102,9 @@ extern "C" size_t msa_attn_workspace_bytes(int32_t num_seqs, int32_t q_per_seq,
   if (plan.splits <= 1) return 0;
   const size_t rows = size_t(num_seqs) * q_per_seq * num_q_heads;
   const size_t splits = size_t(plan.splits);
-  return msa::align256(rows * splits * MSA_HEAD_DIM * 4) + msa::align256(rows * splits * 2 * 4);
+  const size_t pairs = size_t(num_seqs) * q_per_seq * kv_heads;
+  return msa::align256(rows * splits * MSA_HEAD_DIM * 4) + msa::align256(rows * splits * 2 * 4) +
+         msa::align256(pairs * 4);
 }
 
 namespace msa {
@@ -151,7 +136,7 @@ static msa_status check_attn(const msa_pool_desc* kv, const uint8_t* k_codes,
   return MSA_OK;
 }
 
-// Plan, workspace carving and launches (attention, then the split merge).
+// Plan, workspace carving and the launch (the last split of each pair merges).
 template <bool SELECT>
 static msa_status run_attn(AttnArgs a, const msa_pool_desc* kv, int32_t num_seqs,
                            int32_t q_per_seq, int32_t num_q_heads, void* workspace,
@@ -165,11 +150,14 @@ static msa_status run_attn(AttnArgs a, const msa_pool_desc* kv, int32_t num_seqs
     if (!workspace || workspace_bytes < need || misaligned(workspace, 255)) return MSA_ERR_WORKSPACE;
     const size_t rows = size_t(tq) * num_q_heads;
     char* ws = static_cast<char*>(workspace);
+    const size_t o_bytes = align256(rows * a.num_splits * MSA_HEAD_DIM * 4);
     a.part_o = reinterpret_cast<float*>(ws);
-    a.part_ml = reinterpret_cast<float*>(ws + align256(rows * a.num_splits * MSA_HEAD_DIM * 4));
+    a.part_ml = reinterpret_cast<float*>(ws + o_bytes);
+    a.split_cnt = reinterpret_cast<uint32_t*>(ws + o_bytes + align256(rows * a.num_splits * 2 * 4));
   } else {
     a.part_o = nullptr;
     a.part_ml = nullptr;
+    a.split_cnt = nullptr;
   }
   const dim3 grid(a.num_splits, kv->num_heads, unsigned(tq));
   if (plan.tok == kBlockTokens)
@@ -178,13 +166,7 @@ static msa_status run_attn(AttnArgs a, const msa_pool_desc* kv, int32_t num_seqs
   else
     hipLaunchKernelGGL((sparse_attn_kernel<kBlockTokens / kAttnWaves, SELECT>), grid,
                        dim3(64 * kAttnWaves), attn_lds_bytes<kBlockTokens / kAttnWaves>(), s, a);
-  if (hipGetLastError() != hipSuccess) return MSA_ERR_HIP;
-  if (a.num_splits > 1) {
-    hipLaunchKernelGGL(merge_kernel, dim3(unsigned(tq * kv->num_heads)), dim3(256), 0, s,
-                       a.part_o, a.part_ml, a.num_splits, a.out);
-    if (hipGetLastError() != hipSuccess) return MSA_ERR_HIP;
-  }
-  return MSA_OK;
+  return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
 }
 
 static AttnArgs base_args(const msa_pool_desc* kv, const uint8_t* k_codes, const uint8_t* k_scales,

@@ -39,6 +39,8 @@ struct AttnArgs {
   float scale_log2;    // softmax_scale * log2(e)
   float* part_o;       // [T_q * Hq][num_splits][128] unnormalised, when num_splits > 1
   float* part_ml;      // [T_q * Hq][num_splits][2]
+  uint32_t* split_cnt; // [T_q * KV heads] splits arrived, when num_splits > 1 (zero
+                       // between launches: the pair's last split resets it)
   float* out;
 };
 

@@ -180,6 +180,25 @@ __device__ __forceinline__ uint4 load_stream16(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// A buffer descriptor over `bytes` bytes at `base` (gfx9 layout: stride 0,
+// default format word). A buffer load past the record count returns zeros
+// and reads no memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, bytes, 0x00020000);
+}
+
+constexpr int kLoadNonTemporal = 2;  // buffer-load cache policy: streamed, not kept (nt)
+
+// 16 bytes at lane_off + uniform_off of a descriptor's range, non-temporal.
+__device__ __forceinline__ uint4 load_tile16(__amdgpu_buffer_rsrc_t r, uint32_t lane_off, int uniform_off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, uniform_off, kLoadNonTemporal);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+// 4 bytes likewise.
+__device__ __forceinline__ uint32_t load_tile4(__amdgpu_buffer_rsrc_t r, uint32_t lane_off, int uniform_off) {
+  return uint32_t(__builtin_amdgcn_raw_buffer_load_b32(r, lane_off, uniform_off, kLoadNonTemporal));
+}
+
 // ---------------------------------------------------------------- waves
 // Prefix maximum of an unsigned value inside each row of 16 lanes, with DPP
 // row shifts (out-of-row lanes read 0, the identity): lane 15 of a row ends

@@ -9,7 +9,6 @@
 // same time in a given proportion (the read:write mix of a cache writer).
 #include "msa_nvfp4.h"
 #include "nvfp4_tile.h"
-#include "scan_body.h"
 
 namespace msa {
 

@@ -70,20 +70,6 @@ struct TileLoads {
   uint4 s;
 };
 
-// A buffer descriptor over `bytes` bytes at `base` (gfx9 layout: stride 0,
-// default format word). A buffer load past the record count returns zeros
-// and reads no memory.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, bytes, 0x00020000);
-}
-
-constexpr int kLoadNonTemporal = 2;  // buffer-load cache policy: streamed, not kept
-
-__device__ __forceinline__ uint4 load_tile16(__amdgpu_buffer_rsrc_t r, uint32_t lane_off, int uniform_off) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, uniform_off, kLoadNonTemporal);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
 // This wave's loads of one block. `live` (uniform) false stands for an
 // absent block (past the workgroup's count, or an unmapped page): the
 // descriptors then hold no records, every lane receives zeros and nothing is
