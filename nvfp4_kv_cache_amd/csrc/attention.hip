@@ -44,9 +44,13 @@ __constant__ Fp8Lut kAttnLut = make_fp8_lut();
 // One workgroup (attn_workgroup.inc) per (split, KV head, query token).
 // kSelects: the workgroup selects the blocks itself from the indexer's block
 // scores; otherwise the caller's ids are used.
+// Two wavefronts per SIMD (two workgroups per CU), held by the attribute:
+// with one allowed, the compiler moved registers to AGPRs (212 + 36) and
+// workgroups no longer ran two to a CU (measured with per-workgroup time
+// stamps), and the quarter-block form spilled at three.
 template <int TOK, bool kSelects>
 __global__ __launch_bounds__(64 * kAttnWaves)
-__attribute__((amdgpu_waves_per_eu(TOK < kBlockTokens ? 3 : 2))) void sparse_attn_kernel(const AttnArgs a) {
+__attribute__((amdgpu_waves_per_eu(2))) void sparse_attn_kernel(const AttnArgs a) {
   constexpr int MODE = kSelects ? kAttnSelect : kAttnIds;
   const int sp = blockIdx.x, kh = blockIdx.y, qt = blockIdx.z;
   const Fp8Lut& lut_src = kAttnLut;
@@ -64,7 +68,7 @@ inline bool misaligned(const void* p, uintptr_t m) { return (reinterpret_cast<ui
 // at 16, 0.4 us slower at 32 (more workgroups than the chip runs evenly).
 // Otherwise whole blocks per wavefront, R slots per wavefront and
 // ceil(num_sel / 4R) splits per pair. The chip holds kResidentWgs of these
-// workgroups at once (two per CU at the kernel's 183 VGPRs): R = 1, else 2,
+// workgroups at once (two per CU at the kernel's ~210 VGPRs): R = 1, else 2,
 // when that grid fits in one round, otherwise one split per pair (R =
 // ceil(num_sel / 4)), which also needs no merge kernel. Measured at 17
 // slots, us per launch (R = 1 / 2 / 3 / 5): 32 pairs 16.1 / 19.9 / 23.4 /

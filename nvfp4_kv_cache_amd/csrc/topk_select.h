@@ -98,6 +98,22 @@ __device__ __forceinline__ int wave_inclusive_sum(int v, int lane) {
   return v + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
 }
 
+// theta of a selection: the largest x, truncated below bit 11, with at
+// least 16 lanes of the wavefront holding m >= x (radix select on the bit
+// patterns, two bits at a time from the top with three wavefront votes).
+__device__ __forceinline__ uint32_t select_theta(uint32_t m) {
+  uint32_t theta = 0;
+#pragma unroll
+  for (int bit = 29; bit >= 11; bit -= 2) {
+    const uint32_t t1 = theta | (1u << bit), t2 = theta | (2u << bit), t3 = theta | (3u << bit);
+    const int c1 = __popcll(__ballot(m >= t1));
+    const int c2 = __popcll(__ballot(m >= t2));
+    const int c3 = __popcll(__ballot(m >= t3));
+    theta = c3 >= kTopK ? t3 : (c2 >= kTopK ? t2 : (c1 >= kTopK ? t1 : theta));
+  }
+  return theta;
+}
+
 // Selection for one query token with nb visible blocks whose scores are
 // row[0 .. nb-1] (row_len >= nb readable entries); x0 holds chunk 0 as
 // load_score_chunk(row, row_len, 0, lane, x0) returns it. Every lane of the
@@ -171,15 +187,7 @@ __device__ __forceinline__ int select_blocks(const float* row, int row_len, int 
     //    non-negative, so bit 31 is clear. The truncation only admits the
     //    few candidates within ~2^-11 (relative) below the 16th largest; the
     //    exact ranking below sorts them out.
-    uint32_t theta = 0;
-#pragma unroll
-    for (int bit = 29; bit >= 11; bit -= 2) {
-      const uint32_t t1 = theta | (1u << bit), t2 = theta | (2u << bit), t3 = theta | (3u << bit);
-      const int c1 = __popcll(__ballot(m >= t1));
-      const int c2 = __popcll(__ballot(m >= t2));
-      const int c3 = __popcll(__ballot(m >= t3));
-      theta = c3 >= kTopK ? t3 : (c2 >= kTopK ? t2 : (c1 >= kTopK ? t1 : theta));
-    }
+    const uint32_t theta = select_theta(m);
     // 3. compact the candidates reaching theta: a per-lane bit mask of hits,
     //    positions from a prefix sum of its population count, hit values read
     //    back from the LDS copy of the chunk (hits are rare: a lane has 0..2)
@@ -275,6 +283,142 @@ __device__ __forceinline__ int select_blocks(const float* row, int row_len, int 
   }
   *score_out = 0.0f;
   return -1;
+}
+
+// ---------------------------------------------------------------- by W waves
+// The same selection by the W wavefronts of a workgroup together, for a row
+// of one chunk (64 < nb - 1 <= 2,048 candidates): wavefront w holds entries
+// 512 w + 64 k + lane, k < 8, a quarter of the chunk, so the per-entry steps
+// (score bits, lane maxima, hit masks, compaction) cost a quarter each. The
+// union over the wavefronts of a lane's entries is the 32 entries that lane
+// holds in select_blocks, so every wavefront computes the same theta from
+// the combined lane maxima; the candidates of all quarters are compacted
+// into one list and wavefront 0 ranks them exactly. More than 64
+// candidates (many equal scores): wavefront 0 runs select_blocks on the
+// whole chunk instead. Same result as select_blocks for the same row.
+constexpr int kSelWaves = 4;
+constexpr int kSelPerLaneWg = kSelPerLane / kSelWaves;  // 8 entries per lane
+constexpr int kSelDirect = 64;  // at most this many candidates: ranked directly
+
+struct __align__(16) SelectScratchWg {
+  uint32_t lane_max[kSelWaves][64];
+  int32_t wave_hits[kSelWaves];
+  uint64_t cand[64];
+  uint64_t win[kTopK];
+  int32_t id[kTopK + 1];
+  int32_t page[kTopK + 1];
+};
+
+// Wavefront w's quarter of a row's first chunk: lane l gets entries
+// 512 w + 64 k + l (buffer loads over the row, entries past it read 0).
+__device__ __forceinline__ void load_score_quarter(const float* row, int row_len, int wave, int lane,
+                                                   float (&x)[kSelPerLaneWg]) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(row), 0, row_len * int(sizeof(float)), 0x00020000);
+  const uint32_t off = uint32_t(wave * (kSelChunk / kSelWaves) + lane) * uint32_t(sizeof(float));
+#pragma unroll
+  for (int k = 0; k < kSelPerLaneWg; ++k)
+    x[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                         r, off, 64 * k * int(sizeof(float)), 0));
+}
+
+// Every thread of the workgroup calls it (it holds workgroup barriers), with
+// the same nb. xq: this wavefront's quarter (load_score_quarter). sc and
+// full: LDS scratch of the workgroup (full for the many-equal-scores case).
+// Lane l <= 16 of every wavefront receives the block of selected slot l and
+// its table entry (*page_out, unchecked), as select_blocks returns them.
+__device__ __forceinline__ int select_blocks_wg(const float* row, int row_len, int nb,
+                                                const float (&xq)[kSelPerLaneWg],
+                                                SelectScratchWg& sc, SelectScratch& full,
+                                                int wave, int lane, const int32_t* table_row,
+                                                int* page_out) {
+  const int n = nb - 1;  // candidates; the recent block is always kept
+  const int base = wave * (kSelChunk / kSelWaves);
+  uint32_t v[kSelPerLaneWg];
+  uint32_t m = 0;
+#pragma unroll
+  for (int k = 0; k < kSelPerLaneWg; ++k) {
+    v[k] = base + 64 * k + lane < n ? score_bits(xq[k]) : 0u;
+    m = max(m, v[k]);
+  }
+  sc.lane_max[wave][lane] = m;
+  __syncthreads();
+  uint32_t mm = 0;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) mm = max(mm, sc.lane_max[w][lane]);
+  const uint32_t theta = select_theta(mm);
+  uint32_t hits = 0;
+#pragma unroll
+  for (int k = 0; k < kSelPerLaneWg; ++k)
+    hits |= (base + 64 * k + lane < n && v[k] >= theta) ? (1u << k) : 0u;
+  const int mine = __popc(hits);
+  const int incl = wave_inclusive_sum(mine, lane);
+  if (lane == 63) sc.wave_hits[wave] = incl;
+  __syncthreads();
+  int before = 0, cnt = 0;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    const int c = sc.wave_hits[w];
+    before += w < wave ? c : 0;
+    cnt += c;
+  }
+  cnt = __builtin_amdgcn_readfirstlane(cnt);  // uniform
+  if (cnt <= kSelDirect) {
+    int pos = before + incl - mine;
+    while (hits) {
+      const int k = __builtin_ctz(hits);
+      hits &= hits - 1;
+      uint32_t bits = v[0];
+#pragma unroll
+      for (int i = 1; i < kSelPerLaneWg; ++i) bits = k == i ? v[i] : bits;
+      sc.cand[pos++] = make_key(bits, base + 64 * k + lane);
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    if (cnt <= kSelDirect) {
+      // rank by counting against the other candidates, read from their
+      // lanes; the candidates' pages are in flight meanwhile
+      const uint64_t key = lane < cnt ? sc.cand[lane] : 0ull;
+      const int cpage = (table_row && lane < cnt) ? table_row[key_block_id(key)] : -1;
+      const uint32_t klo = uint32_t(key), khi = uint32_t(key >> 32);
+      int r = 0;
+      for (int s = 0; s < cnt; ++s) {
+        const uint64_t o = (uint64_t(uint32_t(__builtin_amdgcn_readlane(int(khi), s))) << 32) |
+                           uint32_t(__builtin_amdgcn_readlane(int(klo), s));
+        r += o > key ? 1 : 0;
+      }
+      const bool won = lane < cnt && r < kTopK;
+      if (won) sc.win[r] = key;
+      wave_lds_sync();
+      // each winner finds its place in ascending block order
+      if (won) {
+        const int id = key_block_id(key);
+        int order = 0;
+#pragma unroll
+        for (int i = 0; i < kTopK; ++i) order += key_block_id(sc.win[i]) < id ? 1 : 0;
+        sc.id[order] = id;
+        sc.page[order] = cpage;
+      }
+      if (lane == kTopK) {
+        sc.id[kTopK] = nb - 1;
+        sc.page[kTopK] = table_row ? table_row[nb - 1] : -1;
+      }
+    } else {
+      float x0[kSelPerLane];
+      load_score_chunk(row, row_len, 0, lane, x0);
+      float score;
+      int page = -1;
+      const int id = select_blocks(row, row_len, nb, x0, full, lane, &score, table_row, &page);
+      if (lane <= kTopK) {
+        sc.id[lane] = id;
+        sc.page[lane] = page;
+      }
+    }
+  }
+  __syncthreads();
+  *page_out = lane <= kTopK ? sc.page[lane] : -1;
+  return lane <= kTopK ? sc.id[lane] : -1;
 }
 
 }  // namespace msa
