@@ -58,8 +58,8 @@ struct WaveLds {
   static constexpr int kP = TOK * kHeadsPerKv;
   static constexpr int kBytes = kV + 2 * kP;
 };
-constexpr float kPScale = 256.0f;                     // P_hi = FP8(256 p)
-constexpr float kPLoScale = 16.0f;                    // P_lo = FP8(16 (256 p - P_hi))
+constexpr float kPScaleLog2 = 8.0f;                   // P_hi = FP8(2^8 p)
+constexpr float kPLoScale = 16.0f;                    // P_lo = FP8(16 (2^8 p - P_hi))
 constexpr int kE8M0One = 0x7F7F7F7F;                  // MFMA operand scale 2^0
 constexpr int kE8M0Sixteenth = 0x7B7B7B7B;            // MFMA operand scale 2^-4
 constexpr int kFp8Ones = 0x38383838;                  // four FP8 E4M3 1.0
