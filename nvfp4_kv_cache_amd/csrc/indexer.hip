@@ -171,10 +171,14 @@ __device__ __forceinline__ void shared_workgroup(const IndexerArgs& a, int j, in
 }
 
 // QG: 16-row MFMA groups per index head = ceil(8 * q_per_seq / 16).
-// Grid (G, shared_rows + num_seqs): the first shared_rows rows are the
-// shared-prefix workgroups (row-major over (group, block)), dispatched first
-// so that they run beside the regular scan; row shared_rows + b holds the G
-// scan workgroups of sequence b.
+// Grid (G, shared_rows + num_seqs + tail_rows): the first shared_rows rows
+// are the shared-prefix workgroups (row-major over (group, block)),
+// dispatched first so that they run beside the regular scan; row
+// shared_rows + b holds the G scan workgroups of sequence b (blocks
+// x + G k below tail_first); the last tail_rows rows hold one workgroup per
+// remaining block (sequence-major). Workgroups are dispatched in grid order,
+// so the short one-block workgroups run last and the chip drains in about
+// one block's time instead of one regular workgroup's.
 // One block in flight per wave: the next block's loads are issued as soon as
 // the current block's codes are consumed, and more resident waves hide the
 // latency better than a second register buffer would (measured with 1 and 8
@@ -196,7 +200,18 @@ __global__ __launch_bounds__(512) void indexer_kernel(const IndexerArgs a) {
     }
     y -= a.shared_rows;
   }
-  scan_workgroup<QG, false>(a, blockIdx.x, gridDim.x, y, kIdxLut, part, lut, list);
+  if (y >= a.num_seqs) {
+    // the trailing one-block workgroups (uniform over the workgroup)
+    const int per_seq = a.max_blocks - a.tail_first;
+    const int u = (y - a.num_seqs) * int(gridDim.x) + int(blockIdx.x);
+    const int b = u / per_seq;
+    if (b >= a.num_seqs) return;
+    scan_workgroup<QG, false>(a, a.tail_first + (u - b * per_seq), 1, 1, b, kIdxLut, part, lut,
+                              list);
+    return;
+  }
+  scan_workgroup<QG, false>(a, blockIdx.x, gridDim.x, a.blocks_per_wg, y, kIdxLut, part, lut,
+                            list);
 }
 
 // Selection kernel: one wavefront per query token (topk_select.h).
@@ -262,6 +277,40 @@ struct SharedGroups {
   int max_group_blocks = 0;
 };
 
+// Workgroups of a scan kernel the chip holds at once (occupancy per CU x
+// CUs), looked up once per device and kernel form; 0 if unknown.
+template <int QG, bool SHARED>
+static int64_t resident_of(int threads, size_t lds) {
+  int dev = -1, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, indexer_kernel<QG, SHARED>, threads,
+                                                   lds) != hipSuccess)
+    return 0;
+  return int64_t(per_cu) * cus;
+}
+static int64_t scan_resident_wgs(int qg_pow2, bool shared, int threads, size_t lds) {
+  constexpr int kDevs = 64;
+  static std::atomic<int64_t> cache[kDevs][3][2][MSA_MAX_HEADS + 1];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) return 0;
+  const int qi = qg_pow2 == 1 ? 0 : (qg_pow2 == 2 ? 1 : 2);
+  const int h = threads / 64;
+  if (h < 1 || h > MSA_MAX_HEADS) return 0;
+  std::atomic<int64_t>& slot = cache[dev][qi][shared ? 1 : 0][h];
+  int64_t r = slot.load(std::memory_order_relaxed);
+  if (r > 0) return r;
+  if (qi == 0)
+    r = shared ? resident_of<1, true>(threads, lds) : resident_of<1, false>(threads, lds);
+  else if (qi == 1)
+    r = shared ? resident_of<2, true>(threads, lds) : resident_of<2, false>(threads, lds);
+  else
+    r = shared ? resident_of<4, true>(threads, lds) : resident_of<4, false>(threads, lds);
+  if (r > 0) slot.store(r, std::memory_order_relaxed);
+  return r;
+}
+
 static msa_status launch_scan(const msa_pool_desc* idx, const uint8_t* idx_codes,
                               const uint8_t* idx_scales, const uint8_t* q_fp8, const float* head_w,
                               int32_t num_q_heads, const int32_t* block_table, int32_t max_blocks,
@@ -289,17 +338,32 @@ static msa_status launch_scan(const msa_pool_desc* idx, const uint8_t* idx_codes
   a.num_groups = shared ? sg.num_groups : 0;
   a.max_group_blocks = shared ? sg.max_group_blocks : 1;
   const int qg = (MSA_HEADS_PER_KV * q_per_seq + 15) / 16;
+  const int qg_pow2 = qg == 1 ? 1 : (qg == 2 ? 2 : 4);
+  const size_t lds = size_t(2) * idx->num_heads * (2 * qg_pow2) * MSA_BLOCK_TOKENS * sizeof(float);
+  const dim3 block(64 * idx->num_heads);
   const int bpw = scan_blocks_per_wg(num_seqs, max_blocks, qg);
   a.blocks_per_wg = bpw;
-  const int gx = (max_blocks + bpw - 1) / bpw;
+  // one-block workgroups for the last blocks of every sequence, about one
+  // chip's worth of resident workgroups in all, when the regular grid takes
+  // several rounds of the chip
+  int gx = (max_blocks + bpw - 1) / bpw;
+  a.tail_first = max_blocks;
+  a.tail_rows = 0;
+  const int64_t resident = scan_resident_wgs(qg_pow2, shared, int(block.x), lds);
+  if (bpw > 1 && resident > 0 && int64_t(num_seqs) * gx > 2 * resident) {
+    const int64_t tail = std::min<int64_t>((resident + num_seqs - 1) / num_seqs, max_blocks / 2);
+    const int g1 = int((max_blocks - tail + bpw - 1) / bpw);
+    if (int64_t(g1) * bpw < max_blocks) {
+      gx = g1;
+      a.tail_first = g1 * bpw;
+      a.tail_rows = int((int64_t(num_seqs) * (max_blocks - a.tail_first) + gx - 1) / gx);
+    }
+  }
   // the shared-prefix workgroups fill whole leading rows of the grid
   const int64_t shared_wgs = int64_t(a.num_groups) * a.max_group_blocks;
   a.shared_rows = int((shared_wgs + gx - 1) / gx);
-  if (int64_t(num_seqs) + a.shared_rows > 65535) return MSA_ERR_UNSUPPORTED;
-  const dim3 grid(gx, num_seqs + a.shared_rows);
-  const dim3 block(64 * idx->num_heads);
-  const int qg_pow2 = qg == 1 ? 1 : (qg == 2 ? 2 : 4);
-  const size_t lds = size_t(2) * idx->num_heads * (2 * qg_pow2) * MSA_BLOCK_TOKENS * sizeof(float);
+  if (int64_t(num_seqs) + a.shared_rows + a.tail_rows > 65535) return MSA_ERR_UNSUPPORTED;
+  const dim3 grid(gx, num_seqs + a.shared_rows + a.tail_rows);
   if (shared) {
     if (qg_pow2 == 1)
       hipLaunchKernelGGL((indexer_kernel<1, true>), grid, block, lds, s, a);

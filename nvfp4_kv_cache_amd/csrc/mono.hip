@@ -202,8 +202,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     __shared__ ScanList list;
     const int b = id / m.scan_per_seq;
     const int x = id - b * m.scan_per_seq;
-    scan_workgroup<QG, true>(m.s, x, m.scan_per_seq, b, kMonoLut, reinterpret_cast<float*>(smem),
-                             lut, list);
+    scan_workgroup<QG, true>(m.s, x, m.scan_per_seq, m.s.blocks_per_wg, b, kMonoLut,
+                             reinterpret_cast<float*>(smem), lut, list);
     arrive(m.scan_cnt + int64_t(b) * kCountWords, x);
   } else if (id < m.n_scan + m.n_block) {
     const int u = id - m.n_scan;

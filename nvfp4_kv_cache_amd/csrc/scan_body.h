@@ -41,6 +41,11 @@ struct IndexerArgs {
   int num_groups;
   int max_group_blocks;         // >= every group_blocks entry, <= max_blocks
   int shared_rows;              // leading grid rows of shared-prefix workgroups
+  // trailing rows of one-block workgroups: blocks tail_first .. max_blocks-1
+  // of every sequence (tail_rows 0: none; the regular workgroups then cover
+  // every block)
+  int tail_first;
+  int tail_rows;
 };
 
 constexpr int kMaxBlocksPerWg = 8;  // blocks per scan workgroup (page list size)
@@ -141,14 +146,15 @@ inline int scan_blocks_per_wg(int64_t num_seqs, int64_t max_blocks, int qg) {
   return bpw;
 }
 
-// Workgroup x of the G scan workgroups of sequence b, one wavefront per
-// index-key head. LDS from the caller: part = [2][H][2*QG][128] floats,
-// lut = 128 table rows, the block list. COHERENT: the block scores are
-// stored at device scope (write-through), for a consumer in the same launch.
+// One scan workgroup of sequence b, one wavefront per index-key head: the
+// blocks x, x + G, x + 2G, ... (at most `count`, below the sequence's last
+// block). LDS from the caller: part = [2][H][2*QG][128] floats, lut = 128
+// table rows, the block list. COHERENT: the block scores are stored at
+// device scope (write-through), for a consumer in the same launch.
 template <int QG, bool COHERENT>
-__device__ __forceinline__ void scan_workgroup(const IndexerArgs& a, int x, int G, int b,
-                                               const Fp8Lut& lut_src, float* part, uint2* lut,
-                                               ScanList& list) {
+__device__ __forceinline__ void scan_workgroup(const IndexerArgs& a, int x, int G, int count,
+                                               int b, const Fp8Lut& lut_src, float* part,
+                                               uint2* lut, ScanList& list) {
 
   const int H = a.num_heads;
   const int Q = a.q_per_seq;
@@ -162,11 +168,11 @@ __device__ __forceinline__ void scan_workgroup(const IndexerArgs& a, int x, int 
   const int L = a.seq_lens[b];
   const bool seq_ok = L >= Q && L <= a.max_blocks * kBlockTokens;
   const int nb_last = seq_ok ? (L - 1) / kBlockTokens + 1 : 0;
-  // workgroup x of a sequence takes blocks x, x + G, x + 2G, ... (G = grid
-  // width), so the workgroups running at any moment read neighbouring pages;
-  // a block of a shared prefix whose page is the group lead's is left to the
-  // shared pass. Wave 0 builds the list (at most 8 blocks, one lane each).
-  const int total = nb_last > x ? min(a.blocks_per_wg, (nb_last - x + G - 1) / G) : 0;
+  // neighbouring workgroups take neighbouring blocks (x, x + 1, ...), so
+  // the workgroups running at any moment read neighbouring pages; a block
+  // of a shared prefix whose page is the group lead's is left to the shared
+  // pass. Wave 0 builds the list (at most 8 blocks, one lane each).
+  const int total = nb_last > x ? min(count, (nb_last - x + G - 1) / G) : 0;
   const int64_t qrow0 = int64_t(b) * Q;
   const int Hq = a.num_q_heads;
   if (threadIdx.x < 64) {
