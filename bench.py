@@ -5,7 +5,8 @@
 One step = one decode step of one layer: msa_indexer_scan (scan the whole
 NVFP4 index cache of every sequence and score its blocks), then
 msa_sparse_attn_select_decode (select top-16 + recent blocks per query token
-and run exact attention over them, in one launch plus the split merge).
+and run exact attention over them, in one launch: the last split of each
+(query token, KV head) pair merges the splits' partials).
 Inputs are synthetic and already resident in HBM (seeded generator, cache
 written by msa_nvfp4_quantize) before the timed region starts.
 
@@ -25,7 +26,7 @@ its own JSON line in the same form.
 
 benchmarks the one-launch decode step for low concurrency (msa_decode_mono:
 scan, selection and attention in one kernel) on the 1 x 4,096-token
-workload against the three-kernel step, with a sweep of small batches, and
+workload against the two-launch step, with a sweep of small batches, and
 prints its own JSON line in the same form.
 """
 from __future__ import annotations
@@ -56,7 +57,7 @@ def parse():
     p.add_argument("--mono", action="store_true",
                    help="benchmark the one-launch decode step (msa_decode_mono) on the "
                         "1 x 4,096-token workload (or --workload), against the "
-                        "three-kernel step, plus a sweep of small batches; prints its own "
+                        "two-launch step, plus a sweep of small batches; prints its own "
                         "JSON line")
     p.add_argument("--workload", type=int, default=None,
                    help="workload index (0..4); 2 = 8 x 262,144 tokens")
@@ -534,7 +535,7 @@ def insert_bench(args):
 
 def mono_bench(args):
     """msa_decode_mono (one launch) against msa_indexer_scan +
-    msa_sparse_attn_select_decode (the three-kernel step) on one workload
+    msa_sparse_attn_select_decode (the two-launch step) on one workload
     (default: 1 x 4,096 tokens, 1 query token), plus a sweep of small
     batches; same JSON contract as the decode benchmark."""
     import numpy as np
@@ -640,7 +641,7 @@ def mono_bench(args):
         sweep.append({"workload": w2.name, "num_seqs": len(lens), "context_tokens": lens[0],
                       "q_per_seq": q,
                       "mono_us": round(wall_us(r2["mono"], args.steps), 2),
-                      "three_kernel_us": round(wall_us(r2["three"], args.steps), 2)})
+                      "two_launch_us": round(wall_us(r2["three"], args.steps), 2)})
         del r2
     res = {
         "metric": "decode query-tokens/s + achieved HBM GB/s (indexer+sparse-attn, 1 layer)",
@@ -668,11 +669,11 @@ def mono_bench(args):
         "hbm_frac_of_peak": round(step_bytes / (us_mono * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": int(step_bytes),
         "kv_bytes_read_per_step": int(kv_read),
-        "three_kernel_us_per_step": round(us_three, 2),
-        "speedup_vs_three_kernel": round(us_three / us_mono, 3),
-        "bit_identical_to_three_kernel": bool(same),
+        "two_launch_us_per_step": round(us_three, 2),
+        "speedup_vs_two_launch": round(us_three / us_mono, 3),
+        "bit_identical_to_two_launch": bool(same),
         "kernels_us": {"msa_decode_mono": round(ev_mono, 2),
-                       "three_kernel_step_events": round(ev_three, 2)},
+                       "two_launch_step_events": round(ev_three, 2)},
         "sweep": sweep,
         "roofline": {"bound": "hbm", "kernel": "mono_kernel (msa_decode_mono)",
                      "achieved": round(step_bytes / (ev_mono * 1e-6) / 1e9, 1),
@@ -756,7 +757,7 @@ def main():
 
     def step():
         # the whole hot path: index scan (scores), then selection + sparse
-        # attention in one launch (plus the split merge)
+        # attention in one launch (the last split of each pair merges)
         scan()
         select_attend()
 
@@ -816,7 +817,7 @@ def main():
     p10, p90 = (float(x) for x in np.percentile(step_us, [10, 90]))
     if not (torch.equal(out, eager_out) and torch.equal(ids, eager_ids)):
         raise RuntimeError("cold steps differ from the warm-up step")
-    # cold stage split: the scan, then selection + attention (+ split merge),
+    # cold stage split: the scan, then selection + attention (merge included),
     # with the extra event between them
     ev = cold_steps(max(args.steps, 50), True)
     scan_us = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3

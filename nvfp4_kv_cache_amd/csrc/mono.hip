@@ -8,9 +8,9 @@
 // system results separate").
 //
 // A small step is latency-bound: every stage is a chain of dependent memory
-// round trips, and the three-kernel path (scan, selection + attention, split
-// merge) runs them back to back. Here the attention does not wait for the
-// selection. One 1-D grid holds three kinds of workgroup, in this order:
+// round trips, and the two-launch path (scan, then selection + attention
+// with the split merge) runs them back to back. Here the attention does not
+// wait for the selection. One 1-D grid holds three kinds of workgroup, in this order:
 //   1. scan workgroups (scan_body.h), scan_per_seq per sequence, which store
 //      their block scores at device scope and count themselves in the
 //      sequence's arrival counter;
@@ -30,7 +30,7 @@
 // is why the entry point bounds the grid (low concurrency, short contexts:
 // query tokens x 4 KV heads x max_blocks <= 1,024).
 //
-// The values are those of the three-kernel path: the scan and the block
+// The values are those of the two-launch path: the scan and the block
 // partials are the same code, the selection sees the same scores, and the
 // merge combines the same partials in the same order, so the ids and the
 // output match msa_indexer_scan + msa_sparse_attn_select_decode bit for bit

@@ -87,9 +87,9 @@ def _check(nb, wl, bitwise):
         torch.cuda.synchronize()
         rid, ro = ref["ids"].cpu().numpy(), ref["o"].cpu().numpy()
         tq = wl.num_q_tokens
-        assert np.array_equal(ids, rid), "ids differ from the three-kernel path"
+        assert np.array_equal(ids, rid), "ids differ from the two-launch path"
         assert np.array_equal(o.view(np.uint32), ro.view(np.uint32)), \
-            "output bits differ from the three-kernel path"
+            "output bits differ from the two-launch path"
         assert tq * 4 * (wl.topk + 1) <= 384
     fails = []
     sc = _selected_scores(ids, bsc)
@@ -163,7 +163,7 @@ def test_mono_repeated_calls_and_counters(nb):
 
 
 def test_mono_invalid_lengths_and_pages(nb):
-    say("mono invalid lengths / page ids vs the three-kernel path")
+    say("mono invalid lengths / page ids vs the two-launch path")
     wl = tiny_config([3000, 2500, 2600, 2700], 1, seed=8)
     pools = S.fill_pools(wl, nb)
     inp = S.device_inputs(wl)
@@ -187,7 +187,7 @@ def test_mono_invalid_lengths_and_pages(nb):
 
 def test_mono_full_size_tiny_workload(nb):
     """The 1 x 4,096-token workload at its real size, in the launch bench.py
-    --mono times: bit-identical to the three-kernel step, oracle-checked."""
+    --mono times: bit-identical to the two-launch step, oracle-checked."""
     wl = get_config(0)
     say(f"mono on {wl.name}")
     fails, _ = _check(nb, wl, True)
@@ -198,7 +198,7 @@ def test_mono_many_equal_scores(nb):
     """1 x 16K where 120 of the 127 candidate blocks alias one physical page,
     so more than 64 candidates tie at the threshold and the selection ranks
     them by arg-max rounds on device-scope loads: the lowest aliased blocks
-    win the ties, bit-identical to the three-kernel path."""
+    win the ties, bit-identical to the two-launch path."""
     say("mono with 120 tied candidates (aliased page)")
     wl = tiny_config([16384], 1, seed=91, spare_pages=0, permute=False)
     bt = wl.block_table
