@@ -642,6 +642,42 @@ def test_shared_prefix_scan_without_groups_is_plain_scan(nb):
     assert torch.equal(ref.view(torch.int32), got.view(torch.int32))
 
 
+@pytest.mark.parametrize("q", [1, 2])
+def test_scan_scores_independent_of_grid(nb, q):
+    """The block scores of a batch large enough for the scan grid's trailing
+    one-block workgroups (44 sequences of up to 256 blocks: 44 x 86 regular
+    workgroups, more than two rounds of the chip) equal, bit for bit, those
+    of scanning each sequence alone (a one-sequence grid of 86 workgroups,
+    no trailing rows): every block is scored once, by the same arithmetic,
+    whichever workgroup takes it."""
+    lens = [32768 - 97 * b for b in range(44)]
+    say(f"scan scores independent of the grid, 44 sequences up to 32K, q={q}")
+    wl = tiny_config(lens, q, seed=90 + q, spare_pages=3, permute=True)
+    pools = S.fill_pools(wl, nb)
+    inp = S.device_inputs(wl)
+    ic, isc = pools[synth.STREAM_IDX]
+    tq = wl.num_q_tokens
+    whole = torch.full((tq, wl.max_blocks), -3.0, dtype=torch.float32, device="cuda")
+    nb.msa_indexer_scan(ic, isc, inp["q_idx"], inp["w"], inp["block_table"], inp["seq_lens"], q,
+                        whole)
+    alone = torch.full_like(whole, -3.0)
+    hq = wl.num_q_heads
+    for b in range(wl.num_seqs):
+        rows = slice(b * q, (b + 1) * q)
+        nb.msa_indexer_scan(ic, isc, inp["q_idx"][rows].contiguous(), inp["w"][rows].contiguous(),
+                            inp["block_table"][b:b + 1].contiguous(),
+                            inp["seq_lens"][b:b + 1].contiguous(), q, alone[rows])
+    torch.cuda.synchronize()
+    assert inp["q_idx"].shape[1] == hq
+    assert torch.equal(whole.view(torch.int32), alone.view(torch.int32))
+    # every visible block has a score; nothing past the visible blocks is written
+    bs = whole.cpu().numpy()
+    for b in range(wl.num_seqs):
+        for i, pos in enumerate(wl.positions(b)):
+            nbk = pos // 128 + 1
+            assert np.all(bs[b * q + i, :nbk] >= 0) and np.all(bs[b * q + i, nbk:] == -3.0)
+
+
 # msa_sparse_attn_decode with the caller's selection and num_sel from 1 to
 # 64 slots, through each form of the launch plan: one workgroup per slot
 # (the four wavefronts share each block) while pairs x num_sel <= 384, else
