@@ -1,5 +1,5 @@
 """Pins of the attention acceptance rule (oracle.acceptance.check_attention):
-every attention verdict of the GPU parity tests passes through it, so each
+every attention decision of the GPU parity tests passes through it, so each
 plausible slip in it (one bar instead of both, a signed instead of an
 absolute error, a NaN that compares false, a broadcast between mismatched
 shapes) must fail one of these.
