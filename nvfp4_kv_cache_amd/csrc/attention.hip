@@ -66,18 +66,23 @@ inline bool misaligned(const void* p, uintptr_t m) { return (reinterpret_cast<ui
 // serial work per wavefront is a quarter block. Measured against whole
 // blocks per wavefront at 17 slots: 2.3 us faster per step at 4 pairs, 1.5 us
 // at 16, 0.4 us slower at 32 (more workgroups than the chip runs evenly).
-// Otherwise whole blocks per wavefront, R slots per wavefront and
+// Otherwise whole blocks per wavefront: R slots per wavefront and
 // ceil(num_sel / 4R) splits per pair. The chip holds kResidentWgs of these
-// workgroups at once (two per CU at the kernel's ~210 VGPRs): R = 1, else 2,
-// when that grid fits in one round, otherwise one split per pair (R =
-// ceil(num_sel / 4)), which also needs no merge kernel. Measured at 17
-// slots, us per launch (R = 1 / 2 / 3 / 5): 32 pairs 16.1 / 19.9 / 23.4 /
-// 27.3; 96 pairs 19.9 / 24.3 / 23.7 / 27.6; 160 pairs 30.4 / 25.2 / 29.8 /
-// 27.8; 192 pairs 31.8 / 31.3 / 30.1 / 28.1; 512 pairs 70.0 / 59.6 / 54.7 /
-// 39.9; a grid of at most 1,024 workgroups, the earlier rule, took R = 3 at
-// 512 pairs.
+// workgroups at once (two per CU at the kernel's ~210 VGPRs). Among the R
+// whose grid fits in one round, the one with the shortest chain wins: R
+// blocks per wavefront at ~3 time units each with one workgroup per CU
+// (a wavefront alone on its SIMD; phase stamps: ~3.2 us per block) or ~5
+// with two (two wavefronts share a SIMD: ~5.5 us), plus ~1.5 for the split
+// merge; ties go to fewer splits. When none fits, one split per pair (R =
+// ceil(num_sel / 4)). Measured at 17 slots, us per launch (R = 1 / 2 / 3 /
+// 5): 32 pairs 15.3 / 17.9 / - / -; 128 pairs 27.9 / 23.4 / 22.0 / 23.9;
+// 180 pairs - / 29.5 / 27.6 / 24.4; 512 pairs - / - / 51.7 / 38.9; and
+// with an earlier build 96 pairs 19.9 / 24.3 / 23.7 / 27.6, 160 pairs
+// 30.4 / 25.2 / 29.8 / 27.8, 192 pairs 31.8 / 31.3 / 30.1 / 28.1: the rule
+// picks the fastest in each.
 constexpr int64_t kSharedMaxWgs = 384;
 constexpr int64_t kResidentWgs = 512;
+constexpr int64_t kCUs = kResidentWgs / 2;
 struct AttnPlan {
   int tok;           // tokens of a block per wavefront: 32 or 128
   int slots_per_wg;  // selected slots per workgroup
@@ -86,11 +91,18 @@ struct AttnPlan {
 inline AttnPlan attn_plan(int64_t pairs, int num_sel) {
   if (pairs * num_sel <= kSharedMaxWgs) return AttnPlan{kBlockTokens / kAttnWaves, 1, num_sel};
   auto splits = [&](int r) { return (num_sel + kAttnWaves * r - 1) / (kAttnWaves * r); };
-  int R = (num_sel + kAttnWaves - 1) / kAttnWaves;  // one split
-  if (pairs * splits(1) <= kResidentWgs)
-    R = 1;
-  else if (pairs * splits(2) <= kResidentWgs)
-    R = 2;
+  const int r_max = (num_sel + kAttnWaves - 1) / kAttnWaves;  // one split
+  int R = r_max;
+  int64_t best = -1;
+  for (int r = 1; r <= r_max; ++r) {
+    const int64_t wgs = pairs * splits(r);
+    if (wgs > kResidentWgs) continue;
+    const int64_t cost = int64_t(r) * (wgs <= kCUs ? 30 : 50) + (splits(r) > 1 ? 15 : 0);
+    if (best < 0 || cost < best || (cost == best && splits(r) < splits(R))) {
+      best = cost;
+      R = r;
+    }
+  }
   return AttnPlan{kBlockTokens, kAttnWaves * R, splits(R)};
 }
 

@@ -156,11 +156,11 @@ def test_attention_launch_forms(nb, nseq):
         assert not fails, "\n".join(fails[:20])
 
 
-# With whole blocks per wavefront the plan takes 1 or 2 slots per wavefront
-# while the grid fits the 512 workgroups the chip holds at once, else one
-# split per (query token, KV head) pair, written without the merge kernel:
-# 160 pairs run 2 slots per wavefront (3 splits), 192 pairs and 8 x 8 query
-# tokens (256 pairs) one split.
+# With whole blocks per wavefront the plan takes the number of slots per
+# wavefront with the shortest chain among the grids that fit the 512
+# workgroups the chip holds at once, else one split per (query token, KV
+# head) pair, written directly: 160 pairs run 2 slots per wavefront (3
+# splits), 192 pairs and 8 x 8 query tokens (256 pairs) one split.
 @pytest.mark.parametrize("nseq,q", [(40, 1), (48, 1), (8, 8)],
                          ids=["2-slots-3-splits", "one-split", "one-split-q8"])
 def test_attention_plan_many_pairs(nb, nseq, q):
@@ -681,9 +681,9 @@ def test_scan_scores_independent_of_grid(nb, q):
 # msa_sparse_attn_decode with the caller's selection and num_sel from 1 to
 # 64 slots, through each form of the launch plan: one workgroup per slot
 # (the four wavefronts share each block) while pairs x num_sel <= 384, else
-# whole blocks per wavefront with 1 or 2 slots per wavefront and the split
-# merge, or one split per pair written directly. (num_sel, lengths, query
-# tokens per sequence, plan exercised.)
+# whole blocks per wavefront with R slots per wavefront and the split merge,
+# or one split per pair written directly. (num_sel, lengths, query tokens
+# per sequence, plan exercised.)
 def _numsel_lens(n, lo, hi, seed):
     return [int(x) for x in np.random.default_rng(seed).integers(lo, hi, size=n)]
 
@@ -695,12 +695,13 @@ NUMSEL = [
     (5, _numsel_lens(25, 1000, 3000, 2), 1, "whole blocks, 2 splits"),
     (33, [5000, 4000], 1, "shared-block waves, 33 partials merged"),
     (33, [5000, 4000, 3000], 1, "whole blocks, 9 splits"),
-    (33, _numsel_lens(16, 4300, 6000, 3), 1, "whole blocks, 2 slots per wave, 5 splits"),
+    (33, _numsel_lens(16, 4300, 6000, 3), 1, "whole blocks, 3 slots per wave, 3 splits"),
     (33, [5000, 4300], 4, "whole blocks, 9 splits, 4 query tokens"),
     (64, [9000], 1, "shared-block waves, 64 partials merged"),
     (64, [9000, 8500], 1, "whole blocks, 16 splits"),
     (64, _numsel_lens(12, 8300, 9500, 4), 1, "whole blocks, 2 slots per wave, 8 splits"),
-    (64, _numsel_lens(40, 8300, 9000, 5), 1, "whole blocks, one split of 16 slots per wave"),
+    (64, _numsel_lens(40, 8300, 9000, 5), 1, "whole blocks, 6 slots per wave, 3 splits"),
+    (64, _numsel_lens(96, 8300, 9000, 6), 1, "whole blocks, one split of 16 slots per wave"),
 ]
 
 

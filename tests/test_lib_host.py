@@ -43,20 +43,29 @@ def test_status_strings(L):
 def _attn_splits(pairs, num_sel):
     # the launch plan: few (query token, KV head) pairs -> one workgroup per
     # selected block; otherwise one block per wavefront (4 per workgroup),
-    # 1 or 2 slots per wavefront while the grid fits the 512 workgroups the
-    # chip holds at once, else one split per pair
+    # R slots per wavefront, the R whose grid fits the 512 workgroups the
+    # chip holds at once with the shortest chain (R blocks at 3 units with
+    # at most one workgroup per CU, 5 with two, + 1.5 for a split merge;
+    # ties to fewer splits), else one split per pair
     if pairs * num_sel <= 384:
         return num_sel
-    for r in (1, 2):
-        if pairs * -(-num_sel // (4 * r)) <= 512:
-            return -(-num_sel // (4 * r))
-    return 1
+    sp = lambda r: -(-num_sel // (4 * r))
+    best = None
+    for r in range(1, -(-num_sel // 4) + 1):
+        wgs = pairs * sp(r)
+        if wgs > 512:
+            continue
+        cost = r * (30 if wgs <= 256 else 50) + (15 if sp(r) > 1 else 0)
+        if best is None or (cost, sp(r)) < best:
+            best = (cost, sp(r))
+    return best[1] if best else 1
 
 
 @pytest.mark.parametrize("seqs,q,heads,sel", [(16, 8, 32, 17), (8, 1, 32, 17), (32, 1, 32, 17),
                                               (1, 1, 32, 17), (2, 1, 8, 64), (45, 1, 32, 17),
                                               (24, 1, 32, 17), (40, 1, 32, 17), (48, 1, 32, 17),
-                                              (96, 1, 32, 17), (4, 1, 32, 64)])
+                                              (96, 1, 32, 17), (4, 1, 32, 64), (16, 1, 32, 33),
+                                              (40, 1, 32, 64), (96, 1, 32, 64)])
 def test_workspace_sizes(L, seqs, q, heads, sel):
     assert nb.msa_indexer_workspace_bytes(8, 1, 2048) == 8 * 2048 * 4
     assert nb.msa_indexer_workspace_bytes(0, 1, 10) == 0
