@@ -186,8 +186,8 @@ __device__ __forceinline__ void shared_workgroup(const IndexerArgs& a, int j, in
 // SHARED: the launch holds shared-prefix workgroups (msa_indexer_scan_shared);
 // their role is compiled only into this form, whose register allocation it
 // raises (112 VGPRs against 84 for the plain scan with one query token).
-// With one query token the plain form is held to five wavefronts per SIMD
-// (at most 96 VGPRs).
+// With one query token the plain form asks for at least five wavefronts per
+// SIMD (at most 96 VGPRs); it compiles to 78, six wavefronts.
 template <int QG, bool SHARED>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(QG == 1 && !SHARED ? 5 : 1)))
 void indexer_kernel(const IndexerArgs a) {

@@ -250,10 +250,11 @@ __device__ __forceinline__ void scan_workgroup(const IndexerArgs& a, int x, int 
   // ROLL (two or more MFMA row groups, a long computation per tile): as soon
   // as tile j is converted, its registers take the next block's tile j, so
   // the next block's loads go out one by one while this block is computed.
-  // With one row group the next block's loads go out after the block, which
-  // keeps the kernel at 82 VGPRs (five wavefronts per SIMD) and measured
-  // 0.8 us faster at 8 x 256K; the rolling form measured 1.3 us faster at
-  // 16 x 64K with 8 query tokens.
+  // With one row group the next block's loads go out after the block: that
+  // form compiles to 78 VGPRs (six wavefronts per SIMD), and the rolling
+  // one, at 82 (five), measured 1.6 us slower at 8 x 256K (forced to six
+  // wavefronts it spilled and took 9 us more). With 8 query tokens the
+  // rolling form measured 1.3-5 us faster at 16 x 64K.
   constexpr bool ROLL = QG > 1;
   // dequantise, multiply, apply ReLU and weights; per-head partials to LDS.
   // sw: this block's scale word; nx: the next block's descriptors (ROLL).
