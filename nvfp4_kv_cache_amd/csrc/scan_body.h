@@ -140,16 +140,19 @@ __device__ __forceinline__ float2 row_pair_max(const float* part, int hs, int H,
 // Blocks per scan workgroup for num_seqs sequences of up to max_blocks
 // blocks and qg 16-row MFMA groups per index head. Halved while the grid
 // would not cover the chip several times over. Measured with one query
-// token: 3 is best for a few long sequences (8 x 256K), 8 for many sequences
-// of mixed length (45 requests, 30K..210K), where much of the grid bound is
-// empty; the grid bound num_seqs x max_blocks is what the host knows. With
+// token (cold launches, us, with the trailing one-block workgroups): a few
+// long sequences (8 x 256K) 94.1-94.3 at 2, 95.2-96.0 at 3, 97.0 at 4,
+// 105.3 at 1; 32 x 32K 54.2-54.8 at 3, 54.0 at 4, 54.8-55.5 at 2; many
+// sequences of mixed length (45 requests, 30K..210K), where much of the
+// grid bound is empty, 233-235 at 8 and 248-252 at 2. The host knows only
+// the grid bound num_seqs x max_blocks and max_blocks. With
 // 5..8 query tokens a workgroup's blocks cost four times the arithmetic and
 // the chip holds about 1,024 workgroups at once (120 VGPRs, 33 KB of LDS
 // each): halving stops at that grid. Measured at 16 x 64K with 8 query
 // tokens: 8 blocks per workgroup (1,024 workgroups) 66.6 us, 4 (2,048)
 // 70.4 us, 2 79.1 us.
 inline int scan_blocks_per_wg(int64_t num_seqs, int64_t max_blocks, int qg) {
-  int bpw = (qg == 1 && num_seqs * max_blocks <= 32768) ? 3 : 8;
+  int bpw = (qg == 1 && num_seqs * max_blocks <= 32768) ? (max_blocks >= 1024 ? 2 : 3) : 8;
   const int64_t min_grid = qg >= 4 ? 1024 : 2048;
   while (bpw > 1 && num_seqs * ((max_blocks + bpw - 1) / bpw) < min_grid) bpw >>= 1;
   return bpw;
