@@ -187,9 +187,13 @@ __device__ __forceinline__ void shared_workgroup(const IndexerArgs& a, int j, in
 // their role is compiled only into this form, whose register allocation it
 // raises (112 VGPRs against 84 for the plain scan with one query token).
 // With one query token the plain form asks for at least five wavefronts per
-// SIMD (at most 96 VGPRs); it compiles to 78, six wavefronts.
+// SIMD (at most 96 VGPRs); it compiles to 78, six wavefronts. With four row
+// groups (5..8 query tokens) it asks for four (at most 128 VGPRs): the four
+// accumulators of a tile's products then fit at 126 VGPRs, where the
+// unconstrained allocation takes 138 and three wavefronts.
 template <int QG, bool SHARED>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(QG == 1 && !SHARED ? 5 : 1)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(
+    QG == 1 && !SHARED ? 5 : (QG == 4 ? 4 : 1))))
 void indexer_kernel(const IndexerArgs a) {
   extern __shared__ float part[];  // [2][H][2*QG][128] partial token scores per index head
   __shared__ uint2 lut[128];

@@ -272,13 +272,22 @@ __device__ __forceinline__ void scan_workgroup(const IndexerArgs& a, int x, int 
         const uint32_t sj = tile_scales(sw, j);
         const v8i kop = dequant32(t.c[j], lut[sj & 0x7F], lut[(sj >> 8) & 0x7F]);
         if constexpr (ROLL) t.c[j] = load_tile16(nx.codes, code_lane, j * 16 * kCodeRow);
+        // the tile's QG products go out back to back, each into its own
+        // accumulator, before their epilogues (with the epilogue after each
+        // product, the compiler gave all of them one accumulator and the
+        // products waited for each other's epilogues: measured 2% slower
+        // with 8 query tokens)
+        v4f acc[QG];
+#pragma unroll
+        for (int rg = 0; rg < QG; ++rg)
+          acc[rg] = mfma_fp8_16x16x128(qop[rg], kop, v4f{0.0f, 0.0f, 0.0f, 0.0f});
+        if constexpr (QG > 1) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int rg = 0; rg < QG; ++rg) {
-          const v4f acc = mfma_fp8_16x16x128(qop[rg], kop, v4f{0.0f, 0.0f, 0.0f, 0.0f});
-          float s = wv[rg][0] * fmaxf(acc[0], 0.0f);
-          s += wv[rg][1] * fmaxf(acc[1], 0.0f);
-          s += wv[rg][2] * fmaxf(acc[2], 0.0f);
-          s += wv[rg][3] * fmaxf(acc[3], 0.0f);
+          float s = wv[rg][0] * fmaxf(acc[rg][0], 0.0f);
+          s += wv[rg][1] * fmaxf(acc[rg][1], 0.0f);
+          s += wv[rg][2] * fmaxf(acc[rg][2], 0.0f);
+          s += wv[rg][3] * fmaxf(acc[rg][3], 0.0f);
           s2[e][rg] = s;
         }
       }
