@@ -460,15 +460,7 @@ def test_select_many_equal_scores(nb, mb):
     say(f"selection with random, all-equal and adversarial scores, {mb} blocks")
     tq = 6
     lens = torch.tensor([mb * 128] * tq, dtype=torch.int32, device="cuda")
-    rng = np.random.default_rng(2 + mb)
-    bs = np.zeros((tq, mb), dtype=np.float32)
-    bs[0] = rng.random(mb, dtype=np.float32)
-    bs[1] = np.tile(np.arange(64, dtype=np.float32)[::-1], mb // 64 + 1)[:mb]   # periodic
-    bs[2] = rng.integers(0, 3, mb).astype(np.float32)                            # few levels
-    bs[3] = -0.0
-    bs[4] = np.arange(mb, dtype=np.float32)                                      # ascending
-    bs[5] = rng.random(mb, dtype=np.float32)
-    bs[5, rng.choice(mb - 1, min(40, mb - 1), replace=False)] = 2.0             # 40-way tie on top
+    bs = _adversarial_scores(mb, tq)
     ids = torch.empty((tq, 17), dtype=torch.int32, device="cuda")
     sc = torch.empty((tq, 17), dtype=torch.float32, device="cuda")
     nb.msa_indexer_select(torch.from_numpy(bs).cuda(), lens, 1, ids, sc)
@@ -480,6 +472,53 @@ def test_select_many_equal_scores(nb, mb):
         got_sc = sc[r].cpu().numpy()
         want_sc = np.where(want >= 0, np.maximum(bs[r], 0)[np.maximum(want, 0)], 0)
         assert np.array_equal(got_sc, want_sc.astype(np.float32)), r
+
+
+def _adversarial_scores(mb, tq=6):
+    rng = np.random.default_rng(2 + mb)
+    bs = np.zeros((tq, mb), dtype=np.float32)
+    bs[0] = rng.random(mb, dtype=np.float32)
+    bs[1] = np.tile(np.arange(64, dtype=np.float32)[::-1], mb // 64 + 1)[:mb]   # periodic
+    bs[2] = rng.integers(0, 3, mb).astype(np.float32)                            # few levels
+    bs[3] = -0.0
+    bs[4] = np.arange(mb, dtype=np.float32)                                      # ascending
+    bs[5] = rng.random(mb, dtype=np.float32)
+    bs[5, rng.choice(mb - 1, min(40, mb - 1), replace=False)] = 2.0             # 40-way tie on top
+    return bs
+
+
+@pytest.mark.parametrize("mb", [3000, 2050, 2049, 1500, 66, 65])
+def test_fused_select_many_equal_scores(nb, mb):
+    # The selection inside the attention launch on adversarial score rows.
+    # 66..2049 blocks: the workgroup's shared selection, and with the
+    # periodic and all-zero rows (hundreds of candidates reach the
+    # threshold) its fall-back to one wavefront's exact rounds; 2050 and up:
+    # the per-wavefront selection over several chunks; 65: direct ranking.
+    say(f"selection inside attention, adversarial scores, {mb} blocks")
+    tq, pages = 6, 8
+    bs = _adversarial_scores(mb, tq)
+    lens = torch.tensor([mb * 128] * tq, dtype=torch.int32, device="cuda")
+    table = (torch.arange(mb, dtype=torch.int32) % pages).repeat(tq, 1).contiguous().cuda()
+    codes = torch.zeros((pages, 4, 128, 64), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((pages, 4, 1024), dtype=torch.uint8, device="cuda")
+    q = torch.zeros((tq, 32, 128), dtype=torch.uint8, device="cuda")
+    out = torch.full((tq, 32, 128), float("nan"), dtype=torch.float32, device="cuda")
+    ws = nb.attn_workspace(tq, 1, 32, 17)
+    ids = torch.empty((tq, 17), dtype=torch.int32, device="cuda")
+    bst = torch.from_numpy(bs).cuda()
+    nb.msa_sparse_attn_select_decode(codes, scales, codes, scales, q, table, lens, 1, bst,
+                                     1.0 / math.sqrt(128.0), out, ws, out_ids=ids)
+    ids2 = torch.empty((tq, 17), dtype=torch.int32, device="cuda")
+    sc = torch.empty((tq, 17), dtype=torch.float32, device="cuda")
+    nb.msa_indexer_select(bst, lens, 1, ids2, sc)
+    torch.cuda.synchronize()
+    from oracle import msa
+    for r in range(tq):
+        want = msa.select_blocks(np.maximum(bs[r].astype(np.float64), 0.0))
+        assert ids[r].cpu().numpy().tolist() == want.tolist(), r
+    assert torch.equal(ids, ids2)
+    # zero K and V: every selected block contributes zero
+    assert torch.equal(out, torch.zeros_like(out))
 
 
 def test_empty_batch_and_bad_shapes(nb):
