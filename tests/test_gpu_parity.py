@@ -487,16 +487,19 @@ def _adversarial_scores(mb, tq=6):
     return bs
 
 
+@pytest.mark.parametrize("rows", [(0, 1, 2, 3, 4, 5), (1, 3, 5)], ids=["whole-block", "shared-block"])
 @pytest.mark.parametrize("mb", [3000, 2050, 2049, 1500, 66, 65])
-def test_fused_select_many_equal_scores(nb, mb):
+def test_fused_select_many_equal_scores(nb, mb, rows):
     # The selection inside the attention launch on adversarial score rows.
     # 66..2049 blocks: the workgroup's shared selection, and with the
     # periodic and all-zero rows (hundreds of candidates reach the
     # threshold) its fall-back to one wavefront's exact rounds; 2050 and up:
     # the per-wavefront selection over several chunks; 65: direct ranking.
-    say(f"selection inside attention, adversarial scores, {mb} blocks")
-    tq, pages = 6, 8
-    bs = _adversarial_scores(mb, tq)
+    # Six query tokens (24 pairs x 17 slots) take the whole-block launch
+    # form, three (12 pairs) the shared-block form.
+    say(f"selection inside attention, adversarial scores, {mb} blocks, rows {rows}")
+    tq, pages = len(rows), 8
+    bs = np.ascontiguousarray(_adversarial_scores(mb)[list(rows)])
     lens = torch.tensor([mb * 128] * tq, dtype=torch.int32, device="cuda")
     table = (torch.arange(mb, dtype=torch.int32) % pages).repeat(tq, 1).contiguous().cuda()
     codes = torch.zeros((pages, 4, 128, 64), dtype=torch.uint8, device="cuda")
