@@ -352,12 +352,12 @@ static msa_status launch_scan(const msa_pool_desc* idx, const uint8_t* idx_codes
   a.blocks_per_wg = bpw;
   // one-block workgroups for the last blocks of every sequence, about one
   // chip's worth of resident workgroups in all, when the regular grid takes
-  // several rounds of the chip
+  // more than one round of the chip (32 x 32K, 1.8 rounds: 54.9 -> 54.1 us)
   int gx = (max_blocks + bpw - 1) / bpw;
   a.tail_first = max_blocks;
   a.tail_rows = 0;
   const int64_t resident = scan_resident_wgs(qg_pow2, shared, int(block.x), lds);
-  if (bpw > 1 && resident > 0 && int64_t(num_seqs) * gx > 2 * resident) {
+  if (bpw > 1 && resident > 0 && int64_t(num_seqs) * gx > resident) {
     const int64_t tail = std::min<int64_t>((resident + num_seqs - 1) / num_seqs, max_blocks / 2);
     const int g1 = int((max_blocks - tail + bpw - 1) / bpw);
     if (int64_t(g1) * bpw < max_blocks) {
